@@ -1,0 +1,209 @@
+"""Paged-attention decode benchmark on one MI355X.
+
+One step = the whole decode hot path over one batch resident in HBM:
+  pa_write_kv_cache (the new token of every sequence, slot-mapped)
+  -> pa_decode (split-K partitions) -> pa_decode_splitk_reduce.
+Default workload: the Llama-3-8B-shaped bf16 GQA batch (64 sequences,
+context lengths U[128, 2048], 32 query / 8 kv heads, head_dim 128, block 16,
+shuffled pool sized 1.25x the need, partition 512).
+
+The KV pool is replicated R times (R x pool >= 2 GB, far above the 256 MB
+last-level cache) and step i uses copy i mod R, so every step streams its KV
+from HBM. Prints ONE JSON line.
+
+value = algorithmic bytes of the step (KV in context counted once per unique
+physical token, plus Q, output, block-table entries, context lengths, int8
+scales, and the write's read + store of the new K/V) / step time.
+roofline = the decode kernel alone: its algorithmic bytes / its mean launch
+duration (HIP events on the stream it runs on) against 8 TB/s.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+sys.path.insert(0, os.path.join(ROOT, "tests"))
+
+METRIC = "decode attention GB/s and % of HBM peak; seq-tokens/sec at bf16 GQA"
+HBM_PEAK_GBS = 8000.0
+KERNEL_SOURCES = ["pa_decode_mfma.hip", "pa_decode_valu.hip", "pa_decode_common.hpp",
+                  "pa_device.hpp"]
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "paged_kv_decode_03_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(cfg: int, partition: int):
+    """HBM bytes per decode launch from committed rocprofv3 counter runs, if
+    they were taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "decode_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    ent = rec.get(f"cfg{cfg}_P{partition}")
+    if not ent or ent.get("kernel_hash") != kernel_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(case, budget_s: float):
+    """The fp64 oracle (write + decode) on this host's cores, repeated until
+    about `budget_s` seconds of work; bytes/s on the same algorithmic count."""
+    import oracle
+    import synth
+    k, v = oracle.fill_cache(case)
+    tr = synth.traffic(case)
+    nbytes = tr["decode"]["total"] + tr["write"]
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.write_kv_cache(case.key, case.value, k, v, case.slot_mapping, case.k_scale,
+                              case.v_scale)
+        oracle.decode_case(case, k, v)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or reps >= 1000:
+            break
+    return {"value": round(nbytes * reps / el / 1e9, 4), "unit": "GB/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"the whole batch (all {case.S} sequences), write + decode, "
+                      f"{reps} repetitions in {el:.1f} s, fp64"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--partition", type=int, default=None, help="split-K partition (tokens)")
+    ap.add_argument("--rotate-gb", type=float, default=2.0)
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the paged decode path here is built and measured on a "
+              "single MI355X; multi-GPU runs are not part of this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import paged_kv_decode_03_amd as pa
+    import synth
+    from gpu_helpers import fill_pool, to_device
+
+    spec = synth.CONFIGS[args.config]
+    P = spec.partition_size if args.partition is None else args.partition
+    case = synth.make_case(spec, args.config)
+    tr = synth.traffic(case)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    dc = to_device(case, dev)
+    k0, v0 = fill_pool(dc, dev)
+    pool_bytes = 2 * k0.numel() * k0.element_size()
+    R = max(2, math.ceil(args.rotate_gb * 1e9 / pool_bytes))
+    pools = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(R - 1)]
+    maxL = case.max_context_len
+    S, Hq, D = case.S, case.Hq, case.D
+    ws = pa.workspace(S, Hq, D, maxL, max(P, 1), dev)
+    out = torch.empty_like(dc.q)
+    scale = float(case.scale)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i, ev=None):
+        k, v = pools[i % R]
+        pa.write_kv_cache(dc.key, dc.value, k, v, dc.slot_mapping, dc.k_scale, dc.v_scale)
+        if ev is not None:
+            ev[0].record(stream)
+        if P > 0:
+            pa.decode(None, dc.q, k, v, dc.block_tables, dc.context_lens, scale, maxL, P, *ws,
+                      k_scale=dc.k_scale, v_scale=dc.v_scale)
+        else:
+            pa.decode(out, dc.q, k, v, dc.block_tables, dc.context_lens, scale, maxL, 0,
+                      k_scale=dc.k_scale, v_scale=dc.v_scale)
+        if ev is not None:
+            ev[1].record(stream)
+        if P > 0:
+            pa.decode_splitk_reduce(out, *ws, dc.context_lens, maxL, P)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i, evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+    dec_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    dec_mean = float(dec_ms.mean())
+
+    step_bytes = tr["decode"]["total"] + tr["write"]
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    achieved = tr["decode"]["total"] / (dec_mean * 1e-3) / 1e9
+    traffic = measured_traffic(args.config, P)
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"f32": "f32", "bf16": "bf16"}[spec.act] + ("+i8kv" if spec.cache == "i8" else ""),
+        "data": "synthetic",
+        "config": {
+            "workload": spec.name, "cfg": args.config, "num_seqs": S, "num_heads": Hq,
+            "num_kv_heads": case.Hkv, "head_dim": D, "block_size": case.B,
+            "context_lens": list(spec.lens), "sum_context": tr["sum_len"],
+            "unique_kv_tokens": tr["unique_tokens"], "partition_size": P, "pool_copies": R,
+            "step": "write + split-K decode + reduce" if P else "write + one-pass decode",
+        },
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "seq_tokens_per_s": round(S / (ms_per_step * 1e-3), 1),
+        "context_tokens_per_s": round(tr["sum_len"] / (ms_per_step * 1e-3), 1),
+        "decode_kernel_us": {"mean": round(dec_mean * 1e3, 2),
+                             "p10": round(float(np.percentile(dec_ms, 10)) * 1e3, 2),
+                             "p90": round(float(np.percentile(dec_ms, 90)) * 1e3, 2)},
+        "bytes": {"decode": tr["decode"]["total"], "kv": tr["decode"]["kv"],
+                  "kv_logical": tr["decode"]["kv_logical"], "write": tr["write"]},
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic, "kernel": "pa_decode (split-K partials)" if P else "pa_decode",
+            "bytes_per_launch": tr["decode"]["total"],
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        del pools
+        torch.cuda.empty_cache()
+        res["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,177 @@
+/*
+ * pa.h -- C ABI of the MI355X (gfx950) paged-attention decode library, libpa.so.
+ *
+ * The method: during decode, every running sequence holds its keys and values
+ * in fixed-size physical blocks of a shared pool, found through a per-sequence
+ * logical->physical block table ("Paged KV-cache" and "PagedAttention kernel",
+ * Continuous-Batching-LLM-Inference-Engine README, feature list). Each step
+ *   1. writes the new token's K/V into the slot the scheduler mapped for it
+ *      ("LLM engine -> KV cache manager: writes KV cache" and "Paged attention
+ *      -> KV cache manager: maps cache slots", "How pakanor/low-latency-
+ *      distributed-llm-serving-infrastructure-custom-k8s-control-plane works",
+ *      Connections), optionally as int8 ("paged INT8 KV storage", "How
+ *      vrajpatel105/paged-inference-engine works", summary);
+ *   2. runs decode attention of the one new query token per sequence over its
+ *      cached tokens, gathering K/V from the non-contiguous blocks inside the
+ *      kernel with no compaction copy (README feature list; "Decoder model ->
+ *      Block allocator: reads block table", paged-inference-engine,
+ *      Connections; "Llama forward -> Paged decode attention", "How
+ *      brave30/mini-inference-engine works", Connections);
+ *   3. for long contexts, splits each sequence's context into partitions and
+ *      combines the per-partition results with a log-sum-exp reduce.
+ *
+ * Math of step 2, for sequence s, query head h, kv head g = h / (Hq / Hkv):
+ *   x_t   = scale * sum_d q[s,h,d] * k_t[d]          t = 0 .. L_s - 1
+ *   out   = sum_t exp(x_t - max x) v_t / sum_t exp(x_t - max x)
+ * with k_t, v_t row t % block_size of block block_tables[s][t / block_size],
+ * dequantised as code * scale[block, g] for an int8 cache.
+ *
+ * Conventions used by every entry point
+ *  - All data pointers are DEVICE pointers owned by the caller. The library
+ *    allocates nothing, keeps no state between calls, and may be called from
+ *    several host threads at once.
+ *  - All tensors are dense, row-major, with the layouts given per argument.
+ *    The KV pool is [num_blocks][num_kv_heads][block_size][head_dim]: the
+ *    block_size x head_dim tile of one (block, kv head) is contiguous.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
+ *    and is asynchronous. Calls on one stream run in order; in a decode step
+ *    pa_write_kv_cache must precede pa_decode, because context_lens counts the
+ *    newly written token.
+ *  - dtypes: PA_F32 (fp32), PA_BF16 (bfloat16), PA_I8 (int8 cache codes).
+ *  - Return value: PA_OK (0) or a negative pa_status. Arguments that the host
+ *    can check are checked before anything is enqueued; on any error nothing
+ *    is enqueued. Values held in device memory (block ids, slots, lengths)
+ *    are trusted: out-of-range values are undefined behaviour, unless the
+ *    environment variable PA_CHECK=1 is set, in which case they are copied to
+ *    the host (synchronising the stream) and checked first (PA_ERR_INDEX).
+ *  - No C++ exception crosses this interface.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_I8 = 2 } pa_dtype;
+
+typedef enum {
+    PA_OK = 0,
+    PA_ERR_NULL = -1,        /* a required pointer is NULL */
+    PA_ERR_SHAPE = -2,       /* a size is out of range or inconsistent */
+    PA_ERR_DTYPE = -3,       /* unknown dtype or unsupported dtype combination */
+    PA_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned */
+    PA_ERR_UNSUPPORTED = -5, /* valid arguments that no kernel instance covers */
+    PA_ERR_LAUNCH = -6,      /* the HIP runtime reported an error at launch */
+    PA_ERR_INDEX = -7        /* PA_CHECK=1 found a device index out of range */
+} pa_status;
+
+/* Library version as MAJOR * 10000 + MINOR * 100 + PATCH. */
+int pa_version(void);
+
+/* Static text for a pa_status value ("unknown status" for others). */
+const char *pa_status_string(int status);
+
+/* Number of context partitions of `partition_size` tokens that cover
+ * `max_context_len` tokens: ceil(max_context_len / partition_size), or 0 when
+ * either is <= 0. Sizes the split-K workspace of pa_decode. */
+int pa_num_partitions(int max_context_len, int partition_size);
+
+/*
+ * pa_write_kv_cache -- slot-mapped write of new tokens' keys and values
+ * ("writes KV cache", "maps cache slots": pakanor ... control-plane page,
+ * Connections; int8 storage: paged-inference-engine page, summary).
+ *
+ * For every token i with slot = slot_mapping[i] >= 0, with b = slot /
+ * block_size and o = slot % block_size, for every kv head g and dim d:
+ *   float cache: k_cache[b][g][o][d] = key[i][g][d] (bit copy; act_dtype must
+ *                equal cache_dtype), likewise value -> v_cache;
+ *   int8 cache:  k_cache[b][g][o][d] = clamp(rint(key[i][g][d] / k_scale[b][g]),
+ *                -127, 127), where the quotient is the correctly rounded fp32
+ *                quotient, rint rounds half to even and a NaN quotient gives 0;
+ *                likewise value with v_scale.
+ * Tokens with slot < 0 are skipped. Every other byte of the pool, and the
+ * scales, are left untouched. Two tokens mapped to one slot: undefined.
+ *
+ *   key, value      [num_tokens][num_kv_heads][head_dim], act_dtype (F32/BF16)
+ *   k_cache,v_cache [num_blocks][num_kv_heads][block_size][head_dim], cache_dtype
+ *   slot_mapping    [num_tokens] int64
+ *   k_scale,v_scale [num_blocks][num_kv_heads] fp32, read only; required (non-NULL)
+ *                   iff cache_dtype == PA_I8, ignored otherwise. The caller
+ *                   chooses them (e.g. absmax / 127 of the block) before the write.
+ * Requirements: num_tokens >= 0 (0 = no-op), num_kv_heads >= 1, head_dim a
+ * multiple of 8 in [8, 1024], block_size >= 1, num_blocks >= 1; key, value,
+ * k_cache, v_cache 16-byte aligned.
+ */
+int pa_write_kv_cache(const void *key, const void *value, void *k_cache, void *v_cache,
+                      const int64_t *slot_mapping, const float *k_scale, const float *v_scale,
+                      int num_tokens, int num_kv_heads, int head_dim, int block_size,
+                      int64_t num_blocks, pa_dtype act_dtype, pa_dtype cache_dtype, void *stream);
+
+/*
+ * pa_decode -- paged decode attention ("PagedAttention kernel ... gathers KV
+ * data from non-contiguous physical blocks in-kernel, no compaction copy",
+ * README feature list; "Paged decode attention", mini-inference-engine page,
+ * Model Compute).
+ *
+ *   out           [num_seqs][num_heads][head_dim], q_dtype. Written only when
+ *                 partition_size == 0.
+ *   q             [num_seqs][num_heads][head_dim], q_dtype (F32 or BF16)
+ *   k_cache, v_cache  pool as above, cache_dtype
+ *   block_tables  [num_seqs][max_blocks_per_seq] int32 physical block ids;
+ *                 only entries < ceil(context_lens[s] / block_size) are read
+ *   context_lens  [num_seqs] int32, 0 <= L_s <= max_context_len; counts the
+ *                 newly written token. L_s = 0 gives an all-zero output.
+ *   k_scale, v_scale  [num_blocks][num_kv_heads] fp32, required iff int8 cache
+ *   scale         softmax scale applied to q . k (usually 1 / sqrt(head_dim))
+ *   num_heads     query heads Hq; num_kv_heads Hkv divides it; query head h
+ *                 reads kv head h / (Hq / Hkv)
+ *   max_context_len  host-side bound on every L_s; must not exceed
+ *                 max_blocks_per_seq * block_size
+ *   partition_size   0: one pass over each whole context, result in `out`.
+ *                 > 0 (a multiple of block_size): split-K. Partition j of
+ *                 sequence s covers tokens [j P, min(L_s, (j+1) P)) and stores
+ *                   tmp_out[s][h][j][:] = that partition's normalised output,
+ *                   tmp_max[s][h][j]    = its largest logit x_t (natural units),
+ *                   tmp_sum[s][h][j]    = sum_t exp(x_t - tmp_max),
+ *                 for j < ceil(L_s / P) only; `out` is not touched. Combine with
+ *                 pa_decode_splitk_reduce.
+ *   tmp_out       [num_seqs][num_heads][NP][head_dim] fp32, tmp_max and tmp_sum
+ *                 [num_seqs][num_heads][NP] fp32, NP = pa_num_partitions(
+ *                 max_context_len, partition_size); caller-owned workspace,
+ *                 required iff partition_size > 0.
+ * Supported instances (others return PA_ERR_UNSUPPORTED):
+ *   group size G = Hq / Hkv in {1, 2}: VALU kernel; head_dim 64 or 128;
+ *     (q, cache) = (F32, F32), (BF16, BF16), (F32, I8), (BF16, I8).
+ *   G in {4, 8}: MFMA kernel; head_dim 128; q BF16; cache BF16 or I8.
+ *   block_size 16 or 32.
+ * Alignment: out, q, k_cache, v_cache, tmp_out 16-byte aligned.
+ */
+int pa_decode(void *out, const void *q, const void *k_cache, const void *v_cache,
+              const int32_t *block_tables, int max_blocks_per_seq, const int32_t *context_lens,
+              const float *k_scale, const float *v_scale, float scale, int num_seqs,
+              int num_heads, int num_kv_heads, int head_dim, int block_size, int64_t num_blocks,
+              int max_context_len, int partition_size, float *tmp_out, float *tmp_max,
+              float *tmp_sum, pa_dtype q_dtype, pa_dtype cache_dtype, void *stream);
+
+/*
+ * pa_decode_splitk_reduce -- log-sum-exp combination of split-K partials.
+ * For each (s, h), over j < n = ceil(L_s / partition_size):
+ *   M = max_j tmp_max[j], W_j = tmp_sum[j] * exp(tmp_max[j] - M),
+ *   out[s][h][:] = sum_j W_j tmp_out[j][:] / sum_j W_j      (0 when n = 0),
+ * rounded to out_dtype (F32 or BF16, round to nearest even).
+ * Arguments as in pa_decode; head_dim a multiple of 2 in [2, 1024];
+ * out and tmp_out 16-byte aligned.
+ */
+int pa_decode_splitk_reduce(void *out, const float *tmp_out, const float *tmp_max,
+                            const float *tmp_sum, const int32_t *context_lens, int num_seqs,
+                            int num_heads, int head_dim, int max_context_len, int partition_size,
+                            pa_dtype out_dtype, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

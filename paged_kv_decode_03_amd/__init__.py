@@ -1,0 +1,186 @@
+"""Paged-attention decode for MI355X (gfx950): Python binding of libpa.so.
+
+Argument marshalling only: every step of the decode path runs in the HIP
+kernels of ``libpa.so`` (built by ``python -m paged_kv_decode_03_amd.build``).
+Torch tensors supply device memory and the current stream; the functions
+check dtype, device, shape and contiguity, then call the C ABI declared in
+``include/pa.h`` with raw pointers. There is no fallback: if the library is
+missing, importing this package raises.
+
+Entry points (same names as the C ABI without the ``pa_`` prefix):
+  write_kv_cache           slot-mapped write of new K/V (copy or int8)
+  decode                   paged decode attention (one pass or split-K partials)
+  decode_splitk_reduce     log-sum-exp reduce of split-K partials
+plus ``workspace`` (allocates the split-K partials with torch) and
+``paged_attention`` (decode + reduce into a new output tensor).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libpa.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run `python -m paged_kv_decode_03_amd.build`")
+
+_lib = ctypes.CDLL(LIB_PATH)
+_p, _i, _i64, _f = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
+_lib.pa_version.restype = _i
+_lib.pa_status_string.restype = ctypes.c_char_p
+_lib.pa_status_string.argtypes = [_i]
+_lib.pa_num_partitions.restype = _i
+_lib.pa_num_partitions.argtypes = [_i, _i]
+_lib.pa_write_kv_cache.restype = _i
+_lib.pa_write_kv_cache.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i64, _i, _i, _p]
+_lib.pa_decode.restype = _i
+_lib.pa_decode.argtypes = [_p, _p, _p, _p, _p, _i, _p, _p, _p, _f, _i, _i, _i, _i, _i, _i64, _i,
+                           _i, _p, _p, _p, _i, _i, _p]
+_lib.pa_decode_splitk_reduce.restype = _i
+_lib.pa_decode_splitk_reduce.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p]
+
+PA_F32, PA_BF16, PA_I8 = 0, 1, 2
+_DTYPE = {torch.float32: PA_F32, torch.bfloat16: PA_BF16, torch.int8: PA_I8}
+
+
+class PAError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: {status_string(status)} (status {status})")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    return _lib
+
+
+def version() -> int:
+    return _lib.pa_version()
+
+
+def status_string(status: int) -> str:
+    return _lib.pa_status_string(int(status)).decode()
+
+
+def num_partitions(max_context_len: int, partition_size: int) -> int:
+    return _lib.pa_num_partitions(int(max_context_len), int(partition_size))
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _dt(t) -> int:
+    try:
+        return _DTYPE[t.dtype]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {t.dtype}") from None
+
+
+def _dev(*ts):
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("all tensors must be on one device")
+    return dev
+
+
+def _stream(stream, device):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(fn, rc):
+    if rc != 0:
+        raise PAError(fn, rc)
+
+
+def write_kv_cache(key, value, k_cache, v_cache, slot_mapping, k_scale=None, v_scale=None,
+                   stream=None):
+    """Write key/value [T, Hkv, D] into the slots ``slot_mapping`` [T] (int64)
+    of the pool k_cache/v_cache [NB, Hkv, B, D]; int8 pools need k_scale and
+    v_scale [NB, Hkv] fp32."""
+    dev = _dev(key, value, k_cache, v_cache, slot_mapping, k_scale, v_scale)
+    if slot_mapping.dtype != torch.int64:
+        raise TypeError("slot_mapping must be int64")
+    T, Hkv, D = key.shape
+    NB, Hkv2, B, D2 = k_cache.shape
+    if value.shape != key.shape or v_cache.shape != k_cache.shape or (Hkv2, D2) != (Hkv, D) \
+            or slot_mapping.shape != (T,):
+        raise ValueError("shape mismatch")
+    rc = _lib.pa_write_kv_cache(_ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache),
+                                _ptr(slot_mapping), _ptr(k_scale), _ptr(v_scale), T, Hkv, D, B,
+                                NB, _dt(key), _dt(k_cache), _stream(stream, dev))
+    _check("pa_write_kv_cache", rc)
+
+
+def decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
+           partition_size=0, tmp_out=None, tmp_max=None, tmp_sum=None, k_scale=None,
+           v_scale=None, stream=None):
+    """Paged decode attention of q [S, Hq, D] over the pool; one pass into
+    ``out`` [S, Hq, D] (partition_size 0) or split-K partials into the
+    workspace (partition_size > 0, a multiple of the block size)."""
+    dev = _dev(out, q, k_cache, v_cache, block_tables, context_lens, tmp_out, tmp_max, tmp_sum,
+               k_scale, v_scale)
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise TypeError("block_tables and context_lens must be int32")
+    S, Hq, D = q.shape
+    NB, Hkv, B, D2 = k_cache.shape
+    if D2 != D or v_cache.shape != k_cache.shape or block_tables.shape[0] != S \
+            or context_lens.shape != (S,) or (out is not None and out.shape != q.shape):
+        raise ValueError("shape mismatch")
+    if out is not None and out.dtype != q.dtype:
+        raise TypeError("out must have the dtype of q")
+    rc = _lib.pa_decode(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                        block_tables.shape[1], _ptr(context_lens), _ptr(k_scale), _ptr(v_scale),
+                        float(scale), S, Hq, Hkv, D, B, NB, int(max_context_len),
+                        int(partition_size), _ptr(tmp_out), _ptr(tmp_max), _ptr(tmp_sum),
+                        _dt(q), _dt(k_cache), _stream(stream, dev))
+    _check("pa_decode", rc)
+
+
+def decode_splitk_reduce(out, tmp_out, tmp_max, tmp_sum, context_lens, max_context_len,
+                         partition_size, stream=None):
+    """Combine split-K partials [S, Hq, NP, D] into out [S, Hq, D]."""
+    dev = _dev(out, tmp_out, tmp_max, tmp_sum, context_lens)
+    S, Hq, D = out.shape
+    rc = _lib.pa_decode_splitk_reduce(_ptr(out), _ptr(tmp_out), _ptr(tmp_max), _ptr(tmp_sum),
+                                      _ptr(context_lens), S, Hq, D, int(max_context_len),
+                                      int(partition_size), _dt(out), _stream(stream, dev))
+    _check("pa_decode_splitk_reduce", rc)
+
+
+def workspace(num_seqs, num_heads, head_dim, max_context_len, partition_size, device):
+    """Split-K partials (tmp_out [S,Hq,NP,D], tmp_max, tmp_sum [S,Hq,NP]) fp32."""
+    NP = max(1, num_partitions(max_context_len, partition_size))
+    return (torch.empty((num_seqs, num_heads, NP, head_dim), dtype=torch.float32, device=device),
+            torch.empty((num_seqs, num_heads, NP), dtype=torch.float32, device=device),
+            torch.empty((num_seqs, num_heads, NP), dtype=torch.float32, device=device))
+
+
+def paged_attention(q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
+                    partition_size=0, k_scale=None, v_scale=None, ws=None, stream=None):
+    """Decode attention into a new tensor: one pass, or split-K + reduce."""
+    out = torch.empty_like(q)
+    if partition_size == 0:
+        decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len, 0,
+               k_scale=k_scale, v_scale=v_scale, stream=stream)
+        return out
+    S, Hq, D = q.shape
+    if ws is None:
+        ws = workspace(S, Hq, D, max_context_len, partition_size, q.device)
+    decode(None, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
+           partition_size, *ws, k_scale=k_scale, v_scale=v_scale, stream=stream)
+    decode_splitk_reduce(out, *ws, context_lens, max_context_len, partition_size, stream=stream)
+    return out

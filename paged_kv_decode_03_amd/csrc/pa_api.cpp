@@ -1,0 +1,172 @@
+// C ABI of libpa.so: argument validation, kernel-instance selection and
+// launch on the caller's stream. Declarations and the contract of every entry
+// point are in include/pa.h.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
+
+#include "pa.h"
+#include "pa_kernels.hpp"
+
+namespace {
+
+constexpr int kVersion = 10000;   // 1.0.0
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool valid_act(pa_dtype d) { return d == PA_F32 || d == PA_BF16; }
+bool valid_cache(pa_dtype d) { return d == PA_F32 || d == PA_BF16 || d == PA_I8; }
+
+int launch_status(hipError_t e) {
+    if (e == hipSuccess) return PA_OK;
+    if (e == hipErrorNotSupported) return PA_ERR_UNSUPPORTED;
+    return PA_ERR_LAUNCH;
+}
+
+bool check_enabled() {
+    const char* v = std::getenv("PA_CHECK");
+    return v && v[0] == '1';
+}
+
+// Copy n elements of a device array to the host (synchronous, debug path).
+template <typename T>
+bool fetch(std::vector<T>& host, const T* dev, int64_t n, hipStream_t st) {
+    host.resize((size_t)n);
+    if (n == 0) return true;
+    if (hipStreamSynchronize(st) != hipSuccess) return false;
+    return hipMemcpy(host.data(), dev, sizeof(T) * (size_t)n, hipMemcpyDeviceToHost) == hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_version(void) { return kVersion; }
+
+const char* pa_status_string(int status) {
+    switch (status) {
+        case PA_OK: return "ok";
+        case PA_ERR_NULL: return "a required pointer is NULL";
+        case PA_ERR_SHAPE: return "a size is out of range or inconsistent";
+        case PA_ERR_DTYPE: return "unknown or unsupported dtype combination";
+        case PA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+        case PA_ERR_UNSUPPORTED: return "no kernel instance covers these arguments";
+        case PA_ERR_LAUNCH: return "the HIP runtime reported a launch error";
+        case PA_ERR_INDEX: return "a device-side index is out of range (PA_CHECK)";
+        default: return "unknown status";
+    }
+}
+
+int pa_num_partitions(int max_context_len, int partition_size) {
+    if (max_context_len <= 0 || partition_size <= 0) return 0;
+    return (int)(((int64_t)max_context_len + partition_size - 1) / partition_size);
+}
+
+int pa_write_kv_cache(const void* key, const void* value, void* k_cache, void* v_cache,
+                      const int64_t* slot_mapping, const float* k_scale, const float* v_scale,
+                      int num_tokens, int num_kv_heads, int head_dim, int block_size,
+                      int64_t num_blocks, pa_dtype act_dtype, pa_dtype cache_dtype, void* stream) {
+    if (num_tokens < 0 || num_kv_heads < 1 || head_dim < 8 || head_dim > 1024 || head_dim % 8 ||
+        block_size < 1 || num_blocks < 1)
+        return PA_ERR_SHAPE;
+    if (!valid_act(act_dtype) || !valid_cache(cache_dtype)) return PA_ERR_DTYPE;
+    if (cache_dtype != PA_I8 && cache_dtype != act_dtype) return PA_ERR_DTYPE;
+    if (num_tokens == 0) return PA_OK;
+    if (!key || !value || !k_cache || !v_cache || !slot_mapping) return PA_ERR_NULL;
+    if (cache_dtype == PA_I8 && (!k_scale || !v_scale)) return PA_ERR_NULL;
+    if (!aligned16(key) || !aligned16(value) || !aligned16(k_cache) || !aligned16(v_cache))
+        return PA_ERR_ALIGN;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (check_enabled()) {
+        std::vector<int64_t> slots;
+        if (!fetch(slots, slot_mapping, num_tokens, st)) return PA_ERR_LAUNCH;
+        for (int64_t sl : slots) {
+            if (sl < 0) continue;
+            if (sl / block_size >= num_blocks) return PA_ERR_INDEX;
+        }
+    }
+    pa::WriteArgs a{key, value, k_cache, v_cache, slot_mapping, k_scale, v_scale,
+                    num_tokens, num_kv_heads, head_dim, block_size,
+                    (pa::Dtype)act_dtype, (pa::Dtype)cache_dtype};
+    return launch_status(pa::launch_write_kv(a, st));
+}
+
+int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+              const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
+              const float* k_scale, const float* v_scale, float scale, int num_seqs,
+              int num_heads, int num_kv_heads, int head_dim, int block_size, int64_t num_blocks,
+              int max_context_len, int partition_size, float* tmp_out, float* tmp_max,
+              float* tmp_sum, pa_dtype q_dtype, pa_dtype cache_dtype, void* stream) {
+    if (num_seqs < 0 || num_heads < 1 || num_kv_heads < 1 || num_heads % num_kv_heads ||
+        head_dim < 1 || block_size < 1 || max_blocks_per_seq < 1 || num_blocks < 1 ||
+        max_context_len < 0 || partition_size < 0)
+        return PA_ERR_SHAPE;
+    if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size) return PA_ERR_SHAPE;
+    if (partition_size > 0 && partition_size % block_size) return PA_ERR_SHAPE;
+    if (!valid_act(q_dtype) || !valid_cache(cache_dtype)) return PA_ERR_DTYPE;
+    if (cache_dtype != PA_I8 && cache_dtype != q_dtype) return PA_ERR_DTYPE;
+    const bool split = partition_size > 0;
+    if (!q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_NULL;
+    if (split ? (!tmp_out || !tmp_max || !tmp_sum) : !out) return PA_ERR_NULL;
+    if (cache_dtype == PA_I8 && (!k_scale || !v_scale)) return PA_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) ||
+        (split ? !aligned16(tmp_out) : !aligned16(out)))
+        return PA_ERR_ALIGN;
+    const int np = split ? pa_num_partitions(max_context_len, partition_size) : 1;
+
+    pa::DecodeArgs a{out, q, k_cache, v_cache, block_tables, context_lens, k_scale, v_scale,
+                     tmp_out, tmp_max, tmp_sum, scale, num_seqs, num_heads, num_kv_heads,
+                     head_dim, block_size, max_blocks_per_seq, partition_size, np,
+                     (pa::Dtype)q_dtype, (pa::Dtype)cache_dtype};
+    const bool mfma = pa::mfma_supports(a);
+    if (!mfma && !pa::valu_supports(a)) return PA_ERR_UNSUPPORTED;
+    const int64_t nwg = (int64_t)num_kv_heads * num_seqs * np;
+    if (nwg > 0x7fffffff) return PA_ERR_SHAPE;
+    if (num_seqs == 0 || np == 0) return PA_OK;
+
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (check_enabled()) {
+        std::vector<int32_t> lens, tables;
+        if (!fetch(lens, context_lens, num_seqs, st) ||
+            !fetch(tables, block_tables, (int64_t)num_seqs * max_blocks_per_seq, st))
+            return PA_ERR_LAUNCH;
+        for (int s = 0; s < num_seqs; ++s) {
+            if (lens[s] < 0 || lens[s] > max_context_len) return PA_ERR_INDEX;
+            const int nb = (lens[s] + block_size - 1) / block_size;
+            for (int b = 0; b < nb; ++b) {
+                const int32_t id = tables[(size_t)s * max_blocks_per_seq + b];
+                if (id < 0 || id >= num_blocks) return PA_ERR_INDEX;
+            }
+        }
+    }
+    return launch_status(mfma ? pa::launch_decode_mfma(a, st) : pa::launch_decode_valu(a, st));
+}
+
+int pa_decode_splitk_reduce(void* out, const float* tmp_out, const float* tmp_max,
+                            const float* tmp_sum, const int32_t* context_lens, int num_seqs,
+                            int num_heads, int head_dim, int max_context_len, int partition_size,
+                            pa_dtype out_dtype, void* stream) {
+    if (num_seqs < 0 || num_heads < 1 || head_dim < 1 || head_dim > 1024 || max_context_len < 0 ||
+        partition_size < 1)
+        return PA_ERR_SHAPE;
+    if (!valid_act(out_dtype)) return PA_ERR_DTYPE;
+    if (num_seqs == 0) return PA_OK;
+    const int np = pa_num_partitions(max_context_len, partition_size);
+    if (!out || !context_lens || (np > 0 && (!tmp_out || !tmp_max || !tmp_sum))) return PA_ERR_NULL;
+    if ((int64_t)num_seqs * num_heads > 0x7fffffff) return PA_ERR_SHAPE;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (check_enabled()) {
+        std::vector<int32_t> lens;
+        if (!fetch(lens, context_lens, num_seqs, st)) return PA_ERR_LAUNCH;
+        for (int s = 0; s < num_seqs; ++s)
+            if (lens[s] < 0 || lens[s] > max_context_len) return PA_ERR_INDEX;
+    }
+    pa::ReduceArgs a{out, tmp_out, tmp_max, tmp_sum, context_lens, num_seqs, num_heads, head_dim,
+                     partition_size, np, (pa::Dtype)out_dtype};
+    return launch_status(pa::launch_reduce(a, st));
+}
+
+}  // extern "C"

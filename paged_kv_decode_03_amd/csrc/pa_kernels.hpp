@@ -1,0 +1,63 @@
+// Internal launch interface between the C ABI (pa_api.cpp) and the kernels.
+// Arguments have been validated by the caller; launchers only enqueue.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+enum Dtype : int { F32 = 0, BF16 = 1, I8 = 2 };
+
+struct WriteArgs {
+    const void* key;
+    const void* value;
+    void* k_cache;
+    void* v_cache;
+    const int64_t* slot_mapping;
+    const float* k_scale;
+    const float* v_scale;
+    int num_tokens, num_kv_heads, head_dim, block_size;
+    Dtype act, cache;
+};
+
+struct DecodeArgs {
+    void* out;
+    const void* q;
+    const void* k_cache;
+    const void* v_cache;
+    const int32_t* block_tables;
+    const int32_t* context_lens;
+    const float* k_scale;
+    const float* v_scale;
+    float* tmp_out;
+    float* tmp_max;
+    float* tmp_sum;
+    float scale;
+    int num_seqs, num_heads, num_kv_heads, head_dim, block_size;
+    int max_blocks_per_seq;
+    int partition_size;   // 0 = one pass
+    int num_partitions;   // grid extent over partitions (1 for one pass)
+    Dtype q_dtype, cache;
+};
+
+struct ReduceArgs {
+    void* out;
+    const float* tmp_out;
+    const float* tmp_max;
+    const float* tmp_sum;
+    const int32_t* context_lens;
+    int num_seqs, num_heads, head_dim, partition_size, num_partitions;
+    Dtype out_dtype;
+};
+
+hipError_t launch_write_kv(const WriteArgs& a, hipStream_t st);
+// Returns hipErrorNotSupported when no instance covers the arguments.
+hipError_t launch_decode_valu(const DecodeArgs& a, hipStream_t st);
+hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t st);
+hipError_t launch_reduce(const ReduceArgs& a, hipStream_t st);
+
+bool valu_supports(const DecodeArgs& a);
+bool mfma_supports(const DecodeArgs& a);
+
+}  // namespace pa

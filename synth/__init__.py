@@ -328,27 +328,23 @@ def make_case(spec: Spec, seed: int) -> Case:
         q32 = q32 * np.float32(spec.q_std)
 
     # token values ---------------------------------------------------------
-    pos_list, seq_list, src_list = [], [], []   # one entry per token to be written
+    # Every token to be written (pre: already in context; new: the decode
+    # step's token) takes its K/V from a "source" draw. Sources are drawn in
+    # order -- group prefixes first, then each sequence's own tokens -- K for
+    # all sources, then V, in chunks that are cast and scattered directly into
+    # the output arrays.
     if prefix:
         G = spec.prefix_groups
-        kp = rng.standard_normal((G, spec.prefix_tokens, Hkv, D), dtype=np.float32)
-        vp = rng.standard_normal((G, spec.prefix_tokens, Hkv, D), dtype=np.float32)
         first_fresh = np.minimum(L.astype(np.int64) - 1, spec.prefix_tokens)
         nfresh = L.astype(np.int64) - first_fresh
-        kf = rng.standard_normal((int(nfresh.sum()), Hkv, D), dtype=np.float32)
-        vf = rng.standard_normal((int(nfresh.sum()), Hkv, D), dtype=np.float32)
-        kall = np.concatenate([kp.reshape(-1, Hkv, D), kf])
-        vall = np.concatenate([vp.reshape(-1, Hkv, D), vf])
-        del kp, vp, kf, vf
+        n_src = G * spec.prefix_tokens + int(nfresh.sum())
         fresh_off = G * spec.prefix_tokens + np.concatenate([[0], np.cumsum(nfresh)[:-1]])
-        # group prefixes: every prefix position, written once into the shared blocks
         pre_slots, pre_src = [], []
         for g in range(G):
             ids = np.asarray(group_ids[g], dtype=np.int64)
             p = np.arange(spec.prefix_tokens, dtype=np.int64)
             pre_slots.append(ids[p // B] * B + p % B)
             pre_src.append(g * spec.prefix_tokens + p)
-        # private positions of each sequence (CoW copies of prefix tokens, then fresh)
         new_slots = np.empty(S, dtype=np.int64)
         new_src = np.empty(S, dtype=np.int64)
         for s in range(S):
@@ -364,28 +360,39 @@ def make_case(spec: Spec, seed: int) -> Case:
         pre_slots = np.concatenate(pre_slots) if pre_slots else np.zeros(0, np.int64)
         pre_src = np.concatenate(pre_src) if pre_src else np.zeros(0, np.int64)
     else:
-        T = int(L.sum())
-        kall = rng.standard_normal((T, Hkv, D), dtype=np.float32)
-        vall = rng.standard_normal((T, Hkv, D), dtype=np.float32)
+        n_src = int(L.sum())
         off = np.concatenate([[0], np.cumsum(L.astype(np.int64))[:-1]]) if S else np.zeros(0, np.int64)
         seq_of = np.repeat(np.arange(S), L)
-        p = np.arange(T, dtype=np.int64) - np.repeat(off, L)
+        p = np.arange(n_src, dtype=np.int64) - np.repeat(off, L)
         slots = bt[seq_of, p // B].astype(np.int64) * B + p % B
         is_new = p == np.repeat(L.astype(np.int64) - 1, L)
         pre_slots, pre_src = slots[~is_new], np.nonzero(~is_new)[0]
         new_slots, new_src = slots[is_new], np.nonzero(is_new)[0]
 
-    kall_c = _cast(kall, spec.act)
-    vall_c = _cast(vall, spec.act)
-    del kall, vall
     q = _cast(q32, spec.act)
+    T_pre = len(pre_src)
+    all_src = np.concatenate([pre_src, new_src]).astype(np.int64)
+    order = np.argsort(all_src, kind="stable")
+    sorted_src = all_src[order]
+    st = storage_dtype(spec.act)
+    outs = []
+    chunk = max(1, (1 << 21) // max(1, Hkv * D))          # ~2M values per draw
+    for _ in range(2):                                      # K, then V
+        allv = np.empty((T_pre + S, Hkv, D), dtype=st)
+        for a0 in range(0, n_src, chunk):
+            a1 = min(n_src, a0 + chunk)
+            x = _cast(rng.standard_normal((a1 - a0, Hkv, D), dtype=np.float32), spec.act)
+            lo, hi = np.searchsorted(sorted_src, [a0, a1])
+            allv[order[lo:hi]] = x[sorted_src[lo:hi] - a0]
+        outs.append(allv)
+    kall, vall = outs
 
     case = Case(
         spec=spec, seed=seed, num_blocks=NB, poison_block=pool.poison,
         scale=np.float32(1.0 / math.sqrt(D)),
         context_lens=L, block_tables=bt, q=q,
-        pre_key=kall_c[pre_src], pre_value=vall_c[pre_src], pre_slots=pre_slots.astype(np.int64),
-        key=kall_c[new_src], value=vall_c[new_src], slot_mapping=new_slots.astype(np.int64),
+        pre_key=kall[:T_pre], pre_value=vall[:T_pre], pre_slots=pre_slots.astype(np.int64),
+        key=kall[T_pre:], value=vall[T_pre:], slot_mapping=new_slots.astype(np.int64),
         k_scale=None, v_scale=None, refcount=pool.refcount.copy(),
     )
     if spec.cache == "i8":
@@ -399,13 +406,13 @@ def absmax_scales(case: Case):
     (block, kv head), in fp32; 1.0 where absmax is 0 or the block is unused."""
     NB, Hkv, B = case.num_blocks, case.Hkv, case.B
     out = []
+    rows = max(1, (1 << 21) // max(1, Hkv * case.D))
     for pre, new in ((case.pre_key, case.key), (case.pre_value, case.value)):
         amax = np.zeros((NB, Hkv), dtype=np.float32)
         for vals, slots in ((pre, case.pre_slots), (new, case.slot_mapping)):
-            if len(slots) == 0:
-                continue
-            a = np.abs(as_f32(vals, case.spec.act)).max(axis=2)          # [T, Hkv]
-            np.maximum.at(amax, slots // B, a)
+            for r0 in range(0, len(slots), rows):
+                a = np.abs(as_f32(vals[r0:r0 + rows], case.spec.act)).max(axis=2)   # [T, Hkv]
+                np.maximum.at(amax, slots[r0:r0 + rows] // B, a)
         sc = amax / np.float32(127.0)
         sc[amax == 0] = np.float32(1.0)
         out.append(sc.astype(np.float32))

@@ -1,0 +1,361 @@
+"""HIP path (through the C ABI) against the fp64 oracle, on the GPU.
+
+Bars: the slot-mapped write is byte-exact over the whole pool (every slot,
+including untouched poison); one-hot probes, L = 1 and placement changes are
+bit-exact; decode outputs are within max |GPU - oracle| <= 1e-5 (fp32),
+2e-2 (bf16) and 3e-2 (int8 KV, same dequantisation on both sides).
+Small cases span several 16-token chunks, several partitions and a ragged
+tail; the full-size workloads run in the bench's launch configuration and are
+checked on sampled sequences (every head and dim of those sequences).
+"""
+import dataclasses
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import pins
+import synth
+from gpu_helpers import (TORCH_DT, as_f64, dev_to_host, fill_pool, host_to_dev, poison_pool,
+                         run_decode, to_device, tol)
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import paged_kv_decode_03_amd as pa
+
+C = synth.CONFIGS
+SMALL = {
+    "cfg1": C[1],
+    "cfg2s": C[2].replace(num_seqs=12, lens=("uniform", 1, 1100), max_len=1100),
+    "cfg3s": C[3].replace(num_seqs=2, lens=("const", 4099), max_len=4099),
+    "cfg4s": C[4].replace(num_seqs=10, lens=("uniform", 1, 1300), max_len=1300),
+    "cfg5s": C[5].replace(num_seqs=16, lens=("lognormal", 200, 1.0, 1, 1500), max_len=1500,
+                          prefix_groups=2, prefix_tokens=256),
+    "mha_bf16_d128": synth.Spec("mha bf16", 6, ("uniform", 1, 700), 8, 8, 128, 16, act="bf16",
+                                cache="bf16", max_len=700),
+    "g2_bf16": synth.Spec("G=2 bf16", 6, ("uniform", 1, 600), 8, 4, 128, 32, act="bf16",
+                          cache="bf16", max_len=600),
+    "mha_i8_f32q": synth.Spec("MHA int8, fp32 q", 5, ("uniform", 1, 500), 4, 4, 64, 16,
+                              act="f32", cache="i8", max_len=500),
+    "mha_bf16_d64": synth.Spec("MHA bf16 D64", 5, ("uniform", 1, 500), 4, 4, 64, 32, act="bf16",
+                               cache="bf16", max_len=500),
+    "g8_i8": synth.Spec("G=8 int8", 6, ("uniform", 1, 900), 32, 4, 128, 16, act="bf16",
+                        cache="i8", max_len=900),
+    "g4_b32": synth.Spec("G=4 B=32", 6, ("uniform", 1, 900), 16, 4, 128, 32, act="bf16",
+                         cache="bf16", max_len=900),
+    "mha_f32_d128_b32": synth.Spec("MHA fp32 D128 B32", 4, ("uniform", 1, 400), 2, 2, 128, 32,
+                                   act="f32", cache="f32", max_len=400),
+    "g2_i8_bf16q": synth.Spec("G=2 int8", 4, ("uniform", 1, 400), 4, 2, 64, 16, act="bf16",
+                              cache="i8", max_len=400),
+}
+
+_cache = {}
+
+
+def prepared(name, seed=7):
+    """(case, device case with filled pool, oracle pool, oracle output)."""
+    key = (name, seed)
+    if key not in _cache:
+        case = synth.make_case(SMALL[name], seed)
+        dc = to_device(case)
+        fill_pool(dc)
+        ok, ov = oracle.fill_cache(case)
+        ref = oracle.decode_case(case, ok, ov)
+        _cache[key] = (case, dc, ok, ov, ref)
+    return _cache[key]
+
+
+def sync():
+    torch.cuda.synchronize()
+
+
+# ---- write ------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_write_pool_byte_exact(name):
+    print(f"[write] {name}", flush=True)
+    case, dc, ok, ov, _ = prepared(name)
+    sync()
+    assert np.array_equal(dev_to_host(dc.k_cache).view(np.uint8), ok.view(np.uint8)), "k pool"
+    assert np.array_equal(dev_to_host(dc.v_cache).view(np.uint8), ov.view(np.uint8)), "v pool"
+
+
+def test_write_skips_negative_slots():
+    case = synth.make_case(SMALL["cfg4s"], 3)
+    dc = to_device(case)
+    k, v = poison_pool(case)
+    slots = dc.slot_mapping.clone()
+    slots[::2] = -1
+    pa.write_kv_cache(dc.key, dc.value, k, v, slots, dc.k_scale, dc.v_scale)
+    ok, ov = case.empty_pool()
+    oracle.write_kv_cache(case.key, case.value, ok, ov, slots.cpu().numpy(), case.k_scale,
+                          case.v_scale)
+    sync()
+    assert np.array_equal(dev_to_host(k), ok) and np.array_equal(dev_to_host(v), ov)
+
+
+def test_write_int8_near_ties():
+    """Quotients within half an fp32 ulp of a half-integer (double-rounding traps)."""
+    pairs = pins.near_tie_pairs()
+    n = len(pairs)
+    x = np.array([p[0] for p in pairs], np.float32)
+    for act in ("f32", "bf16"):
+        key = (synth.bf16_bits(x) if act == "bf16" else x).reshape(n, 1, 1)
+        key8 = np.repeat(key, 8, axis=2)                      # head_dim 8
+        ks = np.array([p[1] for p in pairs], np.float32).reshape(n, 1)
+        slots = np.arange(n, dtype=np.int64)
+        ok = np.full((n, 1, 1, 8), -128, np.int8)
+        ov = ok.copy()
+        oracle.write_kv_cache(key8, key8, ok, ov, slots, ks, ks)
+        k = torch.full((n, 1, 1, 8), -128, dtype=torch.int8, device="cuda")
+        v = k.clone()
+        kd = host_to_dev(key8, act, "cuda")
+        pa.write_kv_cache(kd, kd, k, v, torch.from_numpy(slots).cuda(),
+                          torch.from_numpy(ks).cuda(), torch.from_numpy(ks).cuda())
+        sync()
+        assert np.array_equal(dev_to_host(k), ok), act
+
+
+# ---- decode -----------------------------------------------------------------
+
+PARITY = [(n, 0) for n in SMALL] + [
+    ("cfg1", 16), ("cfg1", 32), ("cfg1", 112),
+    ("cfg2s", 64), ("cfg2s", 512), ("cfg2s", 2048),
+    ("cfg3s", 512), ("cfg3s", 256),
+    ("cfg4s", 128), ("cfg4s", 512),
+    ("cfg5s", 64), ("cfg5s", 512),
+    ("mha_bf16_d128", 128), ("g2_bf16", 96), ("mha_i8_f32q", 64), ("mha_bf16_d64", 64),
+    ("g8_i8", 256), ("g4_b32", 160), ("mha_f32_d128_b32", 96), ("g2_i8_bf16q", 48),
+]
+
+
+@pytest.mark.parametrize("name,P", PARITY)
+def test_decode_parity(name, P):
+    print(f"[decode] {name} P={P}", flush=True)
+    case, dc, ok, ov, ref = prepared(name)
+    out = run_decode(dc, P)
+    sync()
+    got = as_f64(out)
+    assert np.isfinite(got).all(), "non-finite output (poison leaked?)"
+    err = np.abs(got - ref).max()
+    assert err <= tol(case), f"{name} P={P}: max |gpu - oracle| = {err}"
+
+
+@pytest.mark.parametrize("name", ["cfg1", "cfg2s", "cfg5s", "g8_i8"])
+def test_splitk_partials(name):
+    """Each partition's (o_j, m_j, l_j) against the oracle's partials."""
+    case, dc, ok, ov, _ = prepared(name)
+    P = 64
+    S, Hq, D = case.S, case.Hq, case.D
+    ws = pa.workspace(S, Hq, D, case.max_context_len, P, "cuda")
+    for t in ws:
+        t.fill_(float("nan"))
+    pa.decode(None, dc.q, dc.k_cache, dc.v_cache, dc.block_tables, dc.context_lens,
+              float(case.scale), case.max_context_len, P, *ws, k_scale=dc.k_scale,
+              v_scale=dc.v_scale)
+    o, m, l = oracle.decode_partials(case.q, ok, ov, case.block_tables, case.context_lens,
+                                     case.scale, P, case.k_scale, case.v_scale)
+    sync()
+    go, gm, gl = (t.cpu().numpy().astype(np.float64) for t in ws)
+    n = -(-case.context_lens.astype(np.int64) // P)
+    for s in range(S):
+        assert np.isnan(go[s, :, n[s]:]).all(), "partition past the length was written"
+        sl = slice(0, n[s])
+        assert np.abs(go[s, :, sl] - o[s, :, sl]).max() <= tol(case)
+        assert np.abs(gm[s, :, sl] - m[s, :, sl]).max() <= 1e-4 * max(1.0, np.abs(m[s, :, sl]).max())
+        assert np.abs(gl[s, :, sl] / l[s, :, sl] - 1).max() <= 1e-4
+
+
+def test_reduce_from_oracle_partials():
+    """pa_decode_splitk_reduce fed the oracle's partials (rounded to fp32)."""
+    case = synth.make_case(SMALL["cfg2s"], 5)
+    ok, ov = oracle.fill_cache(case)
+    P = 128
+    o, m, l = oracle.decode_partials(case.q, ok, ov, case.block_tables, case.context_lens,
+                                     case.scale, P)
+    o32, m32, l32 = (np.nan_to_num(a, nan=0.0).astype(np.float32) for a in (o, m, l))
+    want = oracle.splitk_reduce(o32.astype(np.float64), m32.astype(np.float64),
+                                l32.astype(np.float64), case.context_lens, P)
+    for dt, tl in ((torch.float32, 1e-5), (torch.bfloat16, 1e-2)):
+        out = torch.empty((case.S, case.Hq, case.D), dtype=dt, device="cuda")
+        pa.decode_splitk_reduce(out, torch.from_numpy(o32).cuda(), torch.from_numpy(m32).cuda(),
+                                torch.from_numpy(l32).cuda(),
+                                torch.from_numpy(case.context_lens).cuda(),
+                                case.max_context_len, P)
+        sync()
+        assert np.abs(as_f64(out) - want).max() <= tl
+
+
+# ---- exactness ----------------------------------------------------------------
+
+def _onehot_case(spec, seed, tstar_of):
+    """q = 128 e_0, k_{t*} = 128 e_0, other k_0 = 0: the output is v_{t*} exactly."""
+    case = synth.make_case(spec, seed)
+    act = spec.act
+    idx, _, _ = pins.source_rows(case)
+    npre = len(case.pre_slots)
+    one = np.float32(128.0)
+    val = synth.bf16_bits(np.array([one]))[0] if act == "bf16" else one
+    zero = np.uint16(0) if act == "bf16" else np.float32(0)
+    pk, nk, q = case.pre_key.copy(), case.key.copy(), np.zeros_like(case.q)
+    pk[:, :, 0] = zero
+    nk[:, :, 0] = zero
+    q[:, :, 0] = val
+    ts = []
+    for s in range(case.S):
+        t = tstar_of(s, int(case.context_lens[s]))
+        ts.append(t)
+        slot = int(case.block_tables[s, t // case.B]) * case.B + t % case.B
+        r = idx[slot]
+        if r < npre:
+            pk[r, :, 0] = val
+        else:
+            nk[r - npre, :, 0] = val
+    new = dataclasses.replace(case, pre_key=pk, key=nk, q=q)
+    if spec.cache == "i8":
+        new.k_scale, new.v_scale = synth.absmax_scales(new)
+    return new, ts
+
+
+@pytest.mark.parametrize("name", ["cfg1", "cfg2s", "cfg4s", "cfg5s", "g2_bf16", "mha_i8_f32q"])
+@pytest.mark.parametrize("P", [0, 64])
+def test_onehot_bit_exact(name, P):
+    spec = SMALL[name]
+    rng = np.random.default_rng(11)
+    for rep in range(3):
+        case, ts = _onehot_case(spec, 20 + rep, lambda s, L: int(rng.integers(0, L)))
+        dc = to_device(case)
+        fill_pool(dc)
+        out = run_decode(dc, P)
+        sync()
+        got = as_f64(out)
+        G = case.Hq // case.Hkv
+        if spec.cache == "i8":
+            # the oracle's write fixes the dequantised row: codes * scale
+            ok, ov = oracle.fill_cache(case)
+            dense = pins.dense_kv(case, ok, ov)
+        else:
+            dense = pins.dense_kv(case)
+        for s, t in enumerate(ts):
+            # float caches: v_{t*} itself; int8: the fp32 product code * scale
+            want = np.repeat(dense[s][1][t].astype(np.float32), G, axis=0)
+            want_q = torch.from_numpy(want).to(TORCH_DT[spec.act])
+            assert np.array_equal(got[s], want_q.double().numpy()), f"{name} seq {s} t*={t}"
+
+
+@pytest.mark.parametrize("spec", [
+    synth.Spec("L1 f32", 6, ("const", 1), 4, 4, 64, 16, act="f32", cache="f32", max_len=16),
+    synth.Spec("L1 bf16 G4", 6, ("const", 1), 32, 8, 128, 16, act="bf16", cache="bf16",
+               max_len=16),
+    synth.Spec("L1 bf16 G8", 6, ("const", 1), 64, 8, 128, 32, act="bf16", cache="bf16",
+               max_len=32),
+    synth.Spec("L1 bf16 G1", 6, ("const", 1), 8, 8, 128, 16, act="bf16", cache="bf16",
+               max_len=16),
+], ids=lambda s: s.name)
+@pytest.mark.parametrize("P", [0, 16])
+def test_context_len_one_returns_v(spec, P):
+    case = synth.make_case(spec, 9)
+    dc = to_device(case)
+    fill_pool(dc)
+    out = run_decode(dc, P)
+    sync()
+    G = case.Hq // case.Hkv
+    want = np.repeat(case.value, G, axis=1)
+    assert np.array_equal(dev_to_host(out), want)
+
+
+@pytest.mark.parametrize("name", ["cfg1", "cfg2s", "cfg4s", "cfg5s", "g2_bf16"])
+def test_placement_invariance_bit_identical(name):
+    case, dc, _, _, _ = prepared(name)
+    base = dev_to_host(run_decode(dc, 0))
+    base_split = dev_to_host(run_decode(dc, 64))
+    variants = [synth.permute_placement(case, 31), synth.permute_placement(case, 32)]
+    if case.spec.prefix_groups:
+        variants.append(synth.unshare_prefixes(case))
+    for var in variants:
+        dv = to_device(var)
+        fill_pool(dv)
+        assert np.array_equal(dev_to_host(run_decode(dv, 0)), base)
+        assert np.array_equal(dev_to_host(run_decode(dv, 64)), base_split)
+
+
+def test_deterministic_repeat():
+    case, dc, _, _, _ = prepared("cfg5s")
+    a = dev_to_host(run_decode(dc, 64))
+    b = dev_to_host(run_decode(dc, 64))
+    assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("name", ["cfg1", "cfg2s", "cfg4s"])
+def test_zero_length_gives_zeros(name):
+    case, dc, ok, ov, ref = prepared(name)
+    lens = dc.context_lens.clone()
+    lens[1] = 0
+    for P in (0, 64):
+        out = torch.full_like(dc.q, float("nan"))
+        if P == 0:
+            pa.decode(out, dc.q, dc.k_cache, dc.v_cache, dc.block_tables, lens, float(case.scale),
+                      case.max_context_len, 0, k_scale=dc.k_scale, v_scale=dc.v_scale)
+        else:
+            ws = pa.workspace(case.S, case.Hq, case.D, case.max_context_len, P, "cuda")
+            pa.decode(None, dc.q, dc.k_cache, dc.v_cache, dc.block_tables, lens,
+                      float(case.scale), case.max_context_len, P, *ws, k_scale=dc.k_scale,
+                      v_scale=dc.v_scale)
+            pa.decode_splitk_reduce(out, *ws, lens, case.max_context_len, P)
+        sync()
+        got = as_f64(out)
+        assert (got[1] == 0).all()
+        keep = [s for s in range(case.S) if s != 1]
+        assert np.abs(got[keep] - ref[keep]).max() <= tol(case)
+
+
+def test_pa_check_rejects_bad_block_id(monkeypatch):
+    """PA_CHECK=1 validates device indices on the host: a block id past the
+    pool is reported and nothing is launched."""
+    case, dc, _, _, _ = prepared("cfg1")
+    bt = dc.block_tables.clone()
+    bt[0, 0] = case.num_blocks + 5
+    monkeypatch.setenv("PA_CHECK", "1")
+    out = torch.empty_like(dc.q)
+    with pytest.raises(pa.PAError) as e:
+        pa.decode(out, dc.q, dc.k_cache, dc.v_cache, bt, dc.context_lens, float(case.scale),
+                  case.max_context_len, 0)
+    assert e.value.status == -7
+    bad = dc.slot_mapping.clone()
+    bad[0] = case.num_blocks * case.B + 3
+    with pytest.raises(pa.PAError):
+        pa.write_kv_cache(dc.key, dc.value, dc.k_cache.clone(), dc.v_cache.clone(), bad)
+
+
+# ---- full-size workloads, sampled ---------------------------------------------
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+def test_full_size_sampled(cfg):
+    spec = C[cfg]
+    print(f"[full] cfg{cfg} generating", flush=True)
+    case = synth.make_case(spec, cfg)
+    dc = to_device(case)
+    print(f"[full] cfg{cfg} gpu write+decode P={spec.partition_size}", flush=True)
+    fill_pool(dc)
+    out = run_decode(dc, spec.partition_size)
+    sync()
+    got = as_f64(out)
+    assert np.isfinite(got).all()
+    print(f"[full] cfg{cfg} oracle", flush=True)
+    ok, ov = oracle.fill_cache(case)
+    assert np.array_equal(dev_to_host(dc.k_cache).view(np.uint8), ok.view(np.uint8))
+    assert np.array_equal(dev_to_host(dc.v_cache).view(np.uint8), ov.view(np.uint8))
+    L = case.context_lens
+    rng = np.random.default_rng(cfg)
+    seqs = sorted({int(np.argmax(L)), int(np.argmin(L)), 0, case.S - 1,
+                   *[int(x) for x in rng.choice(case.S, size=2, replace=False)]})
+    if cfg == 3:
+        seqs = seqs[:2]
+    ref = oracle.decode_case(case, ok, ov, seqs=seqs)
+    err = np.abs(got[seqs] - ref).max()
+    print(f"[full] cfg{cfg} seqs {seqs} max err {err:.3e}", flush=True)
+    assert err <= tol(case)
