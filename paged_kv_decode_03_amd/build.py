@@ -22,6 +22,8 @@ SOURCES = ["pa_api.cpp", "pa_write.hip", "pa_decode_valu.hip", "pa_decode_mfma.h
 CXXFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
     "-fno-fast-math", "-fhip-fp32-correctly-rounded-divide-sqrt",
+    # rounding exactly as written: fused multiply-adds only where fmaf() says so
+    "-ffp-contract=off",
     # no packed-fp32 instructions anywhere in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,

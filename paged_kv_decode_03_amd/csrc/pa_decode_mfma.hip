@@ -165,6 +165,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
             float x[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
+                // x is rounded once; the max and exp2(x - max) see the same x
                 x[i] = row_ror8_add(row_ror4_add(sacc[i])) * xs;
                 if (tail && (c << 4) + 4 * i + tg >= t1) x[i] = kNegInf;
             }

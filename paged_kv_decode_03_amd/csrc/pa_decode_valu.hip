@@ -150,6 +150,9 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(DecodeArgs a) {
             for (int i = 0; i < ND; ++i) dot = fmaf(qf[h][i], kf[i], dot);
             dot = quad_sum(dot);
             if (valid) {
+                // x is rounded once and both the max and exp(x - max) use
+                // that value, so the largest weight is exactly 1 (the build
+                // turns off fma contraction, which would break this)
                 const float x = dot * xs;
                 const float mnew = fmaxf(mrun[h], x);
                 const float alpha = __builtin_amdgcn_exp2f((mrun[h] - mnew) * kLog2e);

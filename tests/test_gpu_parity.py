@@ -206,7 +206,11 @@ def _onehot_case(spec, seed, tstar_of):
     q[:, :, 0] = val
     ts = []
     for s in range(case.S):
-        t = tstar_of(s, int(case.context_lens[s]))
+        # probe only tokens in blocks this sequence owns alone: a probe in a
+        # shared copy-on-write block would be seen by the whole group
+        L = int(case.context_lens[s])
+        own = [t for t in range(L) if case.refcount[case.block_tables[s, t // case.B]] == 1]
+        t = own[tstar_of(s, len(own))]
         ts.append(t)
         slot = int(case.block_tables[s, t // case.B]) * case.B + t % case.B
         r = idx[slot]
@@ -255,12 +259,12 @@ def test_onehot_bit_exact(name, P):
     synth.Spec("L1 bf16 G1", 6, ("const", 1), 8, 8, 128, 16, act="bf16", cache="bf16",
                max_len=16),
 ], ids=lambda s: s.name)
-@pytest.mark.parametrize("P", [0, 16])
-def test_context_len_one_returns_v(spec, P):
+@pytest.mark.parametrize("split", [False, True])
+def test_context_len_one_returns_v(spec, split):
     case = synth.make_case(spec, 9)
     dc = to_device(case)
     fill_pool(dc)
-    out = run_decode(dc, P)
+    out = run_decode(dc, case.B if split else 0)
     sync()
     G = case.Hq // case.Hkv
     want = np.repeat(case.value, G, axis=1)
