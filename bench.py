@@ -2,7 +2,9 @@
 
 One step = the whole decode hot path over one batch resident in HBM:
   pa_write_kv_cache (the new token of every sequence, slot-mapped)
-  -> pa_decode (split-K partitions) -> pa_decode_splitk_reduce.
+  -> pa_decode_balanced (work-balanced split-K with the log-sum-exp combine
+     in the same launch; --schedule partitions runs pa_decode over fixed
+     partitions followed by pa_decode_splitk_reduce instead).
 Default workload: the Llama-3-8B-shaped bf16 GQA batch (64 sequences,
 context lengths U[128, 2048], 32 query / 8 kv heads, head_dim 128, block 16,
 shuffled pool sized 1.25x the need, partition 512).
@@ -45,7 +47,7 @@ def kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(cfg: int, partition: int):
+def measured_traffic(cfg: int, partition: int, schedule: str):
     """HBM bytes per decode launch from committed rocprofv3 counter runs, if
     they were taken on the current kernel source; else None."""
     path = os.path.join(ROOT, "profiles", "decode_traffic.json")
@@ -53,7 +55,7 @@ def measured_traffic(cfg: int, partition: int):
         return None
     with open(path) as fh:
         rec = json.load(fh)
-    ent = rec.get(f"cfg{cfg}_P{partition}")
+    ent = rec.get(f"cfg{cfg}_P{partition}_{schedule}")
     if not ent or ent.get("kernel_hash") != kernel_hash():
         return None
     return ent.get("bytes_per_launch")
@@ -82,16 +84,39 @@ def cpu_baseline(case, budget_s: float):
                       f"{reps} repetitions in {el:.1f} s, fp64"}
 
 
+def copy_probe(torch, nbytes=1 << 30, reps=10):
+    src = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    print(json.dumps({"probe": "device copy", "read_bytes": nbytes, "write_bytes": nbytes,
+                      "us_per_copy": round(ms * 1e3, 2),
+                      "copy_gbs": round(2 * nbytes / (ms * 1e-3) / 1e9, 1)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
-    ap.add_argument("--partition", type=int, default=None, help="split-K partition (tokens)")
+    ap.add_argument("--partition", type=int, default=None,
+                    help="split-K partition, or the smallest balanced piece (tokens)")
+    ap.add_argument("--schedule", choices=["balanced", "partitions"], default="balanced")
     ap.add_argument("--rotate-gb", type=float, default=2.0)
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only time a device copy of 1 GiB (read 1 GiB + write 1 GiB); the "
+                         "reference for calibrating rocprofv3 FETCH_SIZE / WRITE_SIZE")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -101,6 +126,10 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.copy_probe:
+        copy_probe(torch)
+        return
 
     import paged_kv_decode_03_amd as pa
     import synth
@@ -119,7 +148,11 @@ def main():
     pools = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(R - 1)]
     maxL = case.max_context_len
     S, Hq, D = case.S, case.Hq, case.D
-    ws = pa.workspace(S, Hq, D, maxL, max(P, 1), dev)
+    balanced = args.schedule == "balanced"
+    if balanced:
+        ws = pa.balanced_workspace(S, Hq, case.Hkv, D, maxL, P, dev)
+    else:
+        ws = pa.workspace(S, Hq, D, maxL, max(P, 1), dev)
     out = torch.empty_like(dc.q)
     scale = float(case.scale)
     stream = torch.cuda.current_stream(dev)
@@ -129,7 +162,10 @@ def main():
         pa.write_kv_cache(dc.key, dc.value, k, v, dc.slot_mapping, dc.k_scale, dc.v_scale)
         if ev is not None:
             ev[0].record(stream)
-        if P > 0:
+        if balanced:
+            pa.decode_balanced(out, dc.q, k, v, dc.block_tables, dc.context_lens, scale, maxL, P,
+                               *ws, k_scale=dc.k_scale, v_scale=dc.v_scale)
+        elif P > 0:
             pa.decode(None, dc.q, k, v, dc.block_tables, dc.context_lens, scale, maxL, P, *ws,
                       k_scale=dc.k_scale, v_scale=dc.v_scale)
         else:
@@ -137,7 +173,7 @@ def main():
                       k_scale=dc.k_scale, v_scale=dc.v_scale)
         if ev is not None:
             ev[1].record(stream)
-        if P > 0:
+        if not balanced and P > 0:
             pa.decode_splitk_reduce(out, *ws, dc.context_lens, maxL, P)
 
     for i in range(args.warmup):
@@ -161,7 +197,7 @@ def main():
     step_bytes = tr["decode"]["total"] + tr["write"]
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = tr["decode"]["total"] / (dec_mean * 1e-3) / 1e9
-    traffic = measured_traffic(args.config, P)
+    traffic = measured_traffic(args.config, P, args.schedule)
     res = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -180,7 +216,9 @@ def main():
             "num_kv_heads": case.Hkv, "head_dim": D, "block_size": case.B,
             "context_lens": list(spec.lens), "sum_context": tr["sum_len"],
             "unique_kv_tokens": tr["unique_tokens"], "partition_size": P, "pool_copies": R,
-            "step": "write + split-K decode + reduce" if P else "write + one-pass decode",
+            "schedule": args.schedule,
+            "step": ("write + balanced split-K decode (combine fused)" if balanced else
+                     "write + split-K decode + reduce" if P else "write + one-pass decode"),
         },
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "seq_tokens_per_s": round(S / (ms_per_step * 1e-3), 1),
@@ -193,7 +231,9 @@ def main():
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": traffic, "kernel": "pa_decode (split-K partials)" if P else "pa_decode",
+            "traffic": traffic,
+            "kernel": ("pa_decode_balanced" if balanced else
+                       "pa_decode (split-K partials)" if P else "pa_decode"),
             "bytes_per_launch": tr["decode"]["total"],
         },
         "cpu_baseline": None,

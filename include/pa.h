@@ -157,13 +157,53 @@ int pa_decode(void *out, const void *q, const void *k_cache, const void *v_cache
               float *tmp_sum, pa_dtype q_dtype, pa_dtype cache_dtype, void *stream);
 
 /*
+ * pa_decode_balanced -- the same decode attention as pa_decode, scheduled so
+ * that every workgroup streams the same amount of KV whatever the mix of
+ * context lengths, with the log-sum-exp combination of split contexts done
+ * in the same launch; writes `out` directly (no separate reduce).
+ *
+ * Schedule: all (sequence, kv head) contexts are laid end to end as one list
+ * of 16-token chunks; a persistent grid (resident workgroups per CU times the
+ * CU count) splits it into equal contiguous ranges of at least
+ * min_piece_tokens / 16 chunks. A context inside one range is finished in
+ * place. A context cut by range ends leaves one partial per piece in the
+ * workspace; the workgroup that completes its last piece (an atomic counter
+ * per (sequence, kv head)) combines the pieces exactly as
+ * pa_decode_splitk_reduce would, writes `out`, and resets the counter.
+ *
+ *   out, q, k_cache, v_cache, block_tables, context_lens, k_scale, v_scale,
+ *   scale, num_seqs .. max_context_len, q_dtype, cache_dtype: as pa_decode.
+ *   min_piece_tokens  smallest piece a range may be cut to, a multiple of 16.
+ *   tmp_out       [num_seqs][num_heads][NS][head_dim] fp32, tmp_max and tmp_sum
+ *                 [num_seqs][num_heads][NS] fp32, NS = pa_balanced_slots(
+ *                 max_context_len, min_piece_tokens). Contents on return are
+ *                 unspecified.
+ *   counters      [num_seqs][num_kv_heads] int32, all zero before the call; the
+ *                 call leaves them all zero again (zero them once, reuse).
+ * Calls that share `counters` or the workspace must not overlap in time
+ * (e.g. run them on one stream). Supported instances: as pa_decode.
+ * Alignment: out, q, k_cache, v_cache, tmp_out 16-byte aligned.
+ */
+int pa_decode_balanced(void *out, const void *q, const void *k_cache, const void *v_cache,
+                       const int32_t *block_tables, int max_blocks_per_seq,
+                       const int32_t *context_lens, const float *k_scale, const float *v_scale,
+                       float scale, int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                       int block_size, int64_t num_blocks, int max_context_len,
+                       int min_piece_tokens, float *tmp_out, float *tmp_max, float *tmp_sum,
+                       int32_t *counters, pa_dtype q_dtype, pa_dtype cache_dtype, void *stream);
+
+/* Workspace slots per (sequence, query head) that pa_decode_balanced needs:
+ * ceil(ceil(max_context_len / 16) / (min_piece_tokens / 16)) + 1, or 0 when
+ * max_context_len <= 0 or min_piece_tokens < 16. */
+int pa_balanced_slots(int max_context_len, int min_piece_tokens);
+
+/*
  * pa_decode_splitk_reduce -- log-sum-exp combination of split-K partials.
  * For each (s, h), over j < n = ceil(L_s / partition_size):
  *   M = max_j tmp_max[j], W_j = tmp_sum[j] * exp(tmp_max[j] - M),
  *   out[s][h][:] = sum_j W_j tmp_out[j][:] / sum_j W_j      (0 when n = 0),
  * rounded to out_dtype (F32 or BF16, round to nearest even).
- * Arguments as in pa_decode; head_dim a multiple of 2 in [2, 1024];
- * out and tmp_out 16-byte aligned.
+ * Arguments as in pa_decode; head_dim in [1, 1024].
  */
 int pa_decode_splitk_reduce(void *out, const float *tmp_out, const float *tmp_max,
                             const float *tmp_sum, const int32_t *context_lens, int num_seqs,

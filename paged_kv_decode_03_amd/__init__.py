@@ -1,7 +1,7 @@
 """Paged-attention decode for MI355X (gfx950): Python binding of libpa.so.
 
 Argument marshalling only: every step of the decode path runs in the HIP
-kernels of ``libpa.so`` (built by ``python -m paged_kv_decode_03_amd.build``).
+kernels of ``libpa.so`` (built by ``python paged_kv_decode_03_amd/build.py``).
 Torch tensors supply device memory and the current stream; the functions
 check dtype, device, shape and contiguity, then call the C ABI declared in
 ``include/pa.h`` with raw pointers. There is no fallback: if the library is
@@ -11,8 +11,9 @@ Entry points (same names as the C ABI without the ``pa_`` prefix):
   write_kv_cache           slot-mapped write of new K/V (copy or int8)
   decode                   paged decode attention (one pass or split-K partials)
   decode_splitk_reduce     log-sum-exp reduce of split-K partials
-plus ``workspace`` (allocates the split-K partials with torch) and
-``paged_attention`` (decode + reduce into a new output tensor).
+  decode_balanced          work-balanced split-K decode with the reduce fused in
+plus ``workspace`` / ``balanced_workspace`` (allocate with torch) and
+``paged_attention`` (decode into a new output tensor, any schedule).
 """
 from __future__ import annotations
 
@@ -25,7 +26,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libpa.so")
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is not built; run `python -m paged_kv_decode_03_amd.build`")
+    raise ImportError(f"{LIB_PATH} is not built; run `python paged_kv_decode_03_amd/build.py`")
 
 _lib = ctypes.CDLL(LIB_PATH)
 _p, _i, _i64, _f = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
@@ -39,6 +40,11 @@ _lib.pa_write_kv_cache.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _
 _lib.pa_decode.restype = _i
 _lib.pa_decode.argtypes = [_p, _p, _p, _p, _p, _i, _p, _p, _p, _f, _i, _i, _i, _i, _i, _i64, _i,
                            _i, _p, _p, _p, _i, _i, _p]
+_lib.pa_decode_balanced.restype = _i
+_lib.pa_decode_balanced.argtypes = [_p, _p, _p, _p, _p, _i, _p, _p, _p, _f, _i, _i, _i, _i, _i,
+                                    _i64, _i, _i, _p, _p, _p, _p, _i, _i, _p]
+_lib.pa_balanced_slots.restype = _i
+_lib.pa_balanced_slots.argtypes = [_i, _i]
 _lib.pa_decode_splitk_reduce.restype = _i
 _lib.pa_decode_splitk_reduce.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p]
 
@@ -161,6 +167,51 @@ def decode_splitk_reduce(out, tmp_out, tmp_max, tmp_sum, context_lens, max_conte
     _check("pa_decode_splitk_reduce", rc)
 
 
+def balanced_slots(max_context_len: int, min_piece_tokens: int) -> int:
+    return _lib.pa_balanced_slots(int(max_context_len), int(min_piece_tokens))
+
+
+def decode_balanced(out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                    max_context_len, min_piece_tokens, tmp_out, tmp_max, tmp_sum, counters,
+                    k_scale=None, v_scale=None, stream=None):
+    """Work-balanced decode into ``out`` [S, Hq, D]; ``counters`` [S, Hkv] int32
+    must be zero on entry and is zero again on return."""
+    dev = _dev(out, q, k_cache, v_cache, block_tables, context_lens, tmp_out, tmp_max, tmp_sum,
+               counters, k_scale, v_scale)
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32 \
+            or counters.dtype != torch.int32:
+        raise TypeError("block_tables, context_lens and counters must be int32")
+    S, Hq, D = q.shape
+    NB, Hkv, B, D2 = k_cache.shape
+    if D2 != D or v_cache.shape != k_cache.shape or block_tables.shape[0] != S \
+            or context_lens.shape != (S,) or out.shape != q.shape \
+            or counters.numel() < S * Hkv:
+        raise ValueError("shape mismatch")
+    ns = balanced_slots(max_context_len, min_piece_tokens)
+    if tmp_out.numel() < S * Hq * ns * D or tmp_max.numel() < S * Hq * ns \
+            or tmp_sum.numel() < S * Hq * ns:
+        raise ValueError("workspace too small")
+    if out.dtype != q.dtype:
+        raise TypeError("out must have the dtype of q")
+    rc = _lib.pa_decode_balanced(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                 _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
+                                 _ptr(k_scale), _ptr(v_scale), float(scale), S, Hq, Hkv, D, B, NB,
+                                 int(max_context_len), int(min_piece_tokens), _ptr(tmp_out),
+                                 _ptr(tmp_max), _ptr(tmp_sum), _ptr(counters), _dt(q),
+                                 _dt(k_cache), _stream(stream, dev))
+    _check("pa_decode_balanced", rc)
+
+
+def balanced_workspace(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len,
+                       min_piece_tokens, device):
+    """(tmp_out, tmp_max, tmp_sum, counters) for decode_balanced; counters zeroed."""
+    ns = max(1, balanced_slots(max_context_len, min_piece_tokens))
+    return (torch.empty((num_seqs, num_heads, ns, head_dim), dtype=torch.float32, device=device),
+            torch.empty((num_seqs, num_heads, ns), dtype=torch.float32, device=device),
+            torch.empty((num_seqs, num_heads, ns), dtype=torch.float32, device=device),
+            torch.zeros((num_seqs, num_kv_heads), dtype=torch.int32, device=device))
+
+
 def workspace(num_seqs, num_heads, head_dim, max_context_len, partition_size, device):
     """Split-K partials (tmp_out [S,Hq,NP,D], tmp_max, tmp_sum [S,Hq,NP]) fp32."""
     NP = max(1, num_partitions(max_context_len, partition_size))
@@ -170,14 +221,25 @@ def workspace(num_seqs, num_heads, head_dim, max_context_len, partition_size, de
 
 
 def paged_attention(q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
-                    partition_size=0, k_scale=None, v_scale=None, ws=None, stream=None):
-    """Decode attention into a new tensor: one pass, or split-K + reduce."""
+                    partition_size=0, k_scale=None, v_scale=None, ws=None, stream=None,
+                    balanced=False):
+    """Decode attention into a new tensor: one pass (partition_size 0), split-K
+    partitions + reduce, or (balanced=True) the work-balanced schedule with
+    pieces of at least partition_size tokens."""
     out = torch.empty_like(q)
+    S, Hq, D = q.shape
+    if balanced:
+        if ws is None:
+            ws = balanced_workspace(S, Hq, k_cache.shape[1], D, max_context_len, partition_size,
+                                    q.device)
+        decode_balanced(out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                        max_context_len, partition_size, *ws, k_scale=k_scale, v_scale=v_scale,
+                        stream=stream)
+        return out
     if partition_size == 0:
         decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len, 0,
                k_scale=k_scale, v_scale=v_scale, stream=stream)
         return out
-    S, Hq, D = q.shape
     if ws is None:
         ws = workspace(S, Hq, D, max_context_len, partition_size, q.device)
     decode(None, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,

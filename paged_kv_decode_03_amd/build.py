@@ -1,8 +1,9 @@
 """Build libpa.so (HIP kernels for gfx950 + the C ABI) in-tree with hipcc.
 
 Each translation unit under csrc/ is compiled separately (in parallel), then
-linked into paged_kv_decode_03_amd/libpa.so. Run ``python -m
-paged_kv_decode_03_amd.build``; ``__graft_entry__.build()`` calls :func:`build`.
+linked into paged_kv_decode_03_amd/libpa.so. Run ``python
+paged_kv_decode_03_amd/build.py`` (as a file: importing the package loads the
+library being built); ``__graft_entry__.build()`` loads this file by path.
 """
 from __future__ import annotations
 

@@ -6,6 +6,9 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <map>
+#include <mutex>
+#include <utility>
 #include <vector>
 
 #include "pa.h"
@@ -13,7 +16,8 @@
 
 namespace {
 
-constexpr int kVersion = 10000;   // 1.0.0
+constexpr int kVersion = 10100;   // 1.1.0
+constexpr int NW_THREADS = 256;   // threads per decode workgroup
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -40,7 +44,74 @@ bool fetch(std::vector<T>& host, const T* dev, int64_t n, hipStream_t st) {
     return hipMemcpy(host.data(), dev, sizeof(T) * (size_t)n, hipMemcpyDeviceToHost) == hipSuccess;
 }
 
+// Shared validation of the decode arguments (both schedules).
+int check_decode(const void* q, const void* k_cache, const void* v_cache,
+                 const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
+                 const float* k_scale, const float* v_scale, int num_seqs, int num_heads,
+                 int num_kv_heads, int head_dim, int block_size, int64_t num_blocks,
+                 int max_context_len, int partition_size, pa_dtype q_dtype, pa_dtype cache_dtype) {
+    if (num_seqs < 0 || num_heads < 1 || num_kv_heads < 1 || num_heads % num_kv_heads ||
+        head_dim < 1 || block_size < 1 || max_blocks_per_seq < 1 || num_blocks < 1 ||
+        max_context_len < 0 || partition_size < 0)
+        return PA_ERR_SHAPE;
+    if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size) return PA_ERR_SHAPE;
+    if (!valid_act(q_dtype) || !valid_cache(cache_dtype)) return PA_ERR_DTYPE;
+    if (cache_dtype != PA_I8 && cache_dtype != q_dtype) return PA_ERR_DTYPE;
+    if (!q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_NULL;
+    if (cache_dtype == PA_I8 && (!k_scale || !v_scale)) return PA_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_ALIGN;
+    return PA_OK;
+}
+
+// PA_CHECK=1: device indices against the pool and the length bound.
+int check_indices(const int32_t* block_tables, int max_blocks_per_seq,
+                  const int32_t* context_lens, int num_seqs, int block_size, int64_t num_blocks,
+                  int max_context_len, hipStream_t st) {
+    std::vector<int32_t> lens, tables;
+    if (!fetch(lens, context_lens, num_seqs, st) ||
+        !fetch(tables, block_tables, (int64_t)num_seqs * max_blocks_per_seq, st))
+        return PA_ERR_LAUNCH;
+    for (int s = 0; s < num_seqs; ++s) {
+        if (lens[s] < 0 || lens[s] > max_context_len) return PA_ERR_INDEX;
+        const int nb = (lens[s] + block_size - 1) / block_size;
+        for (int b = 0; b < nb; ++b) {
+            const int32_t id = tables[(size_t)s * max_blocks_per_seq + b];
+            if (id < 0 || id >= num_blocks) return PA_ERR_INDEX;
+        }
+    }
+    return PA_OK;
+}
+
 }  // namespace
+
+namespace pa {
+
+// Resident workgroups per CU (occupancy calculator) times the CU count of the
+// stream's device, remembered per (kernel, device).
+int balanced_grid(const void* kernel, hipStream_t st) {
+    static std::mutex mu;
+    static std::map<std::pair<const void*, int>, int> cache;
+    int dev = 0;
+    if (st ? hipStreamGetDevice(st, &dev) != hipSuccess : hipGetDevice(&dev) != hipSuccess)
+        return -1;
+    {
+        std::lock_guard<std::mutex> lk(mu);
+        auto it = cache.find({kernel, dev});
+        if (it != cache.end()) return it->second;
+    }
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return -1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, NW_THREADS, 0) !=
+        hipSuccess)
+        return -1;
+    const int grid = cus * (per_cu > 0 ? per_cu : 1);
+    std::lock_guard<std::mutex> lk(mu);
+    cache[{kernel, dev}] = grid;
+    return grid;
+}
+
+}  // namespace pa
 
 extern "C" {
 
@@ -100,26 +171,20 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
               int num_heads, int num_kv_heads, int head_dim, int block_size, int64_t num_blocks,
               int max_context_len, int partition_size, float* tmp_out, float* tmp_max,
               float* tmp_sum, pa_dtype q_dtype, pa_dtype cache_dtype, void* stream) {
-    if (num_seqs < 0 || num_heads < 1 || num_kv_heads < 1 || num_heads % num_kv_heads ||
-        head_dim < 1 || block_size < 1 || max_blocks_per_seq < 1 || num_blocks < 1 ||
-        max_context_len < 0 || partition_size < 0)
-        return PA_ERR_SHAPE;
-    if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size) return PA_ERR_SHAPE;
+    int rc = check_decode(q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                          k_scale, v_scale, num_seqs, num_heads, num_kv_heads, head_dim,
+                          block_size, num_blocks, max_context_len, partition_size, q_dtype,
+                          cache_dtype);
+    if (rc) return rc;
     if (partition_size > 0 && partition_size % block_size) return PA_ERR_SHAPE;
-    if (!valid_act(q_dtype) || !valid_cache(cache_dtype)) return PA_ERR_DTYPE;
-    if (cache_dtype != PA_I8 && cache_dtype != q_dtype) return PA_ERR_DTYPE;
     const bool split = partition_size > 0;
-    if (!q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_NULL;
     if (split ? (!tmp_out || !tmp_max || !tmp_sum) : !out) return PA_ERR_NULL;
-    if (cache_dtype == PA_I8 && (!k_scale || !v_scale)) return PA_ERR_NULL;
-    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) ||
-        (split ? !aligned16(tmp_out) : !aligned16(out)))
-        return PA_ERR_ALIGN;
+    if (split ? !aligned16(tmp_out) : !aligned16(out)) return PA_ERR_ALIGN;
     const int np = split ? pa_num_partitions(max_context_len, partition_size) : 1;
 
     pa::DecodeArgs a{out, q, k_cache, v_cache, block_tables, context_lens, k_scale, v_scale,
-                     tmp_out, tmp_max, tmp_sum, scale, num_seqs, num_heads, num_kv_heads,
-                     head_dim, block_size, max_blocks_per_seq, partition_size, np,
+                     tmp_out, tmp_max, tmp_sum, nullptr, scale, num_seqs, num_heads,
+                     num_kv_heads, head_dim, block_size, max_blocks_per_seq, partition_size, np,
                      (pa::Dtype)q_dtype, (pa::Dtype)cache_dtype};
     const bool mfma = pa::mfma_supports(a);
     if (!mfma && !pa::valu_supports(a)) return PA_ERR_UNSUPPORTED;
@@ -129,20 +194,57 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
 
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     if (check_enabled()) {
-        std::vector<int32_t> lens, tables;
-        if (!fetch(lens, context_lens, num_seqs, st) ||
-            !fetch(tables, block_tables, (int64_t)num_seqs * max_blocks_per_seq, st))
-            return PA_ERR_LAUNCH;
-        for (int s = 0; s < num_seqs; ++s) {
-            if (lens[s] < 0 || lens[s] > max_context_len) return PA_ERR_INDEX;
-            const int nb = (lens[s] + block_size - 1) / block_size;
-            for (int b = 0; b < nb; ++b) {
-                const int32_t id = tables[(size_t)s * max_blocks_per_seq + b];
-                if (id < 0 || id >= num_blocks) return PA_ERR_INDEX;
-            }
-        }
+        rc = check_indices(block_tables, max_blocks_per_seq, context_lens, num_seqs, block_size,
+                           num_blocks, max_context_len, st);
+        if (rc) return rc;
     }
-    return launch_status(mfma ? pa::launch_decode_mfma(a, st) : pa::launch_decode_valu(a, st));
+    const pa::Schedule sch = pa::Schedule::Partitions;
+    return launch_status(mfma ? pa::launch_decode_mfma(a, sch, st)
+                              : pa::launch_decode_valu(a, sch, st));
+}
+
+int pa_balanced_slots(int max_context_len, int min_piece_tokens) {
+    if (max_context_len <= 0 || min_piece_tokens < 16) return 0;
+    const int64_t chunks = ((int64_t)max_context_len + 15) / 16;
+    const int64_t minc = min_piece_tokens / 16;
+    return (int)((chunks + minc - 1) / minc + 1);
+}
+
+int pa_decode_balanced(void* out, const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* block_tables, int max_blocks_per_seq,
+                       const int32_t* context_lens, const float* k_scale, const float* v_scale,
+                       float scale, int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                       int block_size, int64_t num_blocks, int max_context_len,
+                       int min_piece_tokens, float* tmp_out, float* tmp_max, float* tmp_sum,
+                       int32_t* counters, pa_dtype q_dtype, pa_dtype cache_dtype, void* stream) {
+    int rc = check_decode(q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                          k_scale, v_scale, num_seqs, num_heads, num_kv_heads, head_dim,
+                          block_size, num_blocks, max_context_len, min_piece_tokens, q_dtype,
+                          cache_dtype);
+    if (rc) return rc;
+    if (min_piece_tokens < 16 || min_piece_tokens % 16) return PA_ERR_SHAPE;
+    if (!out || !tmp_out || !tmp_max || !tmp_sum || !counters) return PA_ERR_NULL;
+    if (!aligned16(out) || !aligned16(tmp_out)) return PA_ERR_ALIGN;
+    const int ns = pa_balanced_slots(max_context_len, min_piece_tokens);
+    pa::DecodeArgs a{out, q, k_cache, v_cache, block_tables, context_lens, k_scale, v_scale,
+                     tmp_out, tmp_max, tmp_sum, counters, scale, num_seqs, num_heads,
+                     num_kv_heads, head_dim, block_size, max_blocks_per_seq, min_piece_tokens,
+                     ns > 0 ? ns : 1, (pa::Dtype)q_dtype, (pa::Dtype)cache_dtype};
+    const bool mfma = pa::mfma_supports(a);
+    if (!mfma && !pa::valu_supports(a)) return PA_ERR_UNSUPPORTED;
+    if ((int64_t)num_kv_heads * (((int64_t)max_context_len + 15) / 16) * num_seqs > 0x7fffffff)
+        return PA_ERR_SHAPE;
+    if (num_seqs == 0) return PA_OK;
+
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (check_enabled()) {
+        rc = check_indices(block_tables, max_blocks_per_seq, context_lens, num_seqs, block_size,
+                           num_blocks, max_context_len, st);
+        if (rc) return rc;
+    }
+    const pa::Schedule sch = pa::Schedule::Balanced;
+    return launch_status(mfma ? pa::launch_decode_mfma(a, sch, st)
+                              : pa::launch_decode_valu(a, sch, st));
 }
 
 int pa_decode_splitk_reduce(void* out, const float* tmp_out, const float* tmp_max,

@@ -1,4 +1,4 @@
-// Paged decode attention, MFMA kernel for grouped-query attention (G = 4, 8
+// Paged decode attention, MFMA core for grouped-query attention (G = 4, 8
 // query heads per kv head; head_dim 128; bf16 queries; bf16 or int8 cache).
 //
 // Method: "PagedAttention kernel ... gathers KV data from non-contiguous
@@ -33,74 +33,79 @@
 namespace pa {
 namespace {
 
-constexpr int NW = 4;
-constexpr int D = 128;
+template <int G_, Dtype CT>
+struct MfmaCore {
+    static constexpr int G = G_;
+    static constexpr int D = 128;
+    static constexpr bool BASE2 = true;
+    static constexpr int NHB = G / 4;           // 4-head groups
+    static constexpr bool Q8 = (CT == I8);
+    static constexpr int CE = Q8 ? 1 : 2;        // cache bytes per element
 
-template <int G, Dtype CT>
-__global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
-    constexpr int NHB = G / 4;                 // 4-head groups
-    constexpr bool Q8 = (CT == I8);
-    constexpr int CE = Q8 ? 1 : 2;
-
-    __shared__ WaveStates<NW, G, D> st;
-
-    const WorkItem wi = work_item(a);
-    const int g = wi.g, s = wi.s, j = wi.j;
-    const int L = a.context_lens[s];
-    const int P = a.partition_size > 0 ? a.partition_size : L;
-    const int t0 = j * P;
-    if (L == 0 || t0 >= L) {
-        if (a.partition_size == 0) store_zeros<G, D>(a, s, g);
-        return;
-    }
-    const int t1 = min(L, t0 + P);
-    const int c0 = t0 >> 4, c1 = (t1 + 15) >> 4;
-
-    const int lane = threadIdx.x & 63;
-    const int wave = uniform(threadIdx.x >> 6);
-    const int j4 = lane & 3, qd = (lane >> 2) & 3, tg = lane >> 4;
-
-    // Query operands. bf16 cache: dims 8*(4m+qd) .. +7 for m = 0..3.
-    // int8 cache: dims 16*(4m+qd) .. +15 for m = 0..1 (two 16-byte halves).
-    uint4 qr[NHB][4];
-#pragma unroll
-    for (int hb = 0; hb < NHB; ++hb) {
-        const uint16_t* qrow =
-            (const uint16_t*)a.q + ((int64_t)s * a.num_heads + g * G + hb * 4 + j4) * D;
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-            qr[hb][m] = Q8 ? ld16(qrow + 16 * (4 * (m >> 1) + qd) + 8 * (m & 1))
-                           : ld16(qrow + 8 * (4 * m + qd));
-    }
-
-    float mrun[NHB], lrun[NHB];
-    f32x4 acc[NHB][8];
-#pragma unroll
-    for (int hb = 0; hb < NHB; ++hb) {
-        mrun[hb] = kNegInf;
-        lrun[hb] = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[hb][e] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    }
-
-    const float sl2 = a.scale * kLog2e;
-    const int shift = (a.block_size == 32) ? 1 : 0;
-    const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
-    const int64_t head_stride = (int64_t)a.block_size * D;
-    const int64_t block_stride = head_stride * a.num_kv_heads;
-    // byte offsets inside a 16-token chunk
-    const int k_off = (4 * j4 + tg) * D * CE + (Q8 ? 16 * qd : 16 * qd);
-    const int v_off = tg * D * CE + (lane & 15) * 8 * CE;
-
+    struct State {
+        float m[NHB], l[NHB];
+        f32x4 acc[NHB][8];                       // acc[hb][e][i]: dim 8*(4*qd+i)+e
+    };
     struct Chunk {
         uint4 k[4];        // bf16: pieces m = 0..3; int8: k[0], k[1] used
         uint4 v[4];        // bf16: one 16-byte load per step; int8: .x/.y of each
         float ks, vs;
     };
-    auto load = [&](int c) {
+
+    const DecodeArgs& a;
+    int lane, j4, qd, tg;
+    int k_off, v_off;                            // byte offsets inside a chunk
+    float sl2;
+    int shift;
+    int64_t head_stride, block_stride;
+    // per segment
+    const int32_t* bt;
+    int g;
+    uint4 qr[NHB][4];
+
+    __device__ explicit MfmaCore(const DecodeArgs& args) : a(args) {
+        lane = threadIdx.x & 63;
+        j4 = lane & 3;
+        qd = (lane >> 2) & 3;
+        tg = lane >> 4;
+        k_off = (4 * j4 + tg) * D * CE + 16 * qd;
+        v_off = tg * D * CE + (lane & 15) * 8 * CE;
+        sl2 = a.scale * kLog2e;
+        shift = (a.block_size == 32) ? 1 : 0;
+        head_stride = (int64_t)a.block_size * D;
+        block_stride = head_stride * a.num_kv_heads;
+    }
+
+    // Query operands. bf16 cache: dims 8*(4m+qd) .. +7 for m = 0..3.
+    // int8 cache: dims 16*(4(m>>1)+qd) + 8(m&1) .. +7.
+    __device__ void begin_segment(int s, int g_) {
+        g = g_;
+        bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+#pragma unroll
+        for (int hb = 0; hb < NHB; ++hb) {
+            const uint16_t* qrow =
+                (const uint16_t*)a.q + ((int64_t)s * a.num_heads + g * G + hb * 4 + j4) * D;
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+                qr[hb][m] = Q8 ? ld16(qrow + 16 * (4 * (m >> 1) + qd) + 8 * (m & 1))
+                               : ld16(qrow + 8 * (4 * m + qd));
+        }
+    }
+
+    __device__ void init(State& S) const {
+#pragma unroll
+        for (int hb = 0; hb < NHB; ++hb) {
+            S.m[hb] = kNegInf;
+            S.l[hb] = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) S.acc[hb][e] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        }
+    }
+
+    __device__ Chunk load(int c) const {
         Chunk ch;
-        const int phys = bt[c >> shift];
-        const int64_t off = phys * block_stride + g * head_stride + (int64_t)(c & shift) * 16 * D;
+        const int phys = ld_const(bt, c >> shift);
+        const int64_t off = phys * block_stride + g * head_stride + (int64_t)(c & shift) * CHUNK * D;
         const char* kp = (const char*)a.k_cache + off * CE + k_off;
         const char* vp = (const char*)a.v_cache + off * CE + v_off;
         if constexpr (Q8) {
@@ -112,8 +117,8 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
                 const uint2 w = ld8(vp + step * 4 * D);
                 ch.v[step] = make_uint4(w.x, w.y, 0, 0);
             }
-            ch.ks = a.k_scale[(int64_t)phys * a.num_kv_heads + g];
-            ch.vs = a.v_scale[(int64_t)phys * a.num_kv_heads + g];
+            ch.ks = ld_const(a.k_scale, (int64_t)phys * a.num_kv_heads + g);
+            ch.vs = ld_const(a.v_scale, (int64_t)phys * a.num_kv_heads + g);
         } else {
 #pragma unroll
             for (int m = 0; m < 4; ++m) ch.k[m] = ld16(kp + 64 * m);
@@ -122,17 +127,12 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
             ch.ks = ch.vs = 1.0f;
         }
         return ch;
-    };
+    }
 
-    int c = c0 + wave;
-    Chunk cur;
-    if (c < c1) cur = load(c);
-    for (; c < c1; c += NW) {
-        Chunk nxt;
-        if (c + NW < c1) nxt = load(c + NW);
-        const bool tail = ((c + 1) << 4) > t1;
+    __device__ void step(State& S, const Chunk& cur, int c, int t1) const {
+        const bool tail = ((c + 1) * CHUNK) > t1;
 
-        // ---- logits: x[hb][i] for token 4*i + tg, head 4*hb + j4 ----------
+        // ---- logits: x[hb][i] for token 4*i + tg, head 4*hb + j4 --------------
         i16x4 ka[8];
         if constexpr (Q8) {
 #pragma unroll
@@ -167,30 +167,30 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
             for (int i = 0; i < 4; ++i) {
                 // x is rounded once; the max and exp2(x - max) see the same x
                 x[i] = row_ror8_add(row_ror4_add(sacc[i])) * xs;
-                if (tail && (c << 4) + 4 * i + tg >= t1) x[i] = kNegInf;
+                if (tail && c * CHUNK + 4 * i + tg >= t1) x[i] = kNegInf;
             }
             const float mblk = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-            const float mnew = fmaxf(mrun[hb], mblk);
+            const float mnew = fmaxf(S.m[hb], mblk);
             const float muse = (mnew == kNegInf) ? 0.0f : mnew;
-            alpha[hb] = __builtin_amdgcn_exp2f(mrun[hb] - muse);
+            alpha[hb] = __builtin_amdgcn_exp2f(S.m[hb] - muse);
             float psum = 0.0f;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 p[hb][i] = __builtin_amdgcn_exp2f(x[i] - muse);
                 psum += p[hb][i];
             }
-            lrun[hb] = lrun[hb] * alpha[hb] + psum;
-            mrun[hb] = mnew;
+            S.l[hb] = S.l[hb] * alpha[hb] + psum;
+            S.m[hb] = mnew;
             rescale |= (alpha[hb] != 1.0f);
         }
         if (__any(rescale)) {
 #pragma unroll
             for (int hb = 0; hb < NHB; ++hb)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) acc[hb][e] *= alpha[hb];
+                for (int e = 0; e < 8; ++e) S.acc[hb][e] *= alpha[hb];
         }
 
-        // ---- PV -----------------------------------------------------------
+        // ---- PV ----------------------------------------------------------------
 #pragma unroll
         for (int step = 0; step < 4; ++step) {
             float vf[8];
@@ -209,7 +209,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
                     vf[2 * n + 1] = bf16hi(w4[n]);
                 }
             }
-            if (tail && (c << 4) + 4 * step + tg >= t1) {
+            if (tail && c * CHUNK + 4 * step + tg >= t1) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) vf[e] = 0.0f;   // excluded rows may hold NaN
             }
@@ -217,42 +217,66 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
             for (int hb = 0; hb < NHB; ++hb) {
                 const float pb = p[hb][step] * cur.vs;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) acc[hb][e] = mfma4x4x1f32(vf[e], pb, acc[hb][e]);
+                for (int e = 0; e < 8; ++e) S.acc[hb][e] = mfma4x4x1f32(vf[e], pb, S.acc[hb][e]);
             }
         }
-        cur = nxt;
     }
 
-    // ---- merge the 4 row states of the wave, then the waves ----------------
+    // merge the 4 row states of the wave and write the wave's state
+    __device__ void to_lds(State& S, WaveStates<G, D>& st, int wave) const {
 #pragma unroll
-    for (int hb = 0; hb < NHB; ++hb) {
-        float flat[32];
+        for (int hb = 0; hb < NHB; ++hb) {
+            float flat[32];
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
+            for (int e = 0; e < 8; ++e)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) flat[4 * e + i] = acc[hb][e][i];
-        merge_xor<true>(mrun[hb], lrun[hb], flat, 16);
-        merge_xor<true>(mrun[hb], lrun[hb], flat, 32);
-        if (tg == 0) {
-            const int h = hb * 4 + j4;
-            if (qd == 0) {
-                st.m[wave][h] = mrun[hb];
-                st.l[wave][h] = lrun[hb];
+                for (int i = 0; i < 4; ++i) flat[4 * e + i] = S.acc[hb][e][i];
+            float m = S.m[hb], l = S.l[hb];
+            merge_xor<true>(m, l, flat, 16);
+            merge_xor<true>(m, l, flat, 32);
+            if (tg == 0) {
+                const int h = hb * 4 + j4;
+                if (qd == 0) {
+                    st.m[wave][h] = m;
+                    st.l[wave][h] = l;
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) st.acc[wave][h][8 * (4 * qd + i) + e] = flat[4 * e + i];
             }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) st.acc[wave][h][8 * (4 * qd + i) + e] = flat[4 * e + i];
         }
     }
-    __syncthreads();
-    finish<NW, G, D, true>(st, a, s, g, j);
+};
+
+// Register budget per lane: 168 (3 waves per SIMD) for G = 4, 256 (2 waves)
+// for G = 8; enough resident waves to keep HBM busy with one chunk in flight.
+template <int G>
+constexpr int kWavesPerEU = G == 4 ? 3 : 2;
+
+template <int G, Dtype CT>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kWavesPerEU<G>)))
+void mfma_partitions(DecodeArgs a) {
+    decode_partitions<MfmaCore<G, CT>>(a);
 }
 
 template <int G, Dtype CT>
-hipError_t launch(const DecodeArgs& a, hipStream_t st) {
-    const int64_t nwg = (int64_t)a.num_kv_heads * a.num_seqs * a.num_partitions;
-    hipLaunchKernelGGL((decode_mfma_kernel<G, CT>), dim3((unsigned)nwg), dim3(NW * 64), 0, st, a);
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kWavesPerEU<G>)))
+void mfma_balanced(DecodeArgs a) {
+    decode_balanced<MfmaCore<G, CT>>(a);
+}
+
+template <int G, Dtype CT>
+hipError_t launch(const DecodeArgs& a, Schedule sch, hipStream_t st) {
+    if (sch == Schedule::Balanced) {
+        const void* fn = reinterpret_cast<const void*>(&mfma_balanced<G, CT>);
+        const int grid = balanced_grid(fn, st);
+        if (grid <= 0) return hipErrorLaunchFailure;
+        hipLaunchKernelGGL((mfma_balanced<G, CT>), dim3(grid), dim3(NW * 64), 0, st, a);
+    } else {
+        const int64_t nwg = (int64_t)a.num_kv_heads * a.num_seqs * a.num_partitions;
+        hipLaunchKernelGGL((mfma_partitions<G, CT>), dim3((unsigned)nwg), dim3(NW * 64), 0, st, a);
+    }
     return hipGetLastError();
 }
 
@@ -260,15 +284,15 @@ hipError_t launch(const DecodeArgs& a, hipStream_t st) {
 
 bool mfma_supports(const DecodeArgs& a) {
     const int G = a.num_heads / a.num_kv_heads;
-    return (G == 4 || G == 8) && a.head_dim == D && a.q_dtype == BF16 &&
+    return (G == 4 || G == 8) && a.head_dim == 128 && a.q_dtype == BF16 &&
            (a.cache == BF16 || a.cache == I8) && (a.block_size == 16 || a.block_size == 32);
 }
 
-hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t st) {
+hipError_t launch_decode_mfma(const DecodeArgs& a, Schedule sch, hipStream_t st) {
     if (!mfma_supports(a)) return hipErrorNotSupported;
     const int G = a.num_heads / a.num_kv_heads;
-    if (a.cache == BF16) return G == 4 ? launch<4, BF16>(a, st) : launch<8, BF16>(a, st);
-    return G == 4 ? launch<4, I8>(a, st) : launch<8, I8>(a, st);
+    if (a.cache == BF16) return G == 4 ? launch<4, BF16>(a, sch, st) : launch<8, BF16>(a, sch, st);
+    return G == 4 ? launch<4, I8>(a, sch, st) : launch<8, I8>(a, sch, st);
 }
 
 }  // namespace pa

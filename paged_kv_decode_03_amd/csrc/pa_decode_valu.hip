@@ -1,4 +1,4 @@
-// Paged decode attention, VALU kernel: multi-head (G = 1) and G = 2 layouts,
+// Paged decode attention, VALU core: multi-head (G = 1) and G = 2 layouts,
 // where the query heads sharing a kv head are too few to make a dense
 // contraction worth the matrix cores.
 //
@@ -7,25 +7,21 @@
 // Inference-Engine README, feature list); the decoder reads the block table
 // ("How vrajpatel105/paged-inference-engine works", Connections).
 //
-// Workgroup = (kv head g, sequence s, partition j), 4 waves. The partition's
-// tokens are taken 16 at a time ("chunks"; a block of 16 or 32 tokens holds
-// 1 or 2 chunks); wave w takes chunks w, w+4, ... Inside a wave, lane
-// (tt = lane/4, qq = lane%4) owns token row tt of the chunk and the 16-byte
-// pieces 4m+qq of that row, so each load instruction reads whole 64-byte runs
-// of 16 rows. Each lane keeps its own online-softmax state over "its" rows
-// (natural-log units) for its quarter of the head dims; the 16 row states of a
-// wave are merged with lane shuffles at the end, the 4 wave states in LDS.
+// Per 16-token chunk, lane (tt = lane/4, qq = lane%4) owns token row tt and
+// the 16-byte pieces 4m+qq of that row, so each load instruction reads whole
+// 64-byte runs of 16 rows. Dot products are fmaf with a quad DPP sum; each
+// lane keeps its own online-softmax state (natural-log units) over "its" rows
+// for its quarter of the head dims. The 16 row states of a wave are merged
+// with lane shuffles, the waves in LDS.
 #include "pa_decode_common.hpp"
 
 namespace pa {
 namespace {
 
-constexpr int NW = 4;
-
 template <Dtype T>
 constexpr int esize() { return T == F32 ? 4 : T == BF16 ? 2 : 1; }
 
-// 16 bytes of cache/query data -> 16/esize floats (exact).
+// 16 bytes of cache data -> 16/esize floats (exact).
 template <Dtype T>
 __device__ __forceinline__ void unpack16(const uint4& w, float* f) {
     const uint32_t v[4] = {w.x, w.y, w.z, w.w};
@@ -46,72 +42,76 @@ __device__ __forceinline__ void unpack16(const uint4& w, float* f) {
     }
 }
 
-template <int D, int G, Dtype QT, Dtype CT>
-__global__ __launch_bounds__(NW * 64) void decode_valu_kernel(DecodeArgs a) {
-    constexpr int CE = esize<CT>();
-    constexpr int EPC = 16 / CE;              // cache elements per 16-byte piece
-    constexpr int NM = D * CE / 64;           // pieces per lane per row
-    constexpr int ND = NM * EPC;              // dims per lane (= D / 4)
+template <int D_, int G_, Dtype QT, Dtype CT>
+struct ValuCore {
+    static constexpr int G = G_;
+    static constexpr int D = D_;
+    static constexpr bool BASE2 = false;
+    static constexpr int CE = esize<CT>();
+    static constexpr int EPC = 16 / CE;          // cache elements per 16-byte piece
+    static constexpr int NM = D * CE / 64;       // pieces per lane per row
+    static constexpr int ND = NM * EPC;          // dims per lane (= D / 4)
     static_assert(ND * 4 == D, "lane split");
 
-    __shared__ WaveStates<NW, G, D> st;
-
-    const WorkItem wi = work_item(a);
-    const int g = wi.g, s = wi.s, j = wi.j;
-    const int L = a.context_lens[s];
-    const int P = a.partition_size > 0 ? a.partition_size : L;
-    const int t0 = j * P;
-    if (L == 0 || t0 >= L) {
-        if (a.partition_size == 0) store_zeros<G, D>(a, s, g);
-        return;
-    }
-    const int t1 = min(L, t0 + P);
-    const int c0 = t0 >> 4, c1 = (t1 + 15) >> 4;
-
-    const int lane = threadIdx.x & 63;
-    const int wave = uniform(threadIdx.x >> 6);
-    const int tt = lane >> 2, qq = lane & 3;
-
-    // query rows of the G heads, in this lane's dims
-    float qf[G][ND];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-        const char* qrow = (const char*)a.q +
-                           (((int64_t)s * a.num_heads + g * G + h) * D) * esize<QT>();
-#pragma unroll
-        for (int m = 0; m < NM; ++m) {
-#pragma unroll
-            for (int e = 0; e < EPC; ++e) {
-                const int d = (4 * m + qq) * EPC + e;
-                qf[h][m * EPC + e] = (QT == F32) ? ((const float*)qrow)[d]
-                                                 : bf16lo(((const uint16_t*)qrow)[d]);
-            }
-        }
-    }
-
-    float mrun[G], lrun[G], acc[G][ND];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-        mrun[h] = kNegInf;
-        lrun[h] = 0.0f;
-#pragma unroll
-        for (int i = 0; i < ND; ++i) acc[h][i] = 0.0f;
-    }
-
-    const int shift = (a.block_size == 32) ? 1 : 0;   // chunks per block: 1 or 2
-    const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
-    const int64_t head_stride = (int64_t)a.block_size * D;
-    const int64_t block_stride = head_stride * a.num_kv_heads;
-    const int row_off = tt * D * CE + 16 * qq;        // bytes inside a 16-token chunk
-
+    struct State {
+        float m[G], l[G], acc[G][ND];
+    };
     struct Chunk {
         uint4 k[NM], v[NM];
         float ks, vs;
     };
-    auto load = [&](int c) {
+
+    const DecodeArgs& a;
+    int lane, tt, qq;
+    int row_off;                                 // bytes inside a 16-token chunk
+    int shift;
+    int64_t head_stride, block_stride;
+    const int32_t* bt;
+    int g;
+    float qf[G][ND];
+
+    __device__ explicit ValuCore(const DecodeArgs& args) : a(args) {
+        lane = threadIdx.x & 63;
+        tt = lane >> 2;
+        qq = lane & 3;
+        row_off = tt * D * CE + 16 * qq;
+        shift = (a.block_size == 32) ? 1 : 0;
+        head_stride = (int64_t)a.block_size * D;
+        block_stride = head_stride * a.num_kv_heads;
+    }
+
+    __device__ void begin_segment(int s, int g_) {
+        g = g_;
+        bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const char* qrow = (const char*)a.q +
+                               (((int64_t)s * a.num_heads + g * G + h) * D) * esize<QT>();
+#pragma unroll
+            for (int m = 0; m < NM; ++m)
+#pragma unroll
+                for (int e = 0; e < EPC; ++e) {
+                    const int d = (4 * m + qq) * EPC + e;
+                    qf[h][m * EPC + e] = (QT == F32) ? ((const float*)qrow)[d]
+                                                     : bf16lo(((const uint16_t*)qrow)[d]);
+                }
+        }
+    }
+
+    __device__ void init(State& S) const {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            S.m[h] = kNegInf;
+            S.l[h] = 0.0f;
+#pragma unroll
+            for (int i = 0; i < ND; ++i) S.acc[h][i] = 0.0f;
+        }
+    }
+
+    __device__ Chunk load(int c) const {
         Chunk ch;
-        const int phys = bt[c >> shift];
-        const int64_t off = phys * block_stride + g * head_stride + (int64_t)(c & shift) * 16 * D;
+        const int phys = ld_const(bt, c >> shift);
+        const int64_t off = phys * block_stride + g * head_stride + (int64_t)(c & shift) * CHUNK * D;
         const char* kp = (const char*)a.k_cache + off * CE + row_off;
         const char* vp = (const char*)a.v_cache + off * CE + row_off;
 #pragma unroll
@@ -120,28 +120,22 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(DecodeArgs a) {
             ch.v[m] = ld16(vp + 64 * m);
         }
         if constexpr (CT == I8) {
-            ch.ks = a.k_scale[(int64_t)phys * a.num_kv_heads + g];
-            ch.vs = a.v_scale[(int64_t)phys * a.num_kv_heads + g];
+            ch.ks = ld_const(a.k_scale, (int64_t)phys * a.num_kv_heads + g);
+            ch.vs = ld_const(a.v_scale, (int64_t)phys * a.num_kv_heads + g);
         } else {
             ch.ks = ch.vs = 1.0f;
         }
         return ch;
-    };
+    }
 
-    int c = c0 + wave;
-    Chunk cur;
-    if (c < c1) cur = load(c);
-    for (; c < c1; c += NW) {
-        Chunk nxt;
-        if (c + NW < c1) nxt = load(c + NW);
-
+    __device__ void step(State& S, const Chunk& cur, int c, int t1) const {
         float kf[ND], vf[ND];
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
             unpack16<CT>(cur.k[m], &kf[m * EPC]);
             unpack16<CT>(cur.v[m], &vf[m * EPC]);
         }
-        const bool valid = (c << 4) + tt < t1;
+        const bool valid = c * CHUNK + tt < t1;
         const float xs = a.scale * cur.ks;
 #pragma unroll
         for (int h = 0; h < G; ++h) {
@@ -150,60 +144,77 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(DecodeArgs a) {
             for (int i = 0; i < ND; ++i) dot = fmaf(qf[h][i], kf[i], dot);
             dot = quad_sum(dot);
             if (valid) {
-                // x is rounded once and both the max and exp(x - max) use
-                // that value, so the largest weight is exactly 1 (the build
-                // turns off fma contraction, which would break this)
+                // x is rounded once and both the max and exp(x - max) use that
+                // value, so the largest weight is exactly 1
                 const float x = dot * xs;
-                const float mnew = fmaxf(mrun[h], x);
-                const float alpha = __builtin_amdgcn_exp2f((mrun[h] - mnew) * kLog2e);
+                const float mnew = fmaxf(S.m[h], x);
+                const float alpha = __builtin_amdgcn_exp2f((S.m[h] - mnew) * kLog2e);
                 const float p = __builtin_amdgcn_exp2f((x - mnew) * kLog2e);
-                lrun[h] = lrun[h] * alpha + p;
+                S.l[h] = S.l[h] * alpha + p;
                 const float pv = p * cur.vs;
 #pragma unroll
-                for (int i = 0; i < ND; ++i) acc[h][i] = fmaf(pv, vf[i], acc[h][i] * alpha);
-                mrun[h] = mnew;
+                for (int i = 0; i < ND; ++i) S.acc[h][i] = fmaf(pv, vf[i], S.acc[h][i] * alpha);
+                S.m[h] = mnew;
             }
         }
-        cur = nxt;
     }
 
-    // merge the 16 row states of the wave (lanes differing in tt)
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-#pragma unroll
-        for (int mask = 4; mask < 64; mask <<= 1) merge_xor<false>(mrun[h], lrun[h], acc[h], mask);
-    }
-    if (tt == 0) {
+    // merge the 16 row states of the wave (lanes differing in tt), write st[wave]
+    __device__ void to_lds(State& S, WaveStates<G, D>& st, int wave) const {
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-            if (qq == 0) {
-                st.m[wave][h] = mrun[h];
-                st.l[wave][h] = lrun[h];
+#pragma unroll
+            for (int mask = 4; mask < 64; mask <<= 1)
+                merge_xor<false>(S.m[h], S.l[h], S.acc[h], mask);
+        }
+        if (tt == 0) {
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                if (qq == 0) {
+                    st.m[wave][h] = S.m[h];
+                    st.l[wave][h] = S.l[h];
+                }
+#pragma unroll
+                for (int m = 0; m < NM; ++m)
+#pragma unroll
+                    for (int e = 0; e < EPC; ++e)
+                        st.acc[wave][h][(4 * m + qq) * EPC + e] = S.acc[h][m * EPC + e];
             }
-#pragma unroll
-            for (int m = 0; m < NM; ++m)
-#pragma unroll
-                for (int e = 0; e < EPC; ++e) st.acc[wave][h][(4 * m + qq) * EPC + e] = acc[h][m * EPC + e];
         }
     }
-    __syncthreads();
-    finish<NW, G, D, false>(st, a, s, g, j);
+};
+
+template <int D, int G, Dtype QT, Dtype CT>
+__global__ __launch_bounds__(NW * 64) void valu_partitions(DecodeArgs a) {
+    decode_partitions<ValuCore<D, G, QT, CT>>(a);
 }
 
 template <int D, int G, Dtype QT, Dtype CT>
-hipError_t launch(const DecodeArgs& a, hipStream_t st) {
-    const int64_t nwg = (int64_t)a.num_kv_heads * a.num_seqs * a.num_partitions;
-    hipLaunchKernelGGL((decode_valu_kernel<D, G, QT, CT>), dim3((unsigned)nwg), dim3(NW * 64), 0,
-                       st, a);
+__global__ __launch_bounds__(NW * 64) void valu_balanced(DecodeArgs a) {
+    decode_balanced<ValuCore<D, G, QT, CT>>(a);
+}
+
+template <int D, int G, Dtype QT, Dtype CT>
+hipError_t launch(const DecodeArgs& a, Schedule sch, hipStream_t st) {
+    if (sch == Schedule::Balanced) {
+        const void* fn = reinterpret_cast<const void*>(&valu_balanced<D, G, QT, CT>);
+        const int grid = balanced_grid(fn, st);
+        if (grid <= 0) return hipErrorLaunchFailure;
+        hipLaunchKernelGGL((valu_balanced<D, G, QT, CT>), dim3(grid), dim3(NW * 64), 0, st, a);
+    } else {
+        const int64_t nwg = (int64_t)a.num_kv_heads * a.num_seqs * a.num_partitions;
+        hipLaunchKernelGGL((valu_partitions<D, G, QT, CT>), dim3((unsigned)nwg), dim3(NW * 64), 0,
+                           st, a);
+    }
     return hipGetLastError();
 }
 
 template <int D, int G>
-hipError_t by_dtype(const DecodeArgs& a, hipStream_t st) {
-    if (a.q_dtype == F32 && a.cache == F32) return launch<D, G, F32, F32>(a, st);
-    if (a.q_dtype == BF16 && a.cache == BF16) return launch<D, G, BF16, BF16>(a, st);
-    if (a.q_dtype == F32 && a.cache == I8) return launch<D, G, F32, I8>(a, st);
-    if (a.q_dtype == BF16 && a.cache == I8) return launch<D, G, BF16, I8>(a, st);
+hipError_t by_dtype(const DecodeArgs& a, Schedule sch, hipStream_t st) {
+    if (a.q_dtype == F32 && a.cache == F32) return launch<D, G, F32, F32>(a, sch, st);
+    if (a.q_dtype == BF16 && a.cache == BF16) return launch<D, G, BF16, BF16>(a, sch, st);
+    if (a.q_dtype == F32 && a.cache == I8) return launch<D, G, F32, I8>(a, sch, st);
+    if (a.q_dtype == BF16 && a.cache == I8) return launch<D, G, BF16, I8>(a, sch, st);
     return hipErrorNotSupported;
 }
 
@@ -217,11 +228,11 @@ bool valu_supports(const DecodeArgs& a) {
            (a.block_size == 16 || a.block_size == 32);
 }
 
-hipError_t launch_decode_valu(const DecodeArgs& a, hipStream_t st) {
+hipError_t launch_decode_valu(const DecodeArgs& a, Schedule sch, hipStream_t st) {
     if (!valu_supports(a)) return hipErrorNotSupported;
     const int G = a.num_heads / a.num_kv_heads;
-    if (a.head_dim == 64) return G == 1 ? by_dtype<64, 1>(a, st) : by_dtype<64, 2>(a, st);
-    return G == 1 ? by_dtype<128, 1>(a, st) : by_dtype<128, 2>(a, st);
+    if (a.head_dim == 64) return G == 1 ? by_dtype<64, 1>(a, sch, st) : by_dtype<64, 2>(a, sch, st);
+    return G == 1 ? by_dtype<128, 1>(a, sch, st) : by_dtype<128, 2>(a, sch, st);
 }
 
 }  // namespace pa

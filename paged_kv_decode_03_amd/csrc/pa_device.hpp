@@ -77,7 +77,22 @@ __device__ __forceinline__ i16x4 as_i16x4(uint32_t lo, uint32_t hi) {
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ uint2 ld8(const void* p) { return *reinterpret_cast<const uint2*>(p); }
 
+// Read-only index data (block tables, lengths, scales): loads through the
+// constant address space, which the kernel never writes, become scalar loads
+// (s_load, into SGPRs) when the index is wave-uniform.
+template <typename T>
+__device__ __forceinline__ T ld_const(const T* p, int64_t i) {
+    typedef const __attribute__((address_space(4))) T* const_ptr;
+    return ((const_ptr)p)[i];   // an address-space cast (C-style cast required)
+}
+
 // Wave-uniform value (lets the compiler keep it in an SGPR).
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ long long uniform64(long long v) {
+    const unsigned long long u = (unsigned long long)v;
+    const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)u);
+    const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(u >> 32));
+    return (long long)(((unsigned long long)hi << 32) | lo);
+}
 
 }  // namespace pa

@@ -33,11 +33,12 @@ struct DecodeArgs {
     float* tmp_out;
     float* tmp_max;
     float* tmp_sum;
+    int32_t* counters;    // [S][Hkv], balanced mode only; zero on entry and exit
     float scale;
     int num_seqs, num_heads, num_kv_heads, head_dim, block_size;
     int max_blocks_per_seq;
-    int partition_size;   // 0 = one pass
-    int num_partitions;   // grid extent over partitions (1 for one pass)
+    int partition_size;   // 0 = one pass; else partition / minimum piece, tokens
+    int num_partitions;   // workspace slots per (s, h) (1 for one pass)
     Dtype q_dtype, cache;
 };
 
@@ -51,10 +52,14 @@ struct ReduceArgs {
     Dtype out_dtype;
 };
 
+enum class Schedule { Partitions, Balanced };
+
 hipError_t launch_write_kv(const WriteArgs& a, hipStream_t st);
 // Returns hipErrorNotSupported when no instance covers the arguments.
-hipError_t launch_decode_valu(const DecodeArgs& a, hipStream_t st);
-hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t st);
+hipError_t launch_decode_valu(const DecodeArgs& a, Schedule sch, hipStream_t st);
+hipError_t launch_decode_mfma(const DecodeArgs& a, Schedule sch, hipStream_t st);
+// Workgroups of a balanced launch: resident workgroups per CU times CUs.
+int balanced_grid(const void* kernel, hipStream_t st);
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t st);
 
 bool valu_supports(const DecodeArgs& a);

@@ -98,10 +98,11 @@ def write_new(dc: DevCase, k, v):
     pa.write_kv_cache(dc.key, dc.value, k, v, dc.slot_mapping, dc.k_scale, dc.v_scale)
 
 
-def run_decode(dc: DevCase, partition_size=0, k=None, v=None, ws=None, max_context_len=None):
+def run_decode(dc: DevCase, partition_size=0, k=None, v=None, ws=None, max_context_len=None,
+               balanced=False):
     k = dc.k_cache if k is None else k
     v = dc.v_cache if v is None else v
     c = dc.case
     maxL = c.max_context_len if max_context_len is None else max_context_len
     return pa.paged_attention(dc.q, k, v, dc.block_tables, dc.context_lens, float(c.scale), maxL,
-                              partition_size, dc.k_scale, dc.v_scale, ws=ws)
+                              partition_size, dc.k_scale, dc.v_scale, ws=ws, balanced=balanced)

@@ -334,6 +334,102 @@ def test_pa_check_rejects_bad_block_id(monkeypatch):
         pa.write_kv_cache(dc.key, dc.value, dc.k_cache.clone(), dc.v_cache.clone(), bad)
 
 
+# ---- work-balanced schedule (pa_decode_balanced) ----------------------------------
+
+BALANCED = [(n, 16) for n in SMALL] + [(n, 64) for n in SMALL] + [
+    ("cfg2s", 256), ("cfg3s", 512), ("cfg4s", 512), ("cfg5s", 256), ("g8_i8", 128),
+    ("cfg1", 112)]
+
+
+@pytest.mark.parametrize("name,P", BALANCED)
+def test_balanced_parity(name, P):
+    """Pieces of >= P tokens; P = 16 cuts contexts into many pieces, so most
+    outputs go through the cross-workgroup combine."""
+    print(f"[balanced] {name} P={P}", flush=True)
+    case, dc, ok, ov, ref = prepared(name)
+    ws = pa.balanced_workspace(case.S, case.Hq, case.Hkv, case.D, case.max_context_len, P,
+                               "cuda")
+    out1 = run_decode(dc, P, ws=ws, balanced=True)
+    out2 = run_decode(dc, P, ws=ws, balanced=True)        # counters must be back at zero
+    sync()
+    assert int(ws[3].abs().sum()) == 0, "counters not reset"
+    got = as_f64(out1)
+    assert np.isfinite(got).all()
+    err = np.abs(got - ref).max()
+    assert err <= tol(case), f"{name} P={P}: max |gpu - oracle| = {err}"
+    assert np.array_equal(dev_to_host(out1), dev_to_host(out2)), "repeat not bit-identical"
+
+
+@pytest.mark.parametrize("name", ["cfg1", "cfg2s", "cfg4s", "cfg5s", "g2_bf16", "mha_i8_f32q"])
+@pytest.mark.parametrize("P", [16, 256])
+def test_balanced_onehot_bit_exact(name, P):
+    spec = SMALL[name]
+    rng = np.random.default_rng(13)
+    for rep in range(2):
+        case, ts = _onehot_case(spec, 40 + rep, lambda s, L: int(rng.integers(0, L)))
+        dc = to_device(case)
+        fill_pool(dc)
+        got = as_f64(run_decode(dc, P, balanced=True))
+        sync()
+        G = case.Hq // case.Hkv
+        if spec.cache == "i8":
+            ok, ov = oracle.fill_cache(case)
+            dense = pins.dense_kv(case, ok, ov)
+        else:
+            dense = pins.dense_kv(case)
+        for s, t in enumerate(ts):
+            want = np.repeat(dense[s][1][t].astype(np.float32), G, axis=0)
+            want_q = torch.from_numpy(want).to(TORCH_DT[spec.act])
+            assert np.array_equal(got[s], want_q.double().numpy()), f"{name} seq {s} t*={t}"
+
+
+@pytest.mark.parametrize("name", ["cfg1", "cfg2s", "cfg5s", "g4_b32"])
+def test_balanced_placement_invariance(name):
+    case, dc, _, _, _ = prepared(name)
+    base = dev_to_host(run_decode(dc, 32, balanced=True))
+    variants = [synth.permute_placement(case, 41)]
+    if case.spec.prefix_groups:
+        variants.append(synth.unshare_prefixes(case))
+    for var in variants:
+        dv = to_device(var)
+        fill_pool(dv)
+        assert np.array_equal(dev_to_host(run_decode(dv, 32, balanced=True)), base)
+
+
+@pytest.mark.parametrize("name", ["cfg1", "cfg2s", "cfg4s", "cfg5s"])
+def test_balanced_zero_lengths(name):
+    """Empty contexts anywhere in the batch (first, middle, last) give zeros and
+    do not disturb the pieces of their neighbours."""
+    case, dc, ok, ov, ref = prepared(name)
+    lens = dc.context_lens.clone()
+    zero = sorted({0, case.S // 2, case.S - 1})
+    lens[zero] = 0
+    ws = pa.balanced_workspace(case.S, case.Hq, case.Hkv, case.D, case.max_context_len, 16,
+                               "cuda")
+    out = torch.full_like(dc.q, float("nan"))
+    pa.decode_balanced(out, dc.q, dc.k_cache, dc.v_cache, dc.block_tables, lens,
+                       float(case.scale), case.max_context_len, 16, *ws, k_scale=dc.k_scale,
+                       v_scale=dc.v_scale)
+    sync()
+    got = as_f64(out)
+    assert (got[zero] == 0).all()
+    keep = [s for s in range(case.S) if s not in zero]
+    assert np.abs(got[keep] - ref[keep]).max() <= tol(case)
+    assert int(ws[3].abs().sum()) == 0
+
+
+def test_balanced_all_empty():
+    case, dc, _, _, _ = prepared("cfg2s")
+    lens = torch.zeros_like(dc.context_lens)
+    ws = pa.balanced_workspace(case.S, case.Hq, case.Hkv, case.D, case.max_context_len, 64,
+                               "cuda")
+    out = torch.full_like(dc.q, float("nan"))
+    pa.decode_balanced(out, dc.q, dc.k_cache, dc.v_cache, dc.block_tables, lens,
+                       float(case.scale), case.max_context_len, 64, *ws)
+    sync()
+    assert (as_f64(out) == 0).all()
+
+
 # ---- full-size workloads, sampled ---------------------------------------------
 
 @pytest.mark.timeout(900)
@@ -346,9 +442,11 @@ def test_full_size_sampled(cfg):
     print(f"[full] cfg{cfg} gpu write+decode P={spec.partition_size}", flush=True)
     fill_pool(dc)
     out = run_decode(dc, spec.partition_size)
+    outb = run_decode(dc, spec.partition_size, balanced=True)
     sync()
     got = as_f64(out)
-    assert np.isfinite(got).all()
+    gotb = as_f64(outb)
+    assert np.isfinite(got).all() and np.isfinite(gotb).all()
     print(f"[full] cfg{cfg} oracle", flush=True)
     ok, ov = oracle.fill_cache(case)
     assert np.array_equal(dev_to_host(dc.k_cache).view(np.uint8), ok.view(np.uint8))
@@ -361,5 +459,7 @@ def test_full_size_sampled(cfg):
         seqs = seqs[:2]
     ref = oracle.decode_case(case, ok, ov, seqs=seqs)
     err = np.abs(got[seqs] - ref).max()
-    print(f"[full] cfg{cfg} seqs {seqs} max err {err:.3e}", flush=True)
-    assert err <= tol(case)
+    errb = np.abs(gotb[seqs] - ref).max()
+    print(f"[full] cfg{cfg} seqs {seqs} max err {err:.3e} (partitions) {errb:.3e} (balanced)",
+          flush=True)
+    assert err <= tol(case) and errb <= tol(case)
