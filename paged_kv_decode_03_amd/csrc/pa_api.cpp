@@ -184,8 +184,8 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
 
     pa::DecodeArgs a{out, q, k_cache, v_cache, block_tables, context_lens, k_scale, v_scale,
                      tmp_out, tmp_max, tmp_sum, nullptr, scale, num_seqs, num_heads,
-                     num_kv_heads, head_dim, block_size, max_blocks_per_seq, partition_size, np,
-                     (pa::Dtype)q_dtype, (pa::Dtype)cache_dtype};
+                     num_kv_heads, head_dim, block_size, max_blocks_per_seq, max_context_len,
+                     partition_size, np, (pa::Dtype)q_dtype, (pa::Dtype)cache_dtype};
     const bool mfma = pa::mfma_supports(a);
     if (!mfma && !pa::valu_supports(a)) return PA_ERR_UNSUPPORTED;
     const int64_t nwg = (int64_t)num_kv_heads * num_seqs * np;
@@ -228,8 +228,9 @@ int pa_decode_balanced(void* out, const void* q, const void* k_cache, const void
     const int ns = pa_balanced_slots(max_context_len, min_piece_tokens);
     pa::DecodeArgs a{out, q, k_cache, v_cache, block_tables, context_lens, k_scale, v_scale,
                      tmp_out, tmp_max, tmp_sum, counters, scale, num_seqs, num_heads,
-                     num_kv_heads, head_dim, block_size, max_blocks_per_seq, min_piece_tokens,
-                     ns > 0 ? ns : 1, (pa::Dtype)q_dtype, (pa::Dtype)cache_dtype};
+                     num_kv_heads, head_dim, block_size, max_blocks_per_seq, max_context_len,
+                     min_piece_tokens, ns > 0 ? ns : 1, (pa::Dtype)q_dtype,
+                     (pa::Dtype)cache_dtype};
     const bool mfma = pa::mfma_supports(a);
     if (!mfma && !pa::valu_supports(a)) return PA_ERR_UNSUPPORTED;
     if ((int64_t)num_kv_heads * (((int64_t)max_context_len + 15) / 16) * num_seqs > 0x7fffffff)

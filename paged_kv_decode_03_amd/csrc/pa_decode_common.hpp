@@ -130,23 +130,58 @@ __device__ __forceinline__ void store_partial(const WaveStates<G, D>& st, const 
     }
 }
 
-// Log-sum-exp combination of workspace slots 0..n-1 of (s, g)'s G heads into
-// out (coherent loads: the slots were written by other workgroups).
+// Most pieces one context can be cut into (the balanced driver sizes ranges
+// so that this holds): the LDS weight table of combine_slots (2 * G * this
+// many floats) then fits in the wave-state space (NW * G * D floats).
+template <int D>
+constexpr int kMaxPieces = NW * D / 2;
+
+// Log-sum-exp combination of workspace slots 0..n-1 (n <= kMaxPieces<D>) of
+// (s, g)'s G heads into out, with coherent loads (the slots were written by
+// other workgroups). No load waits on another: lane k of wave h % NW reads
+// slot k's max and sum, the weights W_k = l_k e^{m_k - M} go through LDS
+// (wts: 2 * G * kMaxPieces<D> floats), and each output dim then issues its n
+// slot loads back to back.
 template <int G, int D>
-__device__ __forceinline__ void combine_slots(const DecodeArgs& a, int s, int g, int n, int nslots) {
+__device__ __forceinline__ void combine_slots(const DecodeArgs& a, int s, int g, int n, int nslots,
+                                              float* wts) {
+    constexpr int KP = kMaxPieces<D>;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    float* wm = wts;                          // [G][KP]: m, then W
+    float* wl = wts + G * KP;                 // [G][KP]: l
+    for (int h = wave; h < G; h += NW) {
+        const int64_t sh = (int64_t)s * a.num_heads + g * G + h;
+        for (int k = lane; k < n; k += 64) {
+            wm[h * KP + k] = ws_load_coherent(a.tmp_max + sh * nslots + k);
+            wl[h * KP + k] = ws_load_coherent(a.tmp_sum + sh * nslots + k);
+        }
+        float M = kNegInf;
+        for (int k = lane; k < n; k += 64) M = fmaxf(M, wm[h * KP + k]);
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+        for (int k = lane; k < n; k += 64)
+            wm[h * KP + k] =
+                wl[h * KP + k] * __builtin_amdgcn_exp2f((wm[h * KP + k] - M) * kLog2e);
+    }
+    __syncthreads();
     for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
         const int h = idx / D, d = idx - h * D;
         const int64_t sh = (int64_t)s * a.num_heads + g * G + h;
-        const float* mp = a.tmp_max + sh * nslots;
-        const float* lp = a.tmp_sum + sh * nslots;
-        float M = kNegInf;
-        for (int k = 0; k < n; ++k) M = fmaxf(M, ws_load_coherent(mp + k));
+        const float* op = a.tmp_out + sh * nslots * D + d;
+        const float* w = wm + h * KP;
         float o = 0.0f, wsum = 0.0f;
-        for (int k = 0; k < n; ++k) {
-            const float W = ws_load_coherent(lp + k) *
-                            __builtin_amdgcn_exp2f((ws_load_coherent(mp + k) - M) * kLog2e);
-            wsum += W;
-            o += W * ws_load_coherent(&a.tmp_out[(sh * nslots + k) * D + d]);
+        int k = 0;
+        for (; k + 4 <= n; k += 4) {
+            const float o0 = ws_load_coherent(op + (int64_t)(k + 0) * D);
+            const float o1 = ws_load_coherent(op + (int64_t)(k + 1) * D);
+            const float o2 = ws_load_coherent(op + (int64_t)(k + 2) * D);
+            const float o3 = ws_load_coherent(op + (int64_t)(k + 3) * D);
+            o += w[k] * o0 + w[k + 1] * o1 + w[k + 2] * o2 + w[k + 3] * o3;
+            wsum += w[k] + w[k + 1] + w[k + 2] + w[k + 3];
+        }
+        for (; k < n; ++k) {
+            o += w[k] * ws_load_coherent(op + (int64_t)k * D);
+            wsum += w[k];
         }
         store_out(a.out, sh * D + d, o / wsum, a.q_dtype);
     }
@@ -286,6 +321,10 @@ __device__ __forceinline__ void decode_balanced(const DecodeArgs& a) {
     const long long minc = a.partition_size / CHUNK;
     long long C = (T + W - 1) / W;
     if (C < minc) C = minc;
+    // at most kMaxPieces<D> pieces per context: pieces <= ceil(n / C) + 1
+    constexpr int KP = kMaxPieces<D>;
+    const long long maxn = (a.max_context_len + CHUNK - 1) / CHUNK;
+    if (C < (maxn + KP - 3) / (KP - 2)) C = (maxn + KP - 3) / (KP - 2);
     if (C < 1) C = 1;
     const long long X0 = (long long)w * C;
     if (X0 >= T) return;                             // uniform across the workgroup
@@ -341,7 +380,9 @@ __device__ __forceinline__ void decode_balanced(const DecodeArgs& a) {
                 sh.last = atomicAdd(&a.counters[(int64_t)s * Hkv + g], 1) == pieces - 1;
             __syncthreads();
             if (sh.last) {
-                combine_slots<G, D>(a, s, g, pieces, a.num_partitions);
+                // the wave states in st are no longer needed: their space holds the weights
+                static_assert(sizeof(st.acc) >= 2 * G * KP * sizeof(float), "LDS");
+                combine_slots<G, D>(a, s, g, pieces, a.num_partitions, &st.acc[0][0][0]);
                 if (tid == 0) a.counters[(int64_t)s * Hkv + g] = 0;
             }
         }

@@ -18,7 +18,8 @@
 //    logits of head j4 for tokens 4*i + tg (i = 0..3, one per register).
 //  softmax: each 16-lane row tg keeps its own online state (base-2 units,
 //    log2(e) folded into the scale) over its tokens, so the running max needs
-//    no cross-lane reduction inside the loop.
+//    no cross-lane reduction inside the loop; the reference max only moves
+//    when it is exceeded by more than 8, so rescales are rare.
 //  PV: v_mfma_f32_4x4x1_16b_f32, 32 per chunk and head group. The A operand
 //    is V row 4*step + tg, dims 8*(l%16) + e, straight from a fully coalesced
 //    16-byte load; the B operand is the lane's own probability register
@@ -41,6 +42,7 @@ struct MfmaCore {
     static constexpr int NHB = G / 4;           // 4-head groups
     static constexpr bool Q8 = (CT == I8);
     static constexpr int CE = Q8 ? 1 : 2;        // cache bytes per element
+    static constexpr float kSlack = 8.0f;        // see step()
 
     struct State {
         float m[NHB], l[NHB];
@@ -169,8 +171,11 @@ struct MfmaCore {
                 x[i] = row_ror8_add(row_ror4_add(sacc[i])) * xs;
                 if (tail && c * CHUNK + 4 * i + tg >= t1) x[i] = kNegInf;
             }
+            // The reference max moves only when a logit exceeds it by more
+            // than kSlack (log2 units): unnormalised weights stay <= 2^kSlack,
+            // and the accumulator rescale below is skipped on most chunks.
             const float mblk = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-            const float mnew = fmaxf(S.m[hb], mblk);
+            const float mnew = (mblk > S.m[hb] + kSlack) ? mblk : S.m[hb];
             const float muse = (mnew == kNegInf) ? 0.0f : mnew;
             alpha[hb] = __builtin_amdgcn_exp2f(S.m[hb] - muse);
             float psum = 0.0f;

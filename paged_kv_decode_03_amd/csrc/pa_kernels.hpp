@@ -37,6 +37,7 @@ struct DecodeArgs {
     float scale;
     int num_seqs, num_heads, num_kv_heads, head_dim, block_size;
     int max_blocks_per_seq;
+    int max_context_len;  // bound on every context length
     int partition_size;   // 0 = one pass; else partition / minimum piece, tokens
     int num_partitions;   // workspace slots per (s, h) (1 for one pass)
     Dtype q_dtype, cache;
