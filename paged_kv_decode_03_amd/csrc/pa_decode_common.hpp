@@ -12,9 +12,15 @@
 // A "core" supplies the per-chunk work for one (sequence, kv head) segment:
 //   begin_segment(s, g)        load the G query rows of the segment
 //   init(State&)               empty state
-//   Chunk load(c)              issue the loads of 16-token chunk c
-//   step(State&, chunk, c, t1) consume it (tokens >= t1 excluded)
-//   to_lds(State&, st, wave)   merge the wave's lane states, write st[wave]
+//   Chunk load(s, g, c)        issue the loads of 16-token chunk c of (s, g)
+//   step(State&, chunk, c, L)  consume it (tokens >= L excluded)
+//   merge_rows(State&)         merge the wave's lane states: afterwards every
+//                              lane holds the state of the whole wave
+//   to_lds(State&, st, wave)   merge_rows, then write the wave's state to st
+//   store_final(State&, s, g)  normalise a merged state and write out
+//   store_slot(State&, slot)   a merged state into workspace slot `slot`, in
+//                              the core's own layout, with coherent stores
+//   combine(slot0, n, s, g)    log-sum-exp of slots slot0 .. slot0+n-1 into out
 #pragma once
 
 #include "pa_device.hpp"
@@ -47,6 +53,23 @@ __device__ __forceinline__ void merge_xor(float& m, float& l, float (&acc)[N], i
         const float ao = __shfl_xor(acc[i], mask);
         acc[i] = acc[i] * a + ao * b;
     }
+    m = M;
+}
+
+// The same merge with the partner in the other 16-lane row (MASK 16) or the
+// other half-wave (MASK 32), exchanged by permlane swaps.
+template <bool BASE2, int MASK, int N>
+__device__ __forceinline__ void merge_rows_xor(float& m, float& l, float (&acc)[N]) {
+    static_assert(MASK == 16 || MASK == 32, "cross-row masks only");
+    auto other = [](float x) { return MASK == 16 ? lane_xor16(x) : lane_xor32(x); };
+    const float mo = other(m);
+    const float lo = other(l);
+    const float M = fmaxf(m, mo);
+    const float a = rel_weight<BASE2>(m, M);
+    const float b = rel_weight<BASE2>(mo, M);
+    l = l * a + lo * b;
+#pragma unroll
+    for (int i = 0; i < N; ++i) acc[i] = acc[i] * a + other(acc[i]) * b;
     m = M;
 }
 
@@ -130,63 +153,6 @@ __device__ __forceinline__ void store_partial(const WaveStates<G, D>& st, const 
     }
 }
 
-// Most pieces one context can be cut into (the balanced driver sizes ranges
-// so that this holds): the LDS weight table of combine_slots (2 * G * this
-// many floats) then fits in the wave-state space (NW * G * D floats).
-template <int D>
-constexpr int kMaxPieces = NW * D / 2;
-
-// Log-sum-exp combination of workspace slots 0..n-1 (n <= kMaxPieces<D>) of
-// (s, g)'s G heads into out, with coherent loads (the slots were written by
-// other workgroups). No load waits on another: lane k of wave h % NW reads
-// slot k's max and sum, the weights W_k = l_k e^{m_k - M} go through LDS
-// (wts: 2 * G * kMaxPieces<D> floats), and each output dim then issues its n
-// slot loads back to back.
-template <int G, int D>
-__device__ __forceinline__ void combine_slots(const DecodeArgs& a, int s, int g, int n, int nslots,
-                                              float* wts) {
-    constexpr int KP = kMaxPieces<D>;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    float* wm = wts;                          // [G][KP]: m, then W
-    float* wl = wts + G * KP;                 // [G][KP]: l
-    for (int h = wave; h < G; h += NW) {
-        const int64_t sh = (int64_t)s * a.num_heads + g * G + h;
-        for (int k = lane; k < n; k += 64) {
-            wm[h * KP + k] = ws_load_coherent(a.tmp_max + sh * nslots + k);
-            wl[h * KP + k] = ws_load_coherent(a.tmp_sum + sh * nslots + k);
-        }
-        float M = kNegInf;
-        for (int k = lane; k < n; k += 64) M = fmaxf(M, wm[h * KP + k]);
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-        for (int k = lane; k < n; k += 64)
-            wm[h * KP + k] =
-                wl[h * KP + k] * __builtin_amdgcn_exp2f((wm[h * KP + k] - M) * kLog2e);
-    }
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
-        const int h = idx / D, d = idx - h * D;
-        const int64_t sh = (int64_t)s * a.num_heads + g * G + h;
-        const float* op = a.tmp_out + sh * nslots * D + d;
-        const float* w = wm + h * KP;
-        float o = 0.0f, wsum = 0.0f;
-        int k = 0;
-        for (; k + 4 <= n; k += 4) {
-            const float o0 = ws_load_coherent(op + (int64_t)(k + 0) * D);
-            const float o1 = ws_load_coherent(op + (int64_t)(k + 1) * D);
-            const float o2 = ws_load_coherent(op + (int64_t)(k + 2) * D);
-            const float o3 = ws_load_coherent(op + (int64_t)(k + 3) * D);
-            o += w[k] * o0 + w[k + 1] * o1 + w[k + 2] * o2 + w[k + 3] * o3;
-            wsum += w[k] + w[k + 1] + w[k + 2] + w[k + 3];
-        }
-        for (; k < n; ++k) {
-            o += w[k] * ws_load_coherent(op + (int64_t)k * D);
-            wsum += w[k];
-        }
-        store_out(a.out, sh * D + d, o / wsum, a.q_dtype);
-    }
-}
-
 // One pass over an empty context: the output is all zeros.
 template <int G, int D>
 __device__ __forceinline__ void store_zeros(const DecodeArgs& a, int s, int g) {
@@ -200,8 +166,8 @@ __device__ __forceinline__ void store_zeros(const DecodeArgs& a, int s, int g) {
 // of the current segment (tokens >= t1 excluded); the merged state of each
 // wave is left in st. Ends with a workgroup barrier.
 template <class Core>
-__device__ __forceinline__ void run_piece(Core& core, WaveStates<Core::G, Core::D>& st,
-                                          int c_begin, int c_end, int t1) {
+__device__ __forceinline__ void run_piece(Core& core, WaveStates<Core::G, Core::D>& st, int s,
+                                          int g, int c_begin, int c_end, int t1) {
     const int wave = uniform(threadIdx.x >> 6);
     typename Core::State S;
     core.init(S);
@@ -209,13 +175,13 @@ __device__ __forceinline__ void run_piece(Core& core, WaveStates<Core::G, Core::
     // two chunk buffers used in turn (no register copies between iterations):
     // the loads of the next chunk are in flight while the current one computes
     typename Core::Chunk b0, b1;
-    if (c < c_end) b0 = core.load(c);
+    if (c < c_end) b0 = core.load(s, g, c);
     while (c < c_end) {
-        if (c + NW < c_end) b1 = core.load(c + NW);
+        if (c + NW < c_end) b1 = core.load(s, g, c + NW);
         core.step(S, b0, c, t1);
         c += NW;
         if (c >= c_end) break;
-        if (c + NW < c_end) b0 = core.load(c + NW);
+        if (c + NW < c_end) b0 = core.load(s, g, c + NW);
         core.step(S, b1, c, t1);
         c += NW;
     }
@@ -245,45 +211,78 @@ __device__ __forceinline__ void decode_partitions(const DecodeArgs& a) {
     const int t1 = min(L, t0 + P);
     Core core(a);
     core.begin_segment(s, g);
-    run_piece(core, st, t0 / CHUNK, (t1 + CHUNK - 1) / CHUNK, t1);
+    run_piece(core, st, s, g, t0 / CHUNK, (t1 + CHUNK - 1) / CHUNK, t1);
     if (a.partition_size > 0)
         store_partial<G, D, Core::BASE2, false>(st, a, s, g, j, a.num_partitions);
     else
         store_final<G, D, Core::BASE2>(st, a, s, g);
 }
 
-// ---- driver 2: work-balanced pieces --------------------------------------------
+// ---- driver 2: work-balanced, wave by wave ---------------------------------------
 // All (sequence, kv head) segments are laid end to end as one list of
-// T = Hkv * sum_s ceil(L_s / 16) chunks, sequence-major. Workgroup w takes the
-// contiguous range [w*C, (w+1)*C), C = max(min_chunks, ceil(T / W)), so every
-// workgroup streams the same number of chunks whatever the length mix. A
-// segment wholly inside one range is finished in place; a segment cut by
-// range ends leaves one partial per piece in the workspace, and the workgroup
-// that completes its last piece (counted with an agent-scope atomic) combines
-// them and resets the counter to 0.
+// T = Hkv * sum_s ceil(L_s / 16) chunks, sequence-major. Every wave of the
+// persistent grid takes one contiguous range of C = max(min_chunks,
+// ceil(T / waves)) chunks, so all waves stream the same number of bytes
+// whatever the length mix, and walks it on its own: no workgroup barrier after
+// the set-up, and the loads of the next chunk -- in the same segment or the
+// next one -- are in flight while the current chunk is computed.
+// A segment wholly inside one range is finished in place. A segment cut by
+// range ends leaves one partial per piece in the workspace; after its stores
+// have completed, each piece's wave increments an agent-scope counter for the
+// segment, and the wave that brings it to the number of pieces combines them
+// all (coherent loads), writes out and resets the counter to 0. No wave ever
+// waits for another.
 //
-// Logical range index: workgroups are dealt round-robin to the 8 XCDs, so the
-// index is remapped to give each XCD a contiguous run of ranges (neighbouring
+// Workgroups are dealt round-robin to the 8 XCDs, so the workgroup index is
+// remapped to give each XCD a contiguous run of ranges (neighbouring
 // sequences, e.g. those sharing prefix blocks, then share that XCD's L2).
 struct BalancedShared {
-    int part[NW * 64];
     int wave_tot[NW];
     long long total;
-    int s0;
-    long long base0;
-    int last;
+    int s0[NW];
+    long long base0[NW];
 };
 
-template <class Core>
-__device__ __forceinline__ void decode_balanced(const DecodeArgs& a) {
-    constexpr int G = Core::G, D = Core::D;
-    __shared__ WaveStates<G, D> st;
-    __shared__ BalancedShared sh;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// Position of one chunk in the segment list (all fields wave-uniform).
+struct SegPos {
+    int s, g, c;      // sequence, kv head, chunk within the segment
+    int L, n;         // context length of s and its chunk count
+    long long A;      // list index of chunk 0 of segment (s, g)
+};
+
+__device__ __forceinline__ SegPos next_pos(const DecodeArgs& a, SegPos p) {
+    if (p.c + 1 < p.n) {
+        ++p.c;
+        return p;
+    }
+    p.c = 0;
+    p.A += p.n;
+    if (++p.g < a.num_kv_heads) return p;
+    p.g = 0;
+    do {                                   // sequences with an empty context have no segments
+        ++p.s;
+        p.L = ld_uniform(a.context_lens, p.s);
+        p.n = (p.L + CHUNK - 1) / CHUNK;
+    } while (p.n == 0);
+    return p;
+}
+
+// Where one wave's range starts; all fields wave-uniform.
+struct WaveRange {
+    long long X0, X1, C, wv;
+    SegPos cur;
+};
+
+// Set-up shared by the balanced drivers: chunk counts, their scan over the
+// sequences, the range size C and the position of each wave's first chunk.
+// Ends with a workgroup barrier; returns false for a wave with no work.
+template <int G, int D>
+__device__ __forceinline__ bool balanced_setup(const DecodeArgs& a, BalancedShared& sh, WaveRange& r) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
     const int S = a.num_seqs, Hkv = a.num_kv_heads;
     const int W = gridDim.x;
 
-    // logical range index (XCD-contiguous); a bijection when W % 8 == 0
+    // logical workgroup index (XCD-contiguous); a bijection when W % 8 == 0
     const int nx = 8;
     const int w = (W % nx) ? (int)blockIdx.x
                            : (int)(blockIdx.x % nx) * (W / nx) + (int)(blockIdx.x / nx);
@@ -293,8 +292,7 @@ __device__ __forceinline__ void decode_balanced(const DecodeArgs& a) {
     const int sb = min(S, tid * K), se = min(S, sb + K);
     int my = 0;
     for (int s = sb; s < se; ++s) my += (ld_const(a.context_lens, s) + CHUNK - 1) / CHUNK;
-    // inclusive scan over the workgroup
-    int inc = my;
+    int inc = my;                                    // inclusive scan over the workgroup
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
         const int y = __shfl_up(inc, off);
@@ -304,100 +302,213 @@ __device__ __forceinline__ void decode_balanced(const DecodeArgs& a) {
     __syncthreads();
     int wbase = 0;
     for (int v = 0; v < wave; ++v) wbase += sh.wave_tot[v];
-    const int excl = wbase + inc - my;            // chunks of sequences before sb
+    const int excl = wbase + inc - my;               // chunks of sequences before sb
     if (tid == NW * 64 - 1) sh.total = (long long)Hkv * (wbase + inc);
     if (w == 0) {
         // sequences with an empty context get zeros (no piece covers them)
         for (int s = sb; s < se; ++s)
-            if (a.context_lens[s] == 0)
-                for (int gg = 0; gg < Hkv; ++gg) {
-                    for (int i = 0; i < G * D; ++i)
-                        store_out(a.out, ((int64_t)s * a.num_heads + gg * G) * D + i, 0.0f,
-                                  a.q_dtype);
-                }
+            if (ld_const(a.context_lens, s) == 0)
+                for (int i = 0; i < Hkv * G * D; ++i)
+                    store_out(a.out, (int64_t)s * a.num_heads * D + i, 0.0f, a.q_dtype);
     }
     __syncthreads();
     const long long T = uniform64(sh.total);
-    const long long minc = a.partition_size / CHUNK;
-    long long C = (T + W - 1) / W;
-    if (C < minc) C = minc;
-    // at most kMaxPieces<D> pieces per context: pieces <= ceil(n / C) + 1
-    constexpr int KP = kMaxPieces<D>;
-    const long long maxn = (a.max_context_len + CHUNK - 1) / CHUNK;
-    if (C < (maxn + KP - 3) / (KP - 2)) C = (maxn + KP - 3) / (KP - 2);
+    const long long Wv = (long long)W * NW;
+    long long C = (T + Wv - 1) / Wv;
+    if (C < a.partition_size / CHUNK) C = a.partition_size / CHUNK;
     if (C < 1) C = 1;
-    const long long X0 = (long long)w * C;
-    if (X0 >= T) return;                             // uniform across the workgroup
-    const long long X1 = min(T, X0 + C);
 
-    // 2. locate the sequence holding chunk X0: Hkv*P(s0) <= X0 < Hkv*P(s0+1)
-    if ((long long)Hkv * excl <= X0 && X0 < (long long)Hkv * (excl + my)) {
-        long long base = (long long)Hkv * excl;
-        for (int s = sb; s < se; ++s) {
-            const long long n = (long long)Hkv * ((a.context_lens[s] + CHUNK - 1) / CHUNK);
-            if (X0 < base + n) {
-                sh.s0 = s;
-                sh.base0 = base;
-                break;
+    // 2. locate the sequence holding the first chunk of each wave's range
+    for (int v = 0; v < NW; ++v) {
+        const long long X0v = ((long long)w * NW + v) * C;
+        if ((long long)Hkv * excl <= X0v && X0v < (long long)Hkv * (excl + my)) {
+            long long base = (long long)Hkv * excl;
+            for (int s = sb; s < se; ++s) {
+                const long long n = (long long)Hkv * ((ld_const(a.context_lens, s) + CHUNK - 1) / CHUNK);
+                if (X0v < base + n) {
+                    sh.s0[v] = s;
+                    sh.base0[v] = base;
+                    break;
+                }
+                base += n;
             }
-            base += n;
         }
     }
     __syncthreads();
+    r.C = C;
+    r.wv = (long long)w * NW + wave;                 // this wave's range index
+    r.X0 = r.wv * C;
+    if (r.X0 >= T) return false;                     // uniform across the wave
+    r.X1 = min(T, r.X0 + C);
+    SegPos& cur = r.cur;
+    cur.s = uniform(sh.s0[wave]);
+    const long long base = uniform64(sh.base0[wave]);
+    cur.L = ld_uniform(a.context_lens, cur.s);
+    cur.n = (cur.L + CHUNK - 1) / CHUNK;
+    cur.g = (int)((r.X0 - base) / cur.n);
+    cur.c = (int)((r.X0 - base) - (long long)cur.g * cur.n);
+    cur.A = base + (long long)cur.g * cur.n;
+    return true;
+}
 
-    // 3. walk the segments of [X0, X1) (all wave-uniform: kept in SGPRs)
-    Core core(a);
-    int s = uniform(sh.s0);
-    long long base = uniform64(sh.base0);            // first chunk of sequence s
-    long long X = X0;
-    int L = uniform(ld_const(a.context_lens, s));
-    long long n = (L + CHUNK - 1) / CHUNK;
-    int g = (int)((X - base) / n);
-    while (X < X1) {
-        if (n == 0) {                                // empty sequence: no segments
-            ++s;
-            L = uniform(ld_const(a.context_lens, s));
-            n = (L + CHUNK - 1) / CHUNK;
-            continue;
-        }
-        const long long A = base + g * n, B = A + n;
-        const int cb = (int)(X - A), ce = (int)(min(X1, B) - A);
-        core.begin_segment(s, g);
-        run_piece(core, st, cb, ce, min(L, ce * CHUNK));
-        if (A >= X0 && B <= X1) {
-            store_final<G, D, Core::BASE2>(st, a, s, g);
-        } else {
-            const int first = (int)(A / C);
-            const int pieces = (int)((B - 1) / C) - first + 1;
-            store_partial<G, D, Core::BASE2, true>(st, a, s, g, w - first, a.num_partitions);
-            // Every wave waits until its coherent stores have completed (the
-            // workgroup barrier alone does not wait for them); then one atomic
-            // publishes the piece, and the workgroup that brings the count to
-            // `pieces` combines all of them with coherent loads.
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
-            if (tid == 0)
-                sh.last = atomicAdd(&a.counters[(int64_t)s * Hkv + g], 1) == pieces - 1;
-            __syncthreads();
-            if (sh.last) {
-                // the wave states in st are no longer needed: their space holds the weights
-                static_assert(sizeof(st.acc) >= 2 * G * KP * sizeof(float), "LDS");
-                combine_slots<G, D>(a, s, g, pieces, a.num_partitions, &st.acc[0][0][0]);
-                if (tid == 0) a.counters[(int64_t)s * Hkv + g] = 0;
-            }
-        }
-        __syncthreads();                             // st is reused by the next piece
-        X = min(X1, B);
-        if (X == B && ++g == Hkv) {
-            g = 0;
-            base += Hkv * n;
-            if (X < X1) {
-                ++s;
-                L = uniform(ld_const(a.context_lens, s));
-                n = (L + CHUNK - 1) / CHUNK;
-            }
+// End of the piece of segment p held in St (this wave's chunks of it are all
+// consumed). A segment wholly inside the range is written out; otherwise the
+// piece is stored to its workspace slot and published -- now if it is the
+// range's last (then after draining this wave's stores), or else held until
+// then. Returns true if it issued global stores that are not yet waited for.
+template <class Core>
+struct PieceEnd {
+    const DecodeArgs& a;
+    const Core& core;
+    const WaveRange& r;
+    int64_t held_seg = -1;                           // a stored, unpublished piece
+    int held_pieces = 0;
+
+    __device__ void publish(int64_t seg, int pieces) const {
+        const int lane = threadIdx.x & 63;
+        int prev = 0;
+        if (lane == 0) prev = atomicAdd(&a.counters[seg], 1);
+        prev = uniform(prev);
+        if (prev == pieces - 1) {                    // every other piece is published
+            const int Hkv = a.num_kv_heads;
+            const int s = (int)(seg / Hkv), g = (int)(seg - (int64_t)s * Hkv);
+            core.combine(seg * a.num_partitions, pieces, s, g);
+            if (lane == 0)
+                __hip_atomic_store(&a.counters[seg], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
+
+    // `last`: p ends the range.
+    __device__ void operator()(typename Core::State& St, const SegPos& p, bool last) {
+        core.merge_rows(St);
+        const long long B = p.A + p.n;
+        if (p.A >= r.X0 && B <= r.X1) {
+            core.store_final(St, p.s, p.g);
+        } else {
+            const long long first = p.A / r.C;
+            const int pieces = (int)((B - 1) / r.C - first) + 1;
+            const int64_t seg = (int64_t)p.s * a.num_kv_heads + p.g;
+            core.store_slot(St, seg * a.num_partitions + (r.wv - first));
+            if (!last) {
+                held_seg = seg;
+                held_pieces = pieces;
+                return;
+            }
+            __builtin_amdgcn_s_waitcnt(0);           // every store of this wave is complete
+            if (held_seg >= 0) publish(held_seg, held_pieces);
+            publish(seg, pieces);
+            held_seg = -1;
+            return;
+        }
+        if (last && held_seg >= 0) {
+            __builtin_amdgcn_s_waitcnt(0);
+            publish(held_seg, held_pieces);
+            held_seg = -1;
+        }
+    }
+};
+
+// Register-path walk (cores without an LDS ring): the next chunk's loads go
+// to registers while the current chunk is computed.
+template <class Core>
+__device__ __forceinline__ void decode_balanced(const DecodeArgs& a) {
+    constexpr int G = Core::G, D = Core::D;
+    __shared__ BalancedShared sh;
+    WaveRange r;
+    if (!balanced_setup<G, D>(a, sh, r)) return;
+    SegPos cur = r.cur;
+    Core core(a);
+    core.begin_segment(cur.s, cur.g);
+    typename Core::State St;
+    core.init(St);
+    PieceEnd<Core> end{a, core, r};
+    // chunks left in the range, in 32 bits: a 64-bit compare would need a VGPR
+    // temporary, which may be one that an in-flight load still targets
+    int left = (int)(r.X1 - r.X0);
+
+    // One chunk: issue the loads of the next chunk into `nb` (at the range end
+    // the current one again, so that every path has the same loads in flight
+    // and the compiler's wait counts stay exact), compute `cb`, end a segment
+    // that ends here. Returns false after the range's last chunk.
+    auto one = [&](typename Core::Chunk& cb, typename Core::Chunk& nb) -> bool {
+        const bool more = left > 1;
+        const SegPos nxp = more ? next_pos(a, cur) : cur;
+        nb = core.load(nxp.s, nxp.g, nxp.c);
+        core.step(St, cb, cur.c, cur.L);
+        if (more && nxp.c != 0) {                    // same segment
+            --left;
+            cur = nxp;
+            return true;
+        }
+        end(St, cur, !more);
+        if (!more) return false;
+        core.begin_segment(nxp.s, nxp.g);
+        core.init(St);
+        --left;
+        cur = nxp;
+        return true;
+    };
+    typename Core::Chunk b0, b1;
+    b0 = core.load(cur.s, cur.g, cur.c);
+    while (one(b0, b1) && one(b1, b0)) {
+    }
+}
+
+// LDS-ring walk: each wave keeps R chunks of its range in flight in its own
+// LDS slots and computes from registers read out of the oldest.
+//
+// Every iteration issues exactly one chunk (past the range end the last chunk
+// again, into the slot just read), so R - 1 issues of DPC vector memory
+// instructions always follow the chunk being waited for, and the wait is one
+// fixed vmcnt. Segment ends drain the wave instead: the query loads of the
+// next segment are waited for there (so the compiler never sees them pending
+// inside the loop), and so are the output stores, which may complete out of
+// order with loads.
+template <class Core>
+__device__ __forceinline__ void decode_balanced_ring(const DecodeArgs& a) {
+    constexpr int G = Core::G, D = Core::D, R = Core::R, SLOT = Core::SLOT, DPC = Core::DPC;
+    __shared__ BalancedShared sh;
+    __shared__ __attribute__((aligned(16))) char ring[NW * R * SLOT];
+    WaveRange r;
+    if (!balanced_setup<G, D>(a, sh, r)) return;
+    char* const mine = ring + uniform(threadIdx.x >> 6) * (R * SLOT);
+    SegPos cur = r.cur;
+    Core core(a);
+    const int n = (int)(r.X1 - r.X0);                // chunks in the range (>= 1)
+    SegPos ahead = cur;                              // next chunk to issue
+    int issued = 0;
+    auto issue_next = [&](char* sp) {
+        core.issue(sp, ahead.s, ahead.g, ahead.c);
+        if (++issued < n) ahead = next_pos(a, ahead);  // else: repeat the last chunk
+    };
+#pragma unroll
+    for (int k = 0; k < R; ++k) issue_next(mine + k * SLOT);
+    core.begin_segment(cur.s, cur.g);
+    wait_vmcnt<0>();
+    typename Core::State St;
+    core.init(St);
+    PieceEnd<Core> end{a, core, r};
+    int slot = 0;
+    for (int i = 0;; ++i) {
+        wait_vmcnt<(R - 1) * DPC>();                 // chunk i is in its slot
+        char* const sp = mine + slot * SLOT;
+        const typename Core::Chunk ch = core.fetch(sp);   // the slot is free again
+        issue_next(sp);
+        slot = (slot + 1 == R) ? 0 : slot + 1;
+        core.step(St, ch, cur.c, cur.L);
+        const bool last = i + 1 == n;
+        if (!last && cur.c + 1 < cur.n) {            // same segment
+            ++cur.c;
+            continue;
+        }
+        end(St, cur, last);
+        if (last) break;
+        cur = next_pos(a, cur);
+        core.begin_segment(cur.s, cur.g);
+        wait_vmcnt<0>();
+        core.init(St);
+    }
+    wait_vmcnt<0>();                                 // no load may land in LDS after the wave ends
 }
 
 }  // namespace pa

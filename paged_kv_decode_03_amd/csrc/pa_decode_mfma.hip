@@ -24,7 +24,10 @@
 //    is V row 4*step + tg, dims 8*(l%16) + e, straight from a fully coalesced
 //    16-byte load; the B operand is the lane's own probability register
 //    `step`, already in place. V and P stay in fp32.
-//  The 4 row states are merged with lane shuffles, the 4 wave states in LDS.
+//  The 4 row states are merged with lane shuffles. Afterwards lane
+//  (tg, qd, j4) owns dims 8*(4*qd + tg) + e, e = 0..7, of head j4: the final
+//  output, a workspace partial and the combine of partials all use that
+//  assignment, so each is one coalesced 16-byte (or 8 x 4-byte) access per lane.
 //
 // No LDS is used in the main loop: K and V go from HBM straight to registers
 // with 16-byte loads, and the next chunk's loads are issued before the current
@@ -56,14 +59,27 @@ struct MfmaCore {
 
     const DecodeArgs& a;
     int lane, j4, qd, tg;
-    int k_off, v_off;                            // byte offsets inside a chunk
+    uint32_t k_off, v_off;                       // byte offsets inside a chunk
     float sl2;
     int shift;
     int64_t head_stride, block_stride;
-    // per segment
-    const int32_t* bt;
-    int g;
-    uint4 qr[NHB][4];
+    uint4 qr[NHB][4];                            // query operands of the segment
+
+    // ---- LDS ring: chunks move HBM -> LDS by direct loads, LDS -> registers
+    // by ds_read, so the chunks in flight hold no VGPRs -----------------------
+    static constexpr int KT = 16 * D * CE;       // bytes of one 16-token K (or V) tile
+    static constexpr int NDK = KT / 1024;        // 1 KB load instructions per tile
+    static constexpr int SLOT = 2 * KT + (Q8 ? 16 : 0);  // K, V, then the int8 scales
+    static constexpr int DPC = 2 * NDK + (Q8 ? 2 : 0);   // vector memory instructions per chunk
+    static constexpr int R = Q8 ? 4 : 2;         // ring slots per wave
+    // The K tile is stored with its 16-byte pieces permuted inside each row, so
+    // that the loads read whole rows (bf16: a quarter-wave reads one 256-byte
+    // row; int8: two 128-byte rows) and the ds_reads that assemble the MFMA
+    // operands hit distinct LDS banks in every group of 8 or 16 lanes. V is
+    // stored as it is (its operand reads are already contiguous).
+    uint32_t kdma[NDK];    // source byte offset in the K tile, per load instruction
+    uint32_t krd[NDK];     // LDS byte offset of the lane's K piece, per piece group
+    uint32_t vrd;          // LDS byte offset of the lane's V piece for step 0
 
     __device__ explicit MfmaCore(const DecodeArgs& args) : a(args) {
         lane = threadIdx.x & 63;
@@ -76,22 +92,100 @@ struct MfmaCore {
         shift = (a.block_size == 32) ? 1 : 0;
         head_stride = (int64_t)a.block_size * D;
         block_stride = head_stride * a.num_kv_heads;
+#pragma unroll
+        for (int i = 0; i < NDK; ++i) {
+            if constexpr (Q8) {
+                // load i, lane 8*rr + t: row 8i + 4(rr&1) + rr/2, piece t^4i^2(rr&1)
+                const int rr = lane >> 3, t = lane & 7;
+                kdma[i] = (8 * i + 4 * (rr & 1) + (rr >> 1)) * 128 + 16 * (t ^ (4 * i) ^ (2 * (rr & 1)));
+                // piece group i: row 4*j4 + tg, piece qd + 4i
+                const int pc = qd + 4 * i;
+                krd[i] = 1024 * (j4 >> 1) +
+                         16 * (8 * (2 * tg + (j4 & 1)) + (pc ^ (4 * (j4 >> 1)) ^ (2 * (j4 & 1))));
+            } else {
+                // load i, lane 16*q + t: row 4i + q; piece bits (t0, t3, t1^i0, t2^i1)
+                const int q = lane >> 4, t = lane & 15;
+                const int pc = (t & 1) | (((t >> 3) & 1) << 1) | ((((t >> 1) & 1) ^ (i & 1)) << 2) |
+                               ((((t >> 2) & 1) ^ (i >> 1)) << 3);
+                kdma[i] = (4 * i + q) * 256 + 16 * pc;
+                // piece group i: row 4*j4 + tg, piece qd + 4i
+                const int tt = (qd & 1) | (((j4 & 1) ^ (i & 1)) << 1) | ((((j4 >> 1) & 1) ^ (i >> 1)) << 2) |
+                               ((qd >> 1) << 3);
+                krd[i] = 1024 * j4 + 16 * (16 * tg + tt);
+            }
+        }
+        vrd = Q8 ? 128 * tg + 8 * (lane & 15) : 16 * lane;
+    }
+
+    // Start the loads of chunk c of segment (s, g) into ring slot `slot`
+    // (DPC vector memory instructions).
+    __device__ void issue(char* slot, int s, int g, int c) const {
+        const int phys = ld_uniform(a.block_tables, (int64_t)s * a.max_blocks_per_seq + (c >> shift));
+        const int64_t off = phys * block_stride + g * head_stride + (int64_t)(c & shift) * CHUNK * D;
+        const char* kt = (const char*)a.k_cache + off * CE;
+        const char* vt = (const char*)a.v_cache + off * CE;
+#pragma unroll
+        for (int i = 0; i < NDK; ++i) dma16(at(kt, kdma[i]), slot + 1024 * i);
+#pragma unroll
+        for (int i = 0; i < NDK; ++i) dma16(at(vt + 1024 * i, 16u * lane), slot + KT + 1024 * i);
+        if constexpr (Q8) {
+            if (lane == 0) {
+                dma4(a.k_scale + (int64_t)phys * a.num_kv_heads + g, slot + 2 * KT);
+                dma4(a.v_scale + (int64_t)phys * a.num_kv_heads + g, slot + 2 * KT + 4);
+            }
+        }
+    }
+
+    // The chunk in ring slot `slot` (its loads complete) as MFMA operands.
+    __device__ Chunk fetch(const char* slot) const {
+        Chunk ch;
+        const uint32_t b = lds_addr(slot);
+        const uint32_t vb = b + KT + vrd;
+        if constexpr (Q8) {
+            u32x4 k0 = ds_read16(b + krd[0]), k1 = ds_read16(b + krd[1]);
+            u32x2 v0 = ds_read8<0>(vb), v1 = ds_read8<512>(vb), v2 = ds_read8<1024>(vb),
+                  v3 = ds_read8<1536>(vb);
+            u32x2 sc = ds_read8<2 * KT>(b);
+            lds_wait(k0, k1, v0, v1, v2, v3, sc);
+            ch.k[0] = make_uint4(k0.x, k0.y, k0.z, k0.w);
+            ch.k[1] = make_uint4(k1.x, k1.y, k1.z, k1.w);
+            ch.k[2] = ch.k[3] = make_uint4(0, 0, 0, 0);
+            ch.v[0] = make_uint4(v0.x, v0.y, 0, 0);
+            ch.v[1] = make_uint4(v1.x, v1.y, 0, 0);
+            ch.v[2] = make_uint4(v2.x, v2.y, 0, 0);
+            ch.v[3] = make_uint4(v3.x, v3.y, 0, 0);
+            ch.ks = __uint_as_float(sc.x);
+            ch.vs = __uint_as_float(sc.y);
+        } else {
+            u32x4 k0 = ds_read16(b + krd[0]), k1 = ds_read16(b + krd[1]), k2 = ds_read16(b + krd[2]),
+                  k3 = ds_read16(b + krd[3]);
+            u32x4 v0 = ds_read16<0>(vb), v1 = ds_read16<1024>(vb), v2 = ds_read16<2048>(vb),
+                  v3 = ds_read16<3072>(vb);
+            lds_wait(k0, k1, k2, k3, v0, v1, v2, v3);
+            ch.k[0] = make_uint4(k0.x, k0.y, k0.z, k0.w);
+            ch.k[1] = make_uint4(k1.x, k1.y, k1.z, k1.w);
+            ch.k[2] = make_uint4(k2.x, k2.y, k2.z, k2.w);
+            ch.k[3] = make_uint4(k3.x, k3.y, k3.z, k3.w);
+            ch.v[0] = make_uint4(v0.x, v0.y, v0.z, v0.w);
+            ch.v[1] = make_uint4(v1.x, v1.y, v1.z, v1.w);
+            ch.v[2] = make_uint4(v2.x, v2.y, v2.z, v2.w);
+            ch.v[3] = make_uint4(v3.x, v3.y, v3.z, v3.w);
+            ch.ks = ch.vs = 1.0f;
+        }
+        return ch;
     }
 
     // Query operands. bf16 cache: dims 8*(4m+qd) .. +7 for m = 0..3.
     // int8 cache: dims 16*(4(m>>1)+qd) + 8(m&1) .. +7.
-    __device__ void begin_segment(int s, int g_) {
-        g = g_;
-        bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+    __device__ void begin_segment(int s, int g) {
+        const uint16_t* q0 = (const uint16_t*)a.q + ((int64_t)s * a.num_heads + g * G) * D;
 #pragma unroll
-        for (int hb = 0; hb < NHB; ++hb) {
-            const uint16_t* qrow =
-                (const uint16_t*)a.q + ((int64_t)s * a.num_heads + g * G + hb * 4 + j4) * D;
+        for (int hb = 0; hb < NHB; ++hb)
 #pragma unroll
-            for (int m = 0; m < 4; ++m)
-                qr[hb][m] = Q8 ? ld16(qrow + 16 * (4 * (m >> 1) + qd) + 8 * (m & 1))
-                               : ld16(qrow + 8 * (4 * m + qd));
-        }
+            for (int m = 0; m < 4; ++m) {
+                const int d = Q8 ? 16 * (4 * (m >> 1) + qd) + 8 * (m & 1) : 8 * (4 * m + qd);
+                qr[hb][m] = ld16(at(q0, 2 * ((hb * 4 + j4) * D + d)));
+            }
     }
 
     __device__ void init(State& S) const {
@@ -104,12 +198,12 @@ struct MfmaCore {
         }
     }
 
-    __device__ Chunk load(int c) const {
+    __device__ Chunk load(int s, int g, int c) const {
         Chunk ch;
-        const int phys = ld_const(bt, c >> shift);
+        const int phys = ld_uniform(a.block_tables, (int64_t)s * a.max_blocks_per_seq + (c >> shift));
         const int64_t off = phys * block_stride + g * head_stride + (int64_t)(c & shift) * CHUNK * D;
-        const char* kp = (const char*)a.k_cache + off * CE + k_off;
-        const char* vp = (const char*)a.v_cache + off * CE + v_off;
+        const char* kp = at((const char*)a.k_cache + off * CE, k_off);
+        const char* vp = at((const char*)a.v_cache + off * CE, v_off);
         if constexpr (Q8) {
             ch.k[0] = ld16(kp);
             ch.k[1] = ld16(kp + 64);
@@ -119,8 +213,8 @@ struct MfmaCore {
                 const uint2 w = ld8(vp + step * 4 * D);
                 ch.v[step] = make_uint4(w.x, w.y, 0, 0);
             }
-            ch.ks = ld_const(a.k_scale, (int64_t)phys * a.num_kv_heads + g);
-            ch.vs = ld_const(a.v_scale, (int64_t)phys * a.num_kv_heads + g);
+            ch.ks = ld_uniform(a.k_scale, (int64_t)phys * a.num_kv_heads + g);
+            ch.vs = ld_uniform(a.v_scale, (int64_t)phys * a.num_kv_heads + g);
         } else {
 #pragma unroll
             for (int m = 0; m < 4; ++m) ch.k[m] = ld16(kp + 64 * m);
@@ -227,8 +321,9 @@ struct MfmaCore {
         }
     }
 
-    // merge the 4 row states of the wave and write the wave's state
-    __device__ void to_lds(State& S, WaveStates<G, D>& st, int wave) const {
+    // Merge the 4 row states (lanes differing in tg): every lane then holds
+    // the wave's state of head 4*hb + j4 for its dim quarter qd.
+    __device__ void merge_rows(State& S) const {
 #pragma unroll
         for (int hb = 0; hb < NHB; ++hb) {
             float flat[32];
@@ -236,26 +331,140 @@ struct MfmaCore {
             for (int e = 0; e < 8; ++e)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) flat[4 * e + i] = S.acc[hb][e][i];
-            float m = S.m[hb], l = S.l[hb];
-            merge_xor<true>(m, l, flat, 16);
-            merge_xor<true>(m, l, flat, 32);
-            if (tg == 0) {
+            merge_rows_xor<true, 16>(S.m[hb], S.l[hb], flat);
+            merge_rows_xor<true, 32>(S.m[hb], S.l[hb], flat);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) S.acc[hb][e][i] = flat[4 * e + i];
+        }
+    }
+
+    __device__ void to_lds(State& S, WaveStates<G, D>& st, int wave) const {
+        merge_rows(S);
+        if (tg == 0) {
+#pragma unroll
+            for (int hb = 0; hb < NHB; ++hb) {
                 const int h = hb * 4 + j4;
                 if (qd == 0) {
-                    st.m[wave][h] = m;
-                    st.l[wave][h] = l;
+                    st.m[wave][h] = S.m[hb];
+                    st.l[wave][h] = S.l[hb];
                 }
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) st.acc[wave][h][8 * (4 * qd + i) + e] = flat[4 * e + i];
+                    for (int e = 0; e < 8; ++e) st.acc[wave][h][8 * (4 * qd + i) + e] = S.acc[hb][e][i];
             }
+        }
+    }
+
+    // This lane's 8 accumulator values (dims 8*(4*qd + tg) + e) of head group hb.
+    __device__ void own(const State& S, int hb, float (&v)[8]) const {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const f32x4 x = S.acc[hb][e];
+            v[e] = tg == 0 ? x[0] : tg == 1 ? x[1] : tg == 2 ? x[2] : x[3];
+        }
+    }
+
+    __device__ void store8(int s, int g, int hb, const float (&v)[8]) const {
+        uint4 w;
+        w.x = f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+        w.y = f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+        w.z = f32_to_bf16(v[4]) | ((uint32_t)f32_to_bf16(v[5]) << 16);
+        w.w = f32_to_bf16(v[6]) | ((uint32_t)f32_to_bf16(v[7]) << 16);
+        uint16_t* o0 = (uint16_t*)a.out + ((int64_t)s * a.num_heads + g * G) * D;
+        *reinterpret_cast<uint4*>(at(o0, 2 * ((hb * 4 + j4) * D + 8 * (4 * qd + tg)))) = w;
+    }
+
+    // out = acc / l after merge_rows.
+    __device__ void store_final(const State& S, int s, int g) const {
+#pragma unroll
+        for (int hb = 0; hb < NHB; ++hb) {
+            float v[8];
+            own(S, hb, v);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = v[e] / S.l[hb];
+            store8(s, g, hb, v);
+        }
+    }
+
+    // Workspace slot (G*D floats in tmp_out, G in tmp_max / tmp_sum): lane L's
+    // 8 unnormalised accumulator values of head group hb at (hb*64 + L)*8, and
+    // m (base 2) and l of head h at h.
+    __device__ void store_slot(const State& S, int64_t slot) const {
+        const __amdgpu_buffer_rsrc_t rs = ws_rsrc(a.tmp_out + slot * (G * D), G * D * 4);
+#pragma unroll
+        for (int hb = 0; hb < NHB; ++hb) {
+            float v[8];
+            own(S, hb, v);
+            const uint32_t off = (hb * 64 + lane) * 32;
+            ws_store16(rs, off, v[0], v[1], v[2], v[3]);
+            ws_store16(rs, off + 16, v[4], v[5], v[6], v[7]);
+            if (lane < 4) {
+                ws_store<true>(at(a.tmp_max + slot * G, 4 * (hb * 4 + j4)), S.m[hb]);
+                ws_store<true>(at(a.tmp_sum + slot * G, 4 * (hb * 4 + j4)), S.l[hb]);
+            }
+        }
+    }
+
+    // Log-sum-exp of slots slot0 .. slot0+n-1 of (s, g) into out: the pieces
+    // are read kBatch at a time with a running maximum (earlier sums are
+    // rescaled when it moves), so their loads overlap.
+    static constexpr int kBatch = G == 4 ? 4 : 2;
+    __device__ void combine(int64_t slot0, int n, int s, int g) const {
+        const __amdgpu_buffer_rsrc_t rs = ws_rsrc(a.tmp_out + slot0 * (G * D), (uint32_t)n * (G * D * 4));
+        const __amdgpu_buffer_rsrc_t rm = ws_rsrc(a.tmp_max + slot0 * G, (uint32_t)n * (G * 4));
+        const __amdgpu_buffer_rsrc_t rl = ws_rsrc(a.tmp_sum + slot0 * G, (uint32_t)n * (G * 4));
+#pragma unroll
+        for (int hb = 0; hb < NHB; ++hb) {
+            const uint32_t hoff = 4 * (hb * 4 + j4);
+            const uint32_t aoff = (hb * 64 + lane) * 32;
+            float M = kNegInf, lsum = 0.0f, o[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] = 0.0f;
+            for (int k0 = 0; k0 < n; k0 += kBatch) {
+                float mk[kBatch], lk[kBatch];
+                u32x4_t a0[kBatch], a1[kBatch];
+#pragma unroll
+                for (int j = 0; j < kBatch; ++j) {
+                    const uint32_t k = (uint32_t)min(k0 + j, n - 1);
+                    mk[j] = ws_load4(rm, k * (G * 4) + hoff);
+                    lk[j] = ws_load4(rl, k * (G * 4) + hoff);
+                    a0[j] = ws_load16(rs, k * (G * D * 4) + aoff);
+                    a1[j] = ws_load16(rs, k * (G * D * 4) + aoff + 16);
+                }
+                float Mb = M;
+#pragma unroll
+                for (int j = 0; j < kBatch; ++j)
+                    if (k0 + j < n) Mb = fmaxf(Mb, mk[j]);
+                const float sc = rel_weight<true>(M, Mb);
+                lsum *= sc;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) o[e] *= sc;
+#pragma unroll
+                for (int j = 0; j < kBatch; ++j) {
+                    const float W = (k0 + j < n) ? rel_weight<true>(mk[j], Mb) : 0.0f;
+                    lsum += W * lk[j];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        o[e] += W * __uint_as_float(a0[j][e]);
+                        o[4 + e] += W * __uint_as_float(a1[j][e]);
+                    }
+                }
+                M = Mb;
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e] = o[e] / lsum;
+            store8(s, g, hb, o);
         }
     }
 };
 
-// Register budget per lane: 168 (3 waves per SIMD) for G = 4, 256 (2 waves)
-// for G = 8; enough resident waves to keep HBM busy with one chunk in flight.
+// Register budget per lane of the register-path kernel: 168 (3 waves per SIMD)
+// for G = 4, 256 (2 waves) for G = 8; enough resident waves to keep HBM busy
+// with one chunk in flight. The ring kernel is held to 2 waves per SIMD by its
+// LDS ring (64 KB per workgroup) and may use 256.
 template <int G>
 constexpr int kWavesPerEU = G == 4 ? 3 : 2;
 
@@ -266,9 +475,9 @@ void mfma_partitions(DecodeArgs a) {
 }
 
 template <int G, Dtype CT>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kWavesPerEU<G>)))
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void mfma_balanced(DecodeArgs a) {
-    decode_balanced<MfmaCore<G, CT>>(a);
+    decode_balanced_ring<MfmaCore<G, CT>>(a);
 }
 
 template <int G, Dtype CT>

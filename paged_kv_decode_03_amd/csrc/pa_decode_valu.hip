@@ -12,7 +12,9 @@
 // 64-byte runs of 16 rows. Dot products are fmaf with a quad DPP sum; each
 // lane keeps its own online-softmax state (natural-log units) over "its" rows
 // for its quarter of the head dims. The 16 row states of a wave are merged
-// with lane shuffles, the waves in LDS.
+// with lane shuffles; a wave's merged state is laid out [head][dim] through a
+// per-wave LDS buffer, so that outputs, workspace partials and their combine
+// are coalesced.
 #include "pa_decode_common.hpp"
 
 namespace pa {
@@ -63,11 +65,9 @@ struct ValuCore {
 
     const DecodeArgs& a;
     int lane, tt, qq;
-    int row_off;                                 // bytes inside a 16-token chunk
+    uint32_t row_off;                            // bytes inside a 16-token chunk
     int shift;
     int64_t head_stride, block_stride;
-    const int32_t* bt;
-    int g;
     float qf[G][ND];
 
     __device__ explicit ValuCore(const DecodeArgs& args) : a(args) {
@@ -80,9 +80,7 @@ struct ValuCore {
         block_stride = head_stride * a.num_kv_heads;
     }
 
-    __device__ void begin_segment(int s, int g_) {
-        g = g_;
-        bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+    __device__ void begin_segment(int s, int g) {
 #pragma unroll
         for (int h = 0; h < G; ++h) {
             const char* qrow = (const char*)a.q +
@@ -108,20 +106,20 @@ struct ValuCore {
         }
     }
 
-    __device__ Chunk load(int c) const {
+    __device__ Chunk load(int s, int g, int c) const {
         Chunk ch;
-        const int phys = ld_const(bt, c >> shift);
+        const int phys = ld_uniform(a.block_tables, (int64_t)s * a.max_blocks_per_seq + (c >> shift));
         const int64_t off = phys * block_stride + g * head_stride + (int64_t)(c & shift) * CHUNK * D;
-        const char* kp = (const char*)a.k_cache + off * CE + row_off;
-        const char* vp = (const char*)a.v_cache + off * CE + row_off;
+        const char* kp = at((const char*)a.k_cache + off * CE, row_off);
+        const char* vp = at((const char*)a.v_cache + off * CE, row_off);
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
             ch.k[m] = ld16(kp + 64 * m);
             ch.v[m] = ld16(vp + 64 * m);
         }
         if constexpr (CT == I8) {
-            ch.ks = ld_const(a.k_scale, (int64_t)phys * a.num_kv_heads + g);
-            ch.vs = ld_const(a.v_scale, (int64_t)phys * a.num_kv_heads + g);
+            ch.ks = ld_uniform(a.k_scale, (int64_t)phys * a.num_kv_heads + g);
+            ch.vs = ld_uniform(a.v_scale, (int64_t)phys * a.num_kv_heads + g);
         } else {
             ch.ks = ch.vs = 1.0f;
         }
@@ -159,14 +157,19 @@ struct ValuCore {
         }
     }
 
-    // merge the 16 row states of the wave (lanes differing in tt), write st[wave]
-    __device__ void to_lds(State& S, WaveStates<G, D>& st, int wave) const {
+    // Merge the 16 row states (lanes differing in tt): every lane then holds
+    // the wave's state for its dims.
+    __device__ void merge_rows(State& S) const {
 #pragma unroll
         for (int h = 0; h < G; ++h) {
 #pragma unroll
             for (int mask = 4; mask < 64; mask <<= 1)
                 merge_xor<false>(S.m[h], S.l[h], S.acc[h], mask);
         }
+    }
+
+    __device__ void to_lds(State& S, WaveStates<G, D>& st, int wave) const {
+        merge_rows(S);
         if (tt == 0) {
 #pragma unroll
             for (int h = 0; h < G; ++h) {
@@ -180,6 +183,68 @@ struct ValuCore {
                     for (int e = 0; e < EPC; ++e)
                         st.acc[wave][h][(4 * m + qq) * EPC + e] = S.acc[h][m * EPC + e];
             }
+        }
+    }
+
+    // The merged state's acc (divided by l if `normalise`) as [head][dim] in
+    // this wave's LDS buffer, readable by every lane of the wave on return.
+    __device__ const float* stage(const State& S, bool normalise) const {
+        __shared__ float buf[NW][G * D];
+        float* b = buf[uniform(threadIdx.x >> 6)];
+        __builtin_amdgcn_wave_barrier();         // earlier reads of b are done
+        if (tt == 0) {
+#pragma unroll
+            for (int h = 0; h < G; ++h)
+#pragma unroll
+                for (int m = 0; m < NM; ++m)
+#pragma unroll
+                    for (int e = 0; e < EPC; ++e) {
+                        const float x = S.acc[h][m * EPC + e];
+                        b[h * D + (4 * m + qq) * EPC + e] = normalise ? x / S.l[h] : x;
+                    }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        return b;
+    }
+
+    // heads g*G .. g*G+G-1 of sequence s are contiguous in out
+    __device__ void store_final(const State& S, int s, int g) const {
+        const float* b = stage(S, true);
+        const int64_t base = ((int64_t)s * a.num_heads + g * G) * D;
+        for (int i = lane; i < G * D; i += 64) store_out(a.out, base + i, b[i], a.q_dtype);
+    }
+
+    // Workspace slot: the unnormalised accumulator [head][dim] (G*D floats in
+    // tmp_out), m (natural units) and l of head h at h in tmp_max / tmp_sum.
+    __device__ void store_slot(const State& S, int64_t slot) const {
+        const float* b = stage(S, false);
+        float* acc = a.tmp_out + slot * (G * D);
+        for (int i = lane; i < G * D; i += 64) ws_store<true>(acc + i, b[i]);
+        if (lane == 0) {
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                ws_store<true>(a.tmp_max + slot * G + h, S.m[h]);
+                ws_store<true>(a.tmp_sum + slot * G + h, S.l[h]);
+            }
+        }
+    }
+
+    // Log-sum-exp of slots slot0 .. slot0+n-1 of (s, g) into out.
+    __device__ void combine(int64_t slot0, int n, int s, int g) const {
+        const int64_t base = ((int64_t)s * a.num_heads + g * G) * D;
+        for (int i = lane; i < G * D; i += 64) {
+            const int h = i / D;
+            float M = kNegInf;
+            for (int k = 0; k < n; ++k) M = fmaxf(M, ws_load_coherent(a.tmp_max + (slot0 + k) * G + h));
+            float lsum = 0.0f, o = 0.0f;
+            for (int k = 0; k < n; ++k) {
+                const float W = rel_weight<false>(ws_load_coherent(a.tmp_max + (slot0 + k) * G + h), M);
+                lsum += W * ws_load_coherent(a.tmp_sum + (slot0 + k) * G + h);
+                o += W * ws_load_coherent(a.tmp_out + (slot0 + k) * (G * D) + i);
+            }
+            store_out(a.out, base + i, o / lsum, a.q_dtype);
         }
     }
 };

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace pa {
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -53,6 +55,24 @@ __device__ __forceinline__ float quad_sum(float v) {
     return v;
 }
 
+// ---- cross-row exchange (gfx950 permlane swaps, no LDS round trip) --------
+
+// The value held by lane (lane ^ 16), resp. (lane ^ 32). The swap instructions
+// exchange the odd 16-lane rows of their first operand with the even rows of
+// the second (resp. the upper half of the first with the lower half of the
+// second); with both operands x, each result holds every lane's partner in
+// half of the lanes.
+__device__ __forceinline__ float lane_xor16(float x) {
+    const uint32_t u = __float_as_uint(x);
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return __uint_as_float((__lane_id() & 16) ? r[0] : r[1]);
+}
+__device__ __forceinline__ float lane_xor32(float x) {
+    const uint32_t u = __float_as_uint(x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __uint_as_float((__lane_id() & 32) ? r[0] : r[1]);
+}
+
 // ---- MFMA ---------------------------------------------------------------
 
 // 16 independent 4x4x4 bf16 products, fp32 accumulate.
@@ -77,6 +97,18 @@ __device__ __forceinline__ i16x4 as_i16x4(uint32_t lo, uint32_t hi) {
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ uint2 ld8(const void* p) { return *reinterpret_cast<const uint2*>(p); }
 
+// base + off, where base is wave-uniform and off a per-lane byte offset below
+// 4 GiB: the address form of global memory instructions with a scalar base and
+// a 32-bit lane offset. The empty asm keeps the compiler from folding the
+// offset into a per-lane 64-bit pointer that it would then hold in two VGPRs
+// for the whole kernel.
+template <typename T>
+__device__ __forceinline__ T* at(T* base, uint32_t off) {
+    asm volatile("" : "+v"(off));
+    typedef typename std::conditional<std::is_const<T>::value, const char, char>::type byte;
+    return reinterpret_cast<T*>(reinterpret_cast<byte*>(base) + off);
+}
+
 // Read-only index data (block tables, lengths, scales): loads through the
 // constant address space, which the kernel never writes, become scalar loads
 // (s_load, into SGPRs) when the index is wave-uniform.
@@ -93,6 +125,99 @@ __device__ __forceinline__ long long uniform64(long long v) {
     const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)u);
     const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(u >> 32));
     return (long long)(((unsigned long long)hi << 32) | lo);
+}
+
+// p[i] for a wave-uniform i, as a scalar load: the address itself is made
+// uniform, so the load cannot become a vector load whose wait would also wait
+// for every vector load in flight.
+template <typename T>
+__device__ __forceinline__ T ld_uniform(const T* p, int64_t i) {
+    const long long addr = uniform64((long long)(p + i));
+    return ld_const(reinterpret_cast<const T*>(addr), 0);
+}
+
+// ---- device-coherent workspace accesses ------------------------------------
+// Buffer loads/stores with the sc1 cache policy: like agent-scope relaxed
+// atomics they are coherent across the XCDs' separate L2 caches, but they move
+// 16 bytes per lane. The resource covers [base, base + bytes); accesses outside
+// it read 0 and write nothing.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+constexpr int kSC1 = 16;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t ws_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4_t ws_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kSC1);
+}
+__device__ __forceinline__ float ws_load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kSC1));
+}
+__device__ __forceinline__ void ws_store16(__amdgpu_buffer_rsrc_t r, uint32_t off, float a, float b, float c,
+                                           float d) {
+    const u32x4_t v = {__float_as_uint(a), __float_as_uint(b), __float_as_uint(c), __float_as_uint(d)};
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kSC1);
+}
+
+// ---- direct global -> LDS loads ------------------------------------------
+// global_load_lds_dwordx4: every lane reads 16 bytes at its own global address
+// and the wave writes them to LDS at lds + 16 * lane (lds is wave-uniform). The
+// transfer completes asynchronously and is counted by vmcnt like any other
+// vector load; nothing but s_waitcnt tells when the data is in LDS.
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ void dma16(const void* g, void* lds) {
+    __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 16, 0, 0);
+}
+// 4 bytes; with only lane 0 active they land at lds itself
+__device__ __forceinline__ void dma4(const void* g, void* lds) {
+    __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 4, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const lds_void*)p;
+}
+
+// LDS reads written as inline asm: the compiler cannot tell which LDS bytes a
+// pending global->LDS load writes, and would otherwise wait for every vector
+// load in flight before each LDS read. The caller orders them with
+// wait_vmcnt before and lds_wait after.
+template <int OFF = 0>
+__device__ __forceinline__ u32x4 ds_read16(uint32_t addr) {
+    u32x4 v;
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF) : "memory");
+    return v;
+}
+template <int OFF = 0>
+__device__ __forceinline__ u32x2 ds_read8(uint32_t addr) {
+    u32x2 v;
+    asm volatile("ds_read_b64 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF) : "memory");
+    return v;
+}
+// Wait for the LDS reads above; the operands tie their results to this point so
+// that no use is scheduled before it.
+__device__ __forceinline__ void lds_wait(u32x4& a, u32x4& b, u32x4& c, u32x4& d, u32x4& e, u32x4& f,
+                                         u32x4& g, u32x4& h) {
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(a), "+v"(b), "+v"(c), "+v"(d), "+v"(e), "+v"(f), "+v"(g), "+v"(h)
+                 :
+                 : "memory");
+}
+__device__ __forceinline__ void lds_wait(u32x4& a, u32x4& b, u32x2& c, u32x2& d, u32x2& e, u32x2& f,
+                                         u32x2& g) {
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(a), "+v"(b), "+v"(c), "+v"(d), "+v"(e), "+v"(f), "+v"(g)
+                 :
+                 : "memory");
+}
+
+// s_waitcnt vmcnt(N): at most N vector memory instructions still in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xf) | ((N >> 4) << 14) | (0x7 << 4) | (0xf << 8));
 }
 
 }  // namespace pa
