@@ -7,7 +7,8 @@ One step = the whole decode hot path over one batch resident in HBM:
      partitions followed by pa_decode_splitk_reduce instead).
 Default workload: the Llama-3-8B-shaped bf16 GQA batch (64 sequences,
 context lengths U[128, 2048], 32 query / 8 kv heads, head_dim 128, block 16,
-shuffled pool sized 1.25x the need, partition 512).
+shuffled pool sized 1.25x the need). Split-K partitions are 512 tokens (the
+workload's own); the balanced schedule cuts pieces of at least 128 tokens.
 
 The KV pool is replicated R times (R x pool >= 2 GB, far above the 256 MB
 last-level cache) and step i uses copy i mod R, so every step streams its KV
@@ -35,6 +36,9 @@ sys.path.insert(0, os.path.join(ROOT, "tests"))
 
 METRIC = "decode attention GB/s and % of HBM peak; seq-tokens/sec at bf16 GQA"
 HBM_PEAK_GBS = 8000.0
+# smallest piece (tokens) of the balanced schedule: a few 16-token chunks per
+# wave range keeps every wave of the persistent grid busy on short batches
+BALANCED_MIN_PIECE = 128
 KERNEL_SOURCES = ["pa_decode_mfma.hip", "pa_decode_valu.hip", "pa_decode_common.hpp",
                   "pa_device.hpp"]
 
@@ -109,7 +113,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--partition", type=int, default=None,
-                    help="split-K partition, or the smallest balanced piece (tokens)")
+                    help="split-K partition (default: the workload's), or the smallest "
+                         f"balanced piece in tokens (default {BALANCED_MIN_PIECE})")
     ap.add_argument("--schedule", choices=["balanced", "partitions"], default="balanced")
     ap.add_argument("--rotate-gb", type=float, default=2.0)
     ap.add_argument("--cpu-budget", type=float, default=12.0)
@@ -136,7 +141,11 @@ def main():
     from gpu_helpers import fill_pool, to_device
 
     spec = synth.CONFIGS[args.config]
-    P = spec.partition_size if args.partition is None else args.partition
+    balanced = args.schedule == "balanced"
+    if args.partition is not None:
+        P = args.partition
+    else:
+        P = BALANCED_MIN_PIECE if balanced else spec.partition_size
     case = synth.make_case(spec, args.config)
     tr = synth.traffic(case)
     dev = torch.device("cuda:0")
@@ -148,7 +157,6 @@ def main():
     pools = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(R - 1)]
     maxL = case.max_context_len
     S, Hq, D = case.S, case.Hq, case.D
-    balanced = args.schedule == "balanced"
     if balanced:
         ws = pa.balanced_workspace(S, Hq, case.Hkv, D, maxL, P, dev)
     else:

@@ -340,20 +340,30 @@ struct MfmaCore {
         }
     }
 
+    // Merge the row states and write the wave's state (partition driver). The
+    // merge goes through LDS permutes here: with the register budget of three
+    // waves per SIMD, the permlane form makes the allocator spill in the loop.
     __device__ void to_lds(State& S, WaveStates<G, D>& st, int wave) const {
-        merge_rows(S);
-        if (tg == 0) {
 #pragma unroll
-            for (int hb = 0; hb < NHB; ++hb) {
+        for (int hb = 0; hb < NHB; ++hb) {
+            float flat[32];
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) flat[4 * e + i] = S.acc[hb][e][i];
+            float m = S.m[hb], l = S.l[hb];
+            merge_xor<true>(m, l, flat, 16);
+            merge_xor<true>(m, l, flat, 32);
+            if (tg == 0) {
                 const int h = hb * 4 + j4;
                 if (qd == 0) {
-                    st.m[wave][h] = S.m[hb];
-                    st.l[wave][h] = S.l[hb];
+                    st.m[wave][h] = m;
+                    st.l[wave][h] = l;
                 }
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) st.acc[wave][h][8 * (4 * qd + i) + e] = S.acc[hb][e][i];
+                    for (int e = 0; e < 8; ++e) st.acc[wave][h][8 * (4 * qd + i) + e] = flat[4 * e + i];
             }
         }
     }
@@ -411,7 +421,7 @@ struct MfmaCore {
     // Log-sum-exp of slots slot0 .. slot0+n-1 of (s, g) into out: the pieces
     // are read kBatch at a time with a running maximum (earlier sums are
     // rescaled when it moves), so their loads overlap.
-    static constexpr int kBatch = G == 4 ? 4 : 2;
+    static constexpr int kBatch = 8;
     __device__ void combine(int64_t slot0, int n, int s, int g) const {
         const __amdgpu_buffer_rsrc_t rs = ws_rsrc(a.tmp_out + slot0 * (G * D), (uint32_t)n * (G * D * 4));
         const __amdgpu_buffer_rsrc_t rm = ws_rsrc(a.tmp_max + slot0 * G, (uint32_t)n * (G * 4));

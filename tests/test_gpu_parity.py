@@ -52,6 +52,19 @@ SMALL = {
                               cache="i8", max_len=400),
 }
 
+# Batches of 20k-30k 16-token chunks over all kv heads: every wave of the
+# balanced schedule's persistent grid gets a range of several chunks, so most
+# contexts are cut into several pieces that go through the in-kernel combine.
+MID = {
+    "mid_g4_bf16": synth.Spec("G=4 bf16, mid-size", 24, ("uniform", 1000, 3000), 32, 8, 128,
+                              16, act="bf16", cache="bf16", max_len=3000),
+    "mid_g8_i8": synth.Spec("G=8 int8, mid-size", 16, ("uniform", 1500, 3500), 64, 8, 128, 32,
+                            act="bf16", cache="i8", max_len=3500),
+    "mid_g8_cow": synth.Spec("G=8 bf16 CoW, mid-size", 48, ("lognormal", 800, 1.0, 1, 6000),
+                             64, 8, 128, 32, act="bf16", cache="bf16", max_len=6000,
+                             prefix_groups=4, prefix_tokens=512),
+}
+
 _cache = {}
 
 
@@ -59,7 +72,7 @@ def prepared(name, seed=7):
     """(case, device case with filled pool, oracle pool, oracle output)."""
     key = (name, seed)
     if key not in _cache:
-        case = synth.make_case(SMALL[name], seed)
+        case = synth.make_case(SMALL[name] if name in SMALL else MID[name], seed)
         dc = to_device(case)
         fill_pool(dc)
         ok, ov = oracle.fill_cache(case)
@@ -418,6 +431,26 @@ def test_balanced_zero_lengths(name):
     assert int(ws[3].abs().sum()) == 0
 
 
+@pytest.mark.parametrize("P", [16, 64])
+@pytest.mark.parametrize("name", list(MID))
+def test_balanced_mid_size(name, P):
+    """Every output against the oracle, repeats bit-identical, and every
+    counter back at zero."""
+    print(f"[mid] {name} P={P}", flush=True)
+    case, dc, ok, ov, ref = prepared(name)
+    ws = pa.balanced_workspace(case.S, case.Hq, case.Hkv, case.D, case.max_context_len, P,
+                               "cuda")
+    a = dev_to_host(run_decode(dc, P, ws=ws, balanced=True))
+    assert int(ws[3].abs().sum()) == 0, "counters not reset"
+    b = dev_to_host(run_decode(dc, P, ws=ws, balanced=True))
+    assert int(ws[3].abs().sum()) == 0, "counters not reset"
+    assert np.array_equal(a, b)
+    got = as_f64(run_decode(dc, P, ws=ws, balanced=True))
+    err = np.abs(got - ref).max()
+    print(f"[mid] {name} P={P} max err {err:.3e}", flush=True)
+    assert err <= tol(case)
+
+
 def test_balanced_all_empty():
     case, dc, _, _, _ = prepared("cfg2s")
     lens = torch.zeros_like(dc.context_lens)
@@ -443,10 +476,12 @@ def test_full_size_sampled(cfg):
     fill_pool(dc)
     out = run_decode(dc, spec.partition_size)
     outb = run_decode(dc, spec.partition_size, balanced=True)
+    outt = run_decode(dc, 64, balanced=True)         # pieces >= 64 tokens
     sync()
     got = as_f64(out)
     gotb = as_f64(outb)
-    assert np.isfinite(got).all() and np.isfinite(gotb).all()
+    gott = as_f64(outt)
+    assert np.isfinite(got).all() and np.isfinite(gotb).all() and np.isfinite(gott).all()
     print(f"[full] cfg{cfg} oracle", flush=True)
     ok, ov = oracle.fill_cache(case)
     assert np.array_equal(dev_to_host(dc.k_cache).view(np.uint8), ok.view(np.uint8))
@@ -460,6 +495,7 @@ def test_full_size_sampled(cfg):
     ref = oracle.decode_case(case, ok, ov, seqs=seqs)
     err = np.abs(got[seqs] - ref).max()
     errb = np.abs(gotb[seqs] - ref).max()
-    print(f"[full] cfg{cfg} seqs {seqs} max err {err:.3e} (partitions) {errb:.3e} (balanced)",
-          flush=True)
-    assert err <= tol(case) and errb <= tol(case)
+    errt = np.abs(gott[seqs] - ref).max()
+    print(f"[full] cfg{cfg} seqs {seqs} max err {err:.3e} (partitions) {errb:.3e} (balanced)"
+          f" {errt:.3e} (balanced, 64-token pieces)", flush=True)
+    assert err <= tol(case) and errb <= tol(case) and errt <= tol(case)
