@@ -192,6 +192,33 @@ int pa_decode_balanced(void *out, const void *q, const void *k_cache, const void
                        int min_piece_tokens, float *tmp_out, float *tmp_max, float *tmp_sum,
                        int32_t *counters, pa_dtype q_dtype, pa_dtype cache_dtype, void *stream);
 
+/*
+ * pa_write_decode_balanced -- one decode step in one call: the slot-mapped
+ * write of every sequence's new token (as pa_write_kv_cache with
+ * num_tokens = num_seqs) followed by pa_decode_balanced. For the MFMA
+ * instances (bf16 q, G = 4 or 8, head_dim 128) both run in one launch: the
+ * wave that loads the chunk holding a sequence's new token writes that token
+ * first; otherwise the two kernels run one after the other on `stream`.
+ *
+ *   key, value    [num_seqs][num_kv_heads][head_dim], q_dtype: row s is the new
+ *                 token of sequence s.
+ *   slot_mapping  [num_seqs] int64: its slot, or < 0 to write nothing. For a
+ *                 non-empty context it must be the slot of logical position
+ *                 context_lens[s] - 1 of sequence s (the token is part of its
+ *                 own context); PA_CHECK=1 verifies this.
+ *   k_cache, v_cache are written; all other arguments as pa_decode_balanced.
+ * Result and pool contents are bit-identical to the two calls.
+ */
+int pa_write_decode_balanced(const void *key, const void *value, const int64_t *slot_mapping,
+                             void *out, const void *q, void *k_cache, void *v_cache,
+                             const int32_t *block_tables, int max_blocks_per_seq,
+                             const int32_t *context_lens, const float *k_scale,
+                             const float *v_scale, float scale, int num_seqs, int num_heads,
+                             int num_kv_heads, int head_dim, int block_size, int64_t num_blocks,
+                             int max_context_len, int min_piece_tokens, float *tmp_out,
+                             float *tmp_max, float *tmp_sum, int32_t *counters, pa_dtype q_dtype,
+                             pa_dtype cache_dtype, void *stream);
+
 /* Workspace slots per (sequence, query head) that pa_decode_balanced needs:
  * ceil(ceil(max_context_len / 16) / (min_piece_tokens / 16)) + 1, or 0 when
  * max_context_len <= 0 or min_piece_tokens < 16. */

@@ -43,6 +43,8 @@ _lib.pa_decode.argtypes = [_p, _p, _p, _p, _p, _i, _p, _p, _p, _f, _i, _i, _i, _
 _lib.pa_decode_balanced.restype = _i
 _lib.pa_decode_balanced.argtypes = [_p, _p, _p, _p, _p, _i, _p, _p, _p, _f, _i, _i, _i, _i, _i,
                                     _i64, _i, _i, _p, _p, _p, _p, _i, _i, _p]
+_lib.pa_write_decode_balanced.restype = _i
+_lib.pa_write_decode_balanced.argtypes = [_p, _p, _p] + _lib.pa_decode_balanced.argtypes
 _lib.pa_balanced_slots.restype = _i
 _lib.pa_balanced_slots.argtypes = [_i, _i]
 _lib.pa_decode_splitk_reduce.restype = _i
@@ -200,6 +202,46 @@ def decode_balanced(out, q, k_cache, v_cache, block_tables, context_lens, scale,
                                  _ptr(tmp_max), _ptr(tmp_sum), _ptr(counters), _dt(q),
                                  _dt(k_cache), _stream(stream, dev))
     _check("pa_decode_balanced", rc)
+
+
+def write_decode_balanced(key, value, slot_mapping, out, q, k_cache, v_cache, block_tables,
+                          context_lens, scale, max_context_len, min_piece_tokens, tmp_out,
+                          tmp_max, tmp_sum, counters, k_scale=None, v_scale=None, stream=None):
+    """write_kv_cache(key, value, k_cache, v_cache, slot_mapping) followed by
+    decode_balanced, in one call (one launch where the kernel supports it):
+    key/value [S, Hkv, D] hold each sequence's new token, slot_mapping [S]
+    (int64) its slot at logical position context_lens[s] - 1."""
+    dev = _dev(key, value, slot_mapping, out, q, k_cache, v_cache, block_tables, context_lens,
+               tmp_out, tmp_max, tmp_sum, counters, k_scale, v_scale)
+    if slot_mapping.dtype != torch.int64:
+        raise TypeError("slot_mapping must be int64")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32 \
+            or counters.dtype != torch.int32:
+        raise TypeError("block_tables, context_lens and counters must be int32")
+    S, Hq, D = q.shape
+    NB, Hkv, B, D2 = k_cache.shape
+    if key.shape != (S, Hkv, D) or value.shape != key.shape or slot_mapping.shape != (S,) \
+            or key.dtype != q.dtype or value.dtype != q.dtype:
+        raise ValueError("key/value must be [S, Hkv, D] of q's dtype, slot_mapping [S]")
+    if D2 != D or v_cache.shape != k_cache.shape or block_tables.shape[0] != S \
+            or context_lens.shape != (S,) or out.shape != q.shape \
+            or counters.numel() < S * Hkv:
+        raise ValueError("shape mismatch")
+    ns = balanced_slots(max_context_len, min_piece_tokens)
+    if tmp_out.numel() < S * Hq * ns * D or tmp_max.numel() < S * Hq * ns \
+            or tmp_sum.numel() < S * Hq * ns:
+        raise ValueError("workspace too small")
+    if out.dtype != q.dtype:
+        raise TypeError("out must have the dtype of q")
+    rc = _lib.pa_write_decode_balanced(_ptr(key), _ptr(value), _ptr(slot_mapping), _ptr(out),
+                                       _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                                       block_tables.shape[1], _ptr(context_lens), _ptr(k_scale),
+                                       _ptr(v_scale), float(scale), S, Hq, Hkv, D, B, NB,
+                                       int(max_context_len), int(min_piece_tokens),
+                                       _ptr(tmp_out), _ptr(tmp_max), _ptr(tmp_sum),
+                                       _ptr(counters), _dt(q), _dt(k_cache),
+                                       _stream(stream, dev))
+    _check("pa_write_decode_balanced", rc)
 
 
 def balanced_workspace(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len,

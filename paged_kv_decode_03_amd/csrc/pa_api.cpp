@@ -82,6 +82,31 @@ int check_indices(const int32_t* block_tables, int max_blocks_per_seq,
     return PA_OK;
 }
 
+// PA_CHECK=1, decodes that write the new tokens: slot s in the pool, and, for a
+// non-empty context, the slot of logical position L_s - 1 of sequence s.
+int check_new_slots(const int64_t* slot_mapping, const int32_t* block_tables,
+                    int max_blocks_per_seq, const int32_t* context_lens, int num_seqs,
+                    int block_size, int64_t num_blocks, hipStream_t st) {
+    std::vector<int64_t> slots;
+    std::vector<int32_t> lens, tables;
+    if (!fetch(slots, slot_mapping, num_seqs, st) || !fetch(lens, context_lens, num_seqs, st) ||
+        !fetch(tables, block_tables, (int64_t)num_seqs * max_blocks_per_seq, st))
+        return PA_ERR_LAUNCH;
+    for (int s = 0; s < num_seqs; ++s) {
+        const int64_t sl = slots[s];
+        if (sl < 0) continue;
+        if (sl / block_size >= num_blocks) return PA_ERR_INDEX;
+        if (lens[s] > 0) {
+            const int t = lens[s] - 1;
+            const int64_t want =
+                (int64_t)tables[(size_t)s * max_blocks_per_seq + t / block_size] * block_size +
+                t % block_size;
+            if (sl != want) return PA_ERR_INDEX;
+        }
+    }
+    return PA_OK;
+}
+
 }  // namespace
 
 namespace pa {
@@ -210,13 +235,19 @@ int pa_balanced_slots(int max_context_len, int min_piece_tokens) {
     return (int)((chunks + minc - 1) / minc + 1);
 }
 
-int pa_decode_balanced(void* out, const void* q, const void* k_cache, const void* v_cache,
-                       const int32_t* block_tables, int max_blocks_per_seq,
-                       const int32_t* context_lens, const float* k_scale, const float* v_scale,
-                       float scale, int num_seqs, int num_heads, int num_kv_heads, int head_dim,
-                       int block_size, int64_t num_blocks, int max_context_len,
-                       int min_piece_tokens, float* tmp_out, float* tmp_max, float* tmp_sum,
-                       int32_t* counters, pa_dtype q_dtype, pa_dtype cache_dtype, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// pa_decode_balanced, optionally writing the new tokens first (key != NULL).
+int balanced(const void* key, const void* value, const int64_t* slot_mapping, void* out,
+             const void* q, const void* k_cache, const void* v_cache,
+             const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
+             const float* k_scale, const float* v_scale, float scale, int num_seqs, int num_heads,
+             int num_kv_heads, int head_dim, int block_size, int64_t num_blocks,
+             int max_context_len, int min_piece_tokens, float* tmp_out, float* tmp_max,
+             float* tmp_sum, int32_t* counters, pa_dtype q_dtype, pa_dtype cache_dtype,
+             void* stream) {
     int rc = check_decode(q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
                           k_scale, v_scale, num_seqs, num_heads, num_kv_heads, head_dim,
                           block_size, num_blocks, max_context_len, min_piece_tokens, q_dtype,
@@ -225,6 +256,12 @@ int pa_decode_balanced(void* out, const void* q, const void* k_cache, const void
     if (min_piece_tokens < 16 || min_piece_tokens % 16) return PA_ERR_SHAPE;
     if (!out || !tmp_out || !tmp_max || !tmp_sum || !counters) return PA_ERR_NULL;
     if (!aligned16(out) || !aligned16(tmp_out)) return PA_ERR_ALIGN;
+    const bool write = slot_mapping != nullptr;
+    if (write) {
+        if (head_dim % 8) return PA_ERR_SHAPE;
+        if (!key || !value) return PA_ERR_NULL;
+        if (!aligned16(key) || !aligned16(value)) return PA_ERR_ALIGN;
+    }
     const int ns = pa_balanced_slots(max_context_len, min_piece_tokens);
     pa::DecodeArgs a{out, q, k_cache, v_cache, block_tables, context_lens, k_scale, v_scale,
                      tmp_out, tmp_max, tmp_sum, counters, scale, num_seqs, num_heads,
@@ -242,10 +279,63 @@ int pa_decode_balanced(void* out, const void* q, const void* k_cache, const void
         rc = check_indices(block_tables, max_blocks_per_seq, context_lens, num_seqs, block_size,
                            num_blocks, max_context_len, st);
         if (rc) return rc;
+        if (write) {
+            rc = check_new_slots(slot_mapping, block_tables, max_blocks_per_seq, context_lens,
+                                 num_seqs, block_size, num_blocks, st);
+            if (rc) return rc;
+        }
     }
     const pa::Schedule sch = pa::Schedule::Balanced;
+    if (write && mfma) {                             // one launch: the decode writes the tokens
+        a.key = key;
+        a.value = value;
+        a.slot_mapping = slot_mapping;
+        return launch_status(pa::launch_decode_mfma(a, sch, st));
+    }
+    if (write) {                                     // the write kernel, then the decode
+        pa::WriteArgs w{key, value, const_cast<void*>(k_cache), const_cast<void*>(v_cache),
+                        slot_mapping, k_scale, v_scale, num_seqs, num_kv_heads, head_dim,
+                        block_size, (pa::Dtype)q_dtype, (pa::Dtype)cache_dtype};
+        rc = launch_status(pa::launch_write_kv(w, st));
+        if (rc) return rc;
+    }
     return launch_status(mfma ? pa::launch_decode_mfma(a, sch, st)
                               : pa::launch_decode_valu(a, sch, st));
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_decode_balanced(void* out, const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* block_tables, int max_blocks_per_seq,
+                       const int32_t* context_lens, const float* k_scale, const float* v_scale,
+                       float scale, int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                       int block_size, int64_t num_blocks, int max_context_len,
+                       int min_piece_tokens, float* tmp_out, float* tmp_max, float* tmp_sum,
+                       int32_t* counters, pa_dtype q_dtype, pa_dtype cache_dtype, void* stream) {
+    return balanced(nullptr, nullptr, nullptr, out, q, k_cache, v_cache, block_tables,
+                    max_blocks_per_seq, context_lens, k_scale, v_scale, scale, num_seqs, num_heads,
+                    num_kv_heads, head_dim, block_size, num_blocks, max_context_len,
+                    min_piece_tokens, tmp_out, tmp_max, tmp_sum, counters, q_dtype, cache_dtype,
+                    stream);
+}
+
+int pa_write_decode_balanced(const void* key, const void* value, const int64_t* slot_mapping,
+                             void* out, const void* q, void* k_cache, void* v_cache,
+                             const int32_t* block_tables, int max_blocks_per_seq,
+                             const int32_t* context_lens, const float* k_scale,
+                             const float* v_scale, float scale, int num_seqs, int num_heads,
+                             int num_kv_heads, int head_dim, int block_size, int64_t num_blocks,
+                             int max_context_len, int min_piece_tokens, float* tmp_out,
+                             float* tmp_max, float* tmp_sum, int32_t* counters, pa_dtype q_dtype,
+                             pa_dtype cache_dtype, void* stream) {
+    if (num_seqs > 0 && !slot_mapping) return PA_ERR_NULL;
+    return balanced(key, value, slot_mapping, out, q, k_cache, v_cache, block_tables,
+                    max_blocks_per_seq, context_lens, k_scale, v_scale, scale, num_seqs, num_heads,
+                    num_kv_heads, head_dim, block_size, num_blocks, max_context_len,
+                    min_piece_tokens, tmp_out, tmp_max, tmp_sum, counters, q_dtype, cache_dtype,
+                    stream);
 }
 
 int pa_decode_splitk_reduce(void* out, const float* tmp_out, const float* tmp_max,

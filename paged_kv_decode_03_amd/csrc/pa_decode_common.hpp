@@ -458,9 +458,12 @@ __device__ __forceinline__ void decode_balanced(const DecodeArgs& a) {
 // LDS slots and computes from registers read out of the oldest.
 //
 // Every iteration issues exactly one chunk (past the range end the last chunk
-// again, into the slot just read), so R - 1 issues of DPC vector memory
-// instructions always follow the chunk being waited for, and the wait is one
-// fixed vmcnt. Segment ends drain the wave instead: the query loads of the
+// again, into the slot just read), so R - 1 issues of at least DPC vector
+// memory loads always follow the chunk being waited for, and the wait is one
+// fixed vmcnt: loads complete in issue order, so with at most (R - 1) * DPC
+// instructions in flight the chunk's loads are done, whatever else (a new
+// token's row loads, its stores) was issued in between. Segment ends drain
+// the wave instead: the query loads of the
 // next segment are waited for there (so the compiler never sees them pending
 // inside the loop), and so are the output stores, which may complete out of
 // order with loads.
@@ -469,6 +472,14 @@ __device__ __forceinline__ void decode_balanced_ring(const DecodeArgs& a) {
     constexpr int G = Core::G, D = Core::D, R = Core::R, SLOT = Core::SLOT, DPC = Core::DPC;
     __shared__ BalancedShared sh;
     __shared__ __attribute__((aligned(16))) char ring[NW * R * SLOT];
+    if (a.slot_mapping != nullptr && blockIdx.x == 0) {
+        // new tokens of sequences with an empty context: no chunk carries them
+        for (int s = threadIdx.x; s < a.num_seqs; s += blockDim.x)
+            if (ld_const(a.context_lens, s) == 0)
+                for (int g = 0; g < a.num_kv_heads; ++g)
+                    for (int v = 0; v < D / 8; ++v)
+                        Core::write_vector_at(a, s, g, v);
+    }
     WaveRange r;
     if (!balanced_setup<G, D>(a, sh, r)) return;
     char* const mine = ring + uniform(threadIdx.x >> 6) * (R * SLOT);
@@ -477,8 +488,14 @@ __device__ __forceinline__ void decode_balanced_ring(const DecodeArgs& a) {
     const int n = (int)(r.X1 - r.X0);                // chunks in the range (>= 1)
     SegPos ahead = cur;                              // next chunk to issue
     int issued = 0;
+    // When the decode writes the new tokens: a segment's last chunk holds the
+    // new token of (s, g), and one wave consumes it. That wave loads the
+    // token's rows with the chunk and, once both are in LDS, writes the token
+    // into its cache slot and over the chunk's stale row (patch_new_token), so
+    // the kernel never reads back what it stores.
+    const bool writes = a.slot_mapping != nullptr;
     auto issue_next = [&](char* sp) {
-        core.issue(sp, ahead.s, ahead.g, ahead.c);
+        core.issue(sp, ahead.s, ahead.g, ahead.c, writes && ahead.c + 1 == ahead.n);
         if (++issued < n) ahead = next_pos(a, ahead);  // else: repeat the last chunk
     };
 #pragma unroll
@@ -492,6 +509,7 @@ __device__ __forceinline__ void decode_balanced_ring(const DecodeArgs& a) {
     for (int i = 0;; ++i) {
         wait_vmcnt<(R - 1) * DPC>();                 // chunk i is in its slot
         char* const sp = mine + slot * SLOT;
+        if (writes && cur.c + 1 == cur.n) core.patch_new_token(sp, cur.s, cur.g, cur.L);
         const typename Core::Chunk ch = core.fetch(sp);   // the slot is free again
         issue_next(sp);
         slot = (slot + 1 == R) ? 0 : slot + 1;

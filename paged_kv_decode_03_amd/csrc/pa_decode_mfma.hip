@@ -33,6 +33,7 @@
 // with 16-byte loads, and the next chunk's loads are issued before the current
 // chunk is computed.
 #include "pa_decode_common.hpp"
+#include "pa_write_row.hpp"
 
 namespace pa {
 namespace {
@@ -69,7 +70,8 @@ struct MfmaCore {
     // by ds_read, so the chunks in flight hold no VGPRs -----------------------
     static constexpr int KT = 16 * D * CE;       // bytes of one 16-token K (or V) tile
     static constexpr int NDK = KT / 1024;        // 1 KB load instructions per tile
-    static constexpr int SLOT = 2 * KT + (Q8 ? 16 : 0);  // K, V, then the int8 scales
+    static constexpr int NEW = 2 * KT + (Q8 ? 16 : 0);   // K, V, the int8 scales, then
+    static constexpr int SLOT = NEW + 4 * D;             // a new token's bf16 K and V rows
     static constexpr int DPC = 2 * NDK + (Q8 ? 2 : 0);   // vector memory instructions per chunk
     static constexpr int R = Q8 ? 4 : 2;         // ring slots per wave
     // The K tile is stored with its 16-byte pieces permuted inside each row, so
@@ -77,6 +79,12 @@ struct MfmaCore {
     // row; int8: two 128-byte rows) and the ds_reads that assemble the MFMA
     // operands hit distinct LDS banks in every group of 8 or 16 lanes. V is
     // stored as it is (its operand reads are already contiguous).
+    // bf16 cache: the piece (16 bytes, dims 8*pc ..) of its row that lane
+    // 16*q + t moves in load i.
+    static __device__ int kpiece(int t, int i) {
+        return (t & 1) | (((t >> 3) & 1) << 1) | ((((t >> 1) & 1) ^ (i & 1)) << 2) |
+               ((((t >> 2) & 1) ^ (i >> 1)) << 3);
+    }
     uint32_t kdma[NDK];    // source byte offset in the K tile, per load instruction
     uint32_t krd[NDK];     // LDS byte offset of the lane's K piece, per piece group
     uint32_t vrd;          // LDS byte offset of the lane's V piece for step 0
@@ -105,9 +113,7 @@ struct MfmaCore {
             } else {
                 // load i, lane 16*q + t: row 4i + q; piece bits (t0, t3, t1^i0, t2^i1)
                 const int q = lane >> 4, t = lane & 15;
-                const int pc = (t & 1) | (((t >> 3) & 1) << 1) | ((((t >> 1) & 1) ^ (i & 1)) << 2) |
-                               ((((t >> 2) & 1) ^ (i >> 1)) << 3);
-                kdma[i] = (4 * i + q) * 256 + 16 * pc;
+                kdma[i] = (4 * i + q) * 256 + 16 * kpiece(t, i);
                 // piece group i: row 4*j4 + tg, piece qd + 4i
                 const int tt = (qd & 1) | (((j4 & 1) ^ (i & 1)) << 1) | ((((j4 >> 1) & 1) ^ (i >> 1)) << 2) |
                                ((qd >> 1) << 3);
@@ -118,8 +124,13 @@ struct MfmaCore {
     }
 
     // Start the loads of chunk c of segment (s, g) into ring slot `slot`
-    // (DPC vector memory instructions).
-    __device__ void issue(char* slot, int s, int g, int c) const {
+    // (DPC vector memory instructions; one more with `fresh`, which also loads
+    // sequence s's new K and V rows of kv head g from key / value).
+    __device__ void issue(char* slot, int s, int g, int c, bool fresh) const {
+        if (fresh && lane < 32) {                // lanes 0..15: K, 16..31: V, 16 bytes each
+            const char* src = (const char*)(lane < 16 ? a.key : a.value);
+            dma16(src + (((int64_t)s * a.num_kv_heads + g) * D + 8 * (lane & 15)) * 2, slot + NEW);
+        }
         const int phys = ld_uniform(a.block_tables, (int64_t)s * a.max_blocks_per_seq + (c >> shift));
         const int64_t off = phys * block_stride + g * head_stride + (int64_t)(c & shift) * CHUNK * D;
         const char* kt = (const char*)a.k_cache + off * CE;
@@ -132,6 +143,73 @@ struct MfmaCore {
             if (lane == 0) {
                 dma4(a.k_scale + (int64_t)phys * a.num_kv_heads + g, slot + 2 * KT);
                 dma4(a.v_scale + (int64_t)phys * a.num_kv_heads + g, slot + 2 * KT + 4);
+            }
+        }
+    }
+
+    static __device__ void write_vector_at(const DecodeArgs& a, int s, int g, int v) {
+        write_vector<BF16, CT>(a.key, a.value, const_cast<void*>(a.k_cache),
+                               const_cast<void*>(a.v_cache), a.slot_mapping, a.k_scale, a.v_scale,
+                               a.num_kv_heads, D, a.block_size, s, g, v);
+    }
+
+    // Ring slot `slot` holds the last chunk of segment (s, g), loaded with
+    // `fresh`: the chunk as the cache held it, and sequence s's new K and V
+    // rows. Its new token (position L - 1) is written here: into the cache slot
+    // slot_mapping[s] (lanes 0..31, one 16-byte vector each), and into the
+    // chunk in LDS, where each lane overwrites the bytes of that row which its
+    // own loads of the chunk brought in. Both take the bytes the write takes
+    // (a copy, or int8 codes with the block's scales), so the chunk is the one
+    // a load after the write would give. A negative slot writes nothing.
+    __device__ void patch_new_token(char* slot, int s, int g, int L) const {
+        const int64_t sl = ld_uniform(a.slot_mapping, (int64_t)s);
+        if (sl < 0) return;
+        const int o = (L - 1) & (CHUNK - 1);     // the token's row in the chunk
+        const uint32_t b = lds_addr(slot), nb = b + NEW;
+        float ks = 1.0f, vs = 1.0f;
+        if constexpr (Q8) {
+            const int64_t sc = (sl / a.block_size) * a.num_kv_heads + g;
+            ks = ld_uniform(a.k_scale, sc);
+            vs = ld_uniform(a.v_scale, sc);
+        }
+        if (lane < 32) {
+            u32x4 w = ds_read16(nb + 16 * lane);
+            lds_wait(w);
+            const bool isk = lane < 16;
+            put_vector<BF16, CT>(const_cast<void*>(isk ? a.k_cache : a.v_cache),
+                                 slot_row(sl, g, lane & 15, 8, a.num_kv_heads, D, a.block_size),
+                                 make_uint4(w.x, w.y, w.z, w.w), isk ? ks : vs);
+        }
+        if constexpr (!Q8) {
+            // load o/4 moves row o: K piece kpiece(t, o/4) and V piece t, lanes 16*(o%4) + t
+            if ((lane >> 4) == (o & 3)) {
+                const int i = o >> 2, t = lane & 15;
+                u32x4 kw = ds_read16(nb + 16 * kpiece(t, i));
+                u32x4 vw = ds_read16(nb + 2 * D + 16 * t);
+                lds_wait(kw, vw);
+                ds_write16(b + 1024 * i + 16 * lane, kw);
+                ds_write16(b + KT + 1024 * i + 16 * lane, vw);
+            }
+        } else {
+            // load o/8 moves row o. K: lanes 8*rr + t, rr = 2*(o%4) + (o/4)%2,
+            // piece t ^ 4*(o/8) ^ 2*(rr%2); V: lanes 8*(o%8) + t, piece t. A
+            // piece is 16 codes, dims 16*piece .. +15.
+            const int i = o >> 3, t = lane & 7;
+            const int rr = 2 * (o & 3) + ((o >> 2) & 1);
+            if ((lane >> 3) == rr) {
+                const int pc = t ^ (4 * i) ^ (2 * (rr & 1));
+                u32x4 w0 = ds_read16(nb + 32 * pc), w1 = ds_read16<16>(nb + 32 * pc);
+                lds_wait(w0, w1);
+                const uint2 c0 = codes_bf16x8(make_uint4(w0.x, w0.y, w0.z, w0.w), ks);
+                const uint2 c1 = codes_bf16x8(make_uint4(w1.x, w1.y, w1.z, w1.w), ks);
+                ds_write16(b + 1024 * i + 16 * lane, u32x4{c0.x, c0.y, c1.x, c1.y});
+            }
+            if ((lane >> 3) == (o & 7)) {
+                u32x4 w0 = ds_read16(nb + 2 * D + 32 * t), w1 = ds_read16<16>(nb + 2 * D + 32 * t);
+                lds_wait(w0, w1);
+                const uint2 c0 = codes_bf16x8(make_uint4(w0.x, w0.y, w0.z, w0.w), vs);
+                const uint2 c1 = codes_bf16x8(make_uint4(w1.x, w1.y, w1.z, w1.w), vs);
+                ds_write16(b + KT + 1024 * i + 16 * lane, u32x4{c0.x, c0.y, c1.x, c1.y});
             }
         }
     }

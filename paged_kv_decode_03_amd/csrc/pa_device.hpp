@@ -180,10 +180,11 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const lds_void*)p;
 }
 
-// LDS reads written as inline asm: the compiler cannot tell which LDS bytes a
-// pending global->LDS load writes, and would otherwise wait for every vector
-// load in flight before each LDS read. The caller orders them with
-// wait_vmcnt before and lds_wait after.
+// LDS reads and writes written as inline asm: the compiler cannot tell which
+// LDS bytes a pending global->LDS load writes, and would otherwise wait for
+// every vector load in flight before each LDS access. The caller orders them
+// with wait_vmcnt before and lds_wait after (a wave's LDS accesses are
+// performed in issue order, so a read sees the same wave's earlier writes).
 template <int OFF = 0>
 __device__ __forceinline__ u32x4 ds_read16(uint32_t addr) {
     u32x4 v;
@@ -196,8 +197,18 @@ __device__ __forceinline__ u32x2 ds_read8(uint32_t addr) {
     asm volatile("ds_read_b64 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF) : "memory");
     return v;
 }
+template <int OFF = 0>
+__device__ __forceinline__ void ds_write16(uint32_t addr, u32x4 v) {
+    asm volatile("ds_write_b128 %0, %1 offset:%2" : : "v"(addr), "v"(v), "i"(OFF) : "memory");
+}
 // Wait for the LDS reads above; the operands tie their results to this point so
 // that no use is scheduled before it.
+__device__ __forceinline__ void lds_wait(u32x4& a) {
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a) : : "memory");
+}
+__device__ __forceinline__ void lds_wait(u32x4& a, u32x4& b) {
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b) : : "memory");
+}
 __device__ __forceinline__ void lds_wait(u32x4& a, u32x4& b, u32x4& c, u32x4& d, u32x4& e, u32x4& f,
                                          u32x4& g, u32x4& h) {
     asm volatile("s_waitcnt lgkmcnt(0)"

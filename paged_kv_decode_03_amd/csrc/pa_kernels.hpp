@@ -41,6 +41,11 @@ struct DecodeArgs {
     int partition_size;   // 0 = one pass; else partition / minimum piece, tokens
     int num_partitions;   // workspace slots per (s, h) (1 for one pass)
     Dtype q_dtype, cache;
+    // New tokens written by the balanced decode itself (null: none): token s of
+    // key / value [S][Hkv][D] (q dtype) goes to slot slot_mapping[s].
+    const void* key = nullptr;
+    const void* value = nullptr;
+    const int64_t* slot_mapping = nullptr;
 };
 
 struct ReduceArgs {

@@ -9,21 +9,10 @@
 // One thread moves one 16-byte vector of one (token, kv head) row: 4 fp32 or
 // 8 bf16 activations. Consecutive threads take consecutive vectors of a row,
 // so both the read of `key` and the write into the slot's row are coalesced.
-#include "pa_device.hpp"
-#include "pa_kernels.hpp"
+#include "pa_write_row.hpp"
 
 namespace pa {
 namespace {
-
-// clamp(rint(x / s), -127, 127) with the correctly rounded fp32 quotient;
-// a NaN quotient gives 0.
-__device__ __forceinline__ int8_t quantize_i8(float x, float s) {
-    float t = __fdiv_rn(x, s);
-    if (t != t) return 0;
-    float r = rintf(t);
-    r = fminf(fmaxf(r, -127.0f), 127.0f);
-    return (int8_t)(int)r;
-}
 
 template <Dtype ACT, Dtype CACHE>
 __global__ __launch_bounds__(256) void write_kv_kernel(WriteArgs a, int64_t total) {
@@ -35,64 +24,9 @@ __global__ __launch_bounds__(256) void write_kv_kernel(WriteArgs a, int64_t tota
         const int64_t tok = idx / per_tok;
         const int r = (int)(idx - tok * per_tok);
         const int g = r / nv;
-        const int v = r - g * nv;
-        const int64_t slot = a.slot_mapping[tok];
-        if (slot < 0) continue;
-        const int64_t b = slot / a.block_size;
-        const int64_t o = slot - b * a.block_size;
-        const int64_t src = (tok * a.num_kv_heads + g) * a.head_dim + (int64_t)v * VEC;
-        const int64_t dst = ((b * a.num_kv_heads + g) * a.block_size + o) * a.head_dim +
-                            (int64_t)v * VEC;
-        if constexpr (CACHE != I8) {
-            constexpr int E = (ACT == F32) ? 4 : 2;
-            *reinterpret_cast<uint4*>((char*)a.k_cache + dst * E) =
-                ld16((const char*)a.key + src * E);
-            *reinterpret_cast<uint4*>((char*)a.v_cache + dst * E) =
-                ld16((const char*)a.value + src * E);
-        } else {
-            constexpr int E = (ACT == F32) ? 4 : 2;
-            const float ks = a.k_scale[b * a.num_kv_heads + g];
-            const float vs = a.v_scale[b * a.num_kv_heads + g];
-            const uint4 kw = ld16((const char*)a.key + src * E);
-            const uint4 vw = ld16((const char*)a.value + src * E);
-            float kx[VEC], vx[VEC];
-            const uint32_t kwa[4] = {kw.x, kw.y, kw.z, kw.w};
-            const uint32_t vwa[4] = {vw.x, vw.y, vw.z, vw.w};
-            if constexpr (ACT == F32) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    kx[i] = __uint_as_float(kwa[i]);
-                    vx[i] = __uint_as_float(vwa[i]);
-                }
-            } else {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    kx[2 * i] = bf16lo(kwa[i]);
-                    kx[2 * i + 1] = bf16hi(kwa[i]);
-                    vx[2 * i] = bf16lo(vwa[i]);
-                    vx[2 * i + 1] = bf16hi(vwa[i]);
-                }
-            }
-            uint32_t kq[VEC / 4], vq[VEC / 4];
-#pragma unroll
-            for (int w = 0; w < VEC / 4; ++w) {
-                uint32_t kk = 0, vv = 0;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    kk |= (uint32_t)(uint8_t)quantize_i8(kx[4 * w + i], ks) << (8 * i);
-                    vv |= (uint32_t)(uint8_t)quantize_i8(vx[4 * w + i], vs) << (8 * i);
-                }
-                kq[w] = kk;
-                vq[w] = vv;
-            }
-            if constexpr (VEC == 8) {
-                *reinterpret_cast<uint2*>((int8_t*)a.k_cache + dst) = make_uint2(kq[0], kq[1]);
-                *reinterpret_cast<uint2*>((int8_t*)a.v_cache + dst) = make_uint2(vq[0], vq[1]);
-            } else {
-                *reinterpret_cast<uint32_t*>((int8_t*)a.k_cache + dst) = kq[0];
-                *reinterpret_cast<uint32_t*>((int8_t*)a.v_cache + dst) = vq[0];
-            }
-        }
+        write_vector<ACT, CACHE>(a.key, a.value, a.k_cache, a.v_cache, a.slot_mapping, a.k_scale,
+                                 a.v_scale, a.num_kv_heads, a.head_dim, a.block_size, tok, g,
+                                 r - g * nv);
     }
 }
 

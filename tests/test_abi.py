@@ -126,3 +126,25 @@ def test_binding_rejects_host_tensors():
     with pytest.raises(ValueError):
         pa.write_kv_cache(x, x, torch.zeros(8, 4, 16, 64), torch.zeros(8, 4, 16, 64),
                           torch.zeros(4, dtype=torch.int64))
+
+
+def write_decode(**kw):
+    args = dict(key=FAKE, value=FAKE, slots=FAKE, out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, MB=8,
+                lens=FAKE, ks=None, vs=None, scale=0.125, S=4, Hq=32, Hkv=8, D=128, B=16, NB=64,
+                maxL=128, P=64, to=FAKE, tm=FAKE, ts=FAKE, cnt=FAKE, qdt=BF16, cdt=BF16)
+    args.update(kw)
+    a = args
+    return pa.lib().pa_write_decode_balanced(
+        a["key"], a["value"], a["slots"], a["out"], a["q"], a["k"], a["v"], a["bt"], a["MB"],
+        a["lens"], a["ks"], a["vs"], a["scale"], a["S"], a["Hq"], a["Hkv"], a["D"], a["B"], a["NB"],
+        a["maxL"], a["P"], a["to"], a["tm"], a["ts"], a["cnt"], a["qdt"], a["cdt"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(slots=None), NULL), (dict(key=None), NULL), (dict(value=None), NULL),
+    (dict(cnt=None), NULL), (dict(key=MIS), ALIGN), (dict(value=MIS), ALIGN),
+    (dict(P=8), SHAPE), (dict(cdt=I8), NULL), (dict(qdt=F32), DTYPE),
+    (dict(S=0, slots=None), OK),
+])
+def test_write_decode_validation(kw, code):
+    assert write_decode(**kw) == code

@@ -499,3 +499,57 @@ def test_full_size_sampled(cfg):
     print(f"[full] cfg{cfg} seqs {seqs} max err {err:.3e} (partitions) {errb:.3e} (balanced)"
           f" {errt:.3e} (balanced, 64-token pieces)", flush=True)
     assert err <= tol(case) and errb <= tol(case) and errt <= tol(case)
+
+
+# ---- write + decode in one call (pa_write_decode_balanced) ------------------------
+
+FUSED = ["cfg2s", "cfg3s", "cfg4s", "cfg5s", "g8_i8", "g4_b32", "mid_g4_bf16", "mid_g8_i8",
+         "mid_g8_cow", "cfg1", "mha_bf16_d128", "g2_i8_bf16q"]
+
+
+@pytest.mark.parametrize("name", FUSED)
+def test_write_decode_matches_two_calls(name):
+    """The new tokens' slots start as poison: the call must write them before any
+    load of their chunk. Output and pool are bit-identical to pa_write_kv_cache
+    followed by pa_decode_balanced (MFMA instances: one launch; the others fall
+    back to the two kernels)."""
+    print(f"[fused] {name}", flush=True)
+    case, dc, ok, ov, ref = prepared(name)
+    P = 64
+
+    def pre_pool():
+        k, v = poison_pool(case)
+        if dc.pre_slots.numel():
+            pa.write_kv_cache(dc.pre_key, dc.pre_value, k, v, dc.pre_slots, dc.k_scale,
+                              dc.v_scale)
+        return k, v
+
+    # two calls
+    k2, v2 = pre_pool()
+    pa.write_kv_cache(dc.key, dc.value, k2, v2, dc.slot_mapping, dc.k_scale, dc.v_scale)
+    ws2 = pa.balanced_workspace(case.S, case.Hq, case.Hkv, case.D, case.max_context_len, P, "cuda")
+    out2 = torch.empty_like(dc.q)
+    pa.decode_balanced(out2, dc.q, k2, v2, dc.block_tables, dc.context_lens, float(case.scale),
+                       case.max_context_len, P, *ws2, k_scale=dc.k_scale, v_scale=dc.v_scale)
+    # one call, twice (the second on a pool that already holds the tokens)
+    k1, v1 = pre_pool()
+    ws1 = pa.balanced_workspace(case.S, case.Hq, case.Hkv, case.D, case.max_context_len, P, "cuda")
+    outs = []
+    for _ in range(2):
+        out1 = torch.full_like(dc.q, float("nan"))
+        pa.write_decode_balanced(dc.key, dc.value, dc.slot_mapping, out1, dc.q, k1, v1,
+                                 dc.block_tables, dc.context_lens, float(case.scale),
+                                 case.max_context_len, P, *ws1, k_scale=dc.k_scale,
+                                 v_scale=dc.v_scale)
+        outs.append(out1)
+    sync()
+    assert int(ws1[3].abs().sum()) == 0, "counters not reset"
+    assert np.array_equal(dev_to_host(k1).view(np.uint8), dev_to_host(k2).view(np.uint8))
+    assert np.array_equal(dev_to_host(v1).view(np.uint8), dev_to_host(v2).view(np.uint8))
+    assert np.array_equal(dev_to_host(k1).view(np.uint8), ok.view(np.uint8))
+    want = dev_to_host(out2)
+    for o in outs:
+        assert np.array_equal(dev_to_host(o), want)
+    err = np.abs(as_f64(outs[0]) - ref).max()
+    print(f"[fused] {name} max err {err:.3e}", flush=True)
+    assert err <= tol(case)
