@@ -19,7 +19,9 @@ from HBM. Prints ONE JSON line.
 value = algorithmic bytes of the step (KV in context counted once per unique
 physical token, plus Q, output, block-table entries, context lengths, int8
 scales, and the write's read + store of the new K/V) / step time.
-Two timed passes of K steps each on the stream the kernels run on. The step
+W warm-up steps come first, continued until 0.1 s of steps have run (the
+GPU's clocks settle over the first tens of milliseconds under load). Then two
+timed passes of K steps each on the stream the kernels run on. The step
 clock brackets the K steps with one pair of HIP events and nothing between
 them (an event recorded between launches costs several microseconds of its
 own); the kernel clock repeats the K steps with an event pair around each
@@ -48,6 +50,7 @@ HBM_PEAK_GBS = 8000.0
 # smallest piece (tokens) of the balanced schedule: a few 16-token chunks per
 # wave range keeps every wave of the persistent grid busy on short batches
 BALANCED_MIN_PIECE = 128
+WARMUP_S = 0.1
 KERNEL_SOURCES = ["pa_decode_mfma.hip", "pa_decode_valu.hip", "pa_decode_common.hpp",
                   "pa_device.hpp", "pa_kernels.hpp", "pa_write_row.hpp"]
 
@@ -206,15 +209,21 @@ def main():
         if not balanced and P > 0:
             pa.decode_splitk_reduce(out, *ws, dc.context_lens, maxL, P)
 
-    for i in range(args.warmup):
-        step(i)
+    # W warm-up steps, continued until WARMUP_S of steps have run: under load
+    # the GPU's clocks take tens of milliseconds to settle.
+    w0, t0 = 0, time.perf_counter()
+    while w0 < args.warmup or time.perf_counter() - t0 < WARMUP_S:
+        step(w0)
+        w0 += 1
+        if w0 % 16 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     # 1. the step clock: K steps with nothing recorded between the two events
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     t_start.record(stream)
     for i in range(args.steps):
-        step(args.warmup + i)
+        step(w0 + i)
     t_end.record(stream)
     torch.cuda.synchronize()
     ms_per_step = t_start.elapsed_time(t_end) / args.steps
@@ -223,7 +232,7 @@ def main():
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
     for i in range(args.steps):
-        step(args.warmup + args.steps + i, evs[i])
+        step(w0 + args.steps + i, evs[i])
     torch.cuda.synchronize()
     pair_ms = np.array([a.elapsed_time(b) for a, b in evs])
     # One launch per step: the launch period of pass 1 bounds the launch's
@@ -243,6 +252,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_steps_run": w0,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",

@@ -197,8 +197,11 @@ int pa_decode_balanced(void *out, const void *q, const void *k_cache, const void
  * write of every sequence's new token (as pa_write_kv_cache with
  * num_tokens = num_seqs) followed by pa_decode_balanced. For the MFMA
  * instances (bf16 q, G = 4 or 8, head_dim 128) both run in one launch: the
- * wave that loads the chunk holding a sequence's new token writes that token
- * first; otherwise the two kernels run one after the other on `stream`.
+ * wave that consumes the chunk holding a sequence's new token loads the
+ * token's rows with it, stores them into the slot and uses them in place of
+ * the chunk's old row (int8: the codes of the chunk's block scales), so the
+ * kernel never reads back what it stores. Otherwise the two kernels run one
+ * after the other on `stream`.
  *
  *   key, value    [num_seqs][num_kv_heads][head_dim], q_dtype: row s is the new
  *                 token of sequence s.

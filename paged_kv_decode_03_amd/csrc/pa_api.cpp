@@ -17,7 +17,6 @@
 namespace {
 
 constexpr int kVersion = 10100;   // 1.1.0
-constexpr int NW_THREADS = 256;   // threads per decode workgroup
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -113,7 +112,7 @@ namespace pa {
 
 // Resident workgroups per CU (occupancy calculator) times the CU count of the
 // stream's device, remembered per (kernel, device).
-int balanced_grid(const void* kernel, hipStream_t st) {
+int balanced_grid(const void* kernel, int threads, hipStream_t st) {
     static std::mutex mu;
     static std::map<std::pair<const void*, int>, int> cache;
     int dev = 0;
@@ -127,7 +126,7 @@ int balanced_grid(const void* kernel, hipStream_t st) {
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return -1;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, NW_THREADS, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) !=
         hipSuccess)
         return -1;
     const int grid = cus * (per_cu > 0 ? per_cu : 1);

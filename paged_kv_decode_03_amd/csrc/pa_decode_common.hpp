@@ -236,11 +236,12 @@ __device__ __forceinline__ void decode_partitions(const DecodeArgs& a) {
 // Workgroups are dealt round-robin to the 8 XCDs, so the workgroup index is
 // remapped to give each XCD a contiguous run of ranges (neighbouring
 // sequences, e.g. those sharing prefix blocks, then share that XCD's L2).
+template <int NWG>                   // waves per workgroup
 struct BalancedShared {
-    int wave_tot[NW];
+    int wave_tot[NWG];
     long long total;
-    int s0[NW];
-    long long base0[NW];
+    int s0[NWG];
+    long long base0[NWG];
 };
 
 // Position of one chunk in the segment list (all fields wave-uniform).
@@ -276,8 +277,9 @@ struct WaveRange {
 // Set-up shared by the balanced drivers: chunk counts, their scan over the
 // sequences, the range size C and the position of each wave's first chunk.
 // Ends with a workgroup barrier; returns false for a wave with no work.
-template <int G, int D>
-__device__ __forceinline__ bool balanced_setup(const DecodeArgs& a, BalancedShared& sh, WaveRange& r) {
+template <int G, int D, int NWG>
+__device__ __forceinline__ bool balanced_setup(const DecodeArgs& a, BalancedShared<NWG>& sh,
+                                               WaveRange& r) {
     const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
     const int S = a.num_seqs, Hkv = a.num_kv_heads;
     const int W = gridDim.x;
@@ -288,7 +290,7 @@ __device__ __forceinline__ bool balanced_setup(const DecodeArgs& a, BalancedShar
                            : (int)(blockIdx.x % nx) * (W / nx) + (int)(blockIdx.x / nx);
 
     // 1. chunk counts per sequence: thread t sums its slice of sequences
-    const int K = (S + NW * 64 - 1) / (NW * 64);
+    const int K = (S + NWG * 64 - 1) / (NWG * 64);
     const int sb = min(S, tid * K), se = min(S, sb + K);
     int my = 0;
     for (int s = sb; s < se; ++s) my += (ld_const(a.context_lens, s) + CHUNK - 1) / CHUNK;
@@ -303,7 +305,7 @@ __device__ __forceinline__ bool balanced_setup(const DecodeArgs& a, BalancedShar
     int wbase = 0;
     for (int v = 0; v < wave; ++v) wbase += sh.wave_tot[v];
     const int excl = wbase + inc - my;               // chunks of sequences before sb
-    if (tid == NW * 64 - 1) sh.total = (long long)Hkv * (wbase + inc);
+    if (tid == NWG * 64 - 1) sh.total = (long long)Hkv * (wbase + inc);
     if (w == 0) {
         // sequences with an empty context get zeros (no piece covers them)
         for (int s = sb; s < se; ++s)
@@ -313,14 +315,14 @@ __device__ __forceinline__ bool balanced_setup(const DecodeArgs& a, BalancedShar
     }
     __syncthreads();
     const long long T = uniform64(sh.total);
-    const long long Wv = (long long)W * NW;
+    const long long Wv = (long long)W * NWG;
     long long C = (T + Wv - 1) / Wv;
     if (C < a.partition_size / CHUNK) C = a.partition_size / CHUNK;
     if (C < 1) C = 1;
 
     // 2. locate the sequence holding the first chunk of each wave's range
-    for (int v = 0; v < NW; ++v) {
-        const long long X0v = ((long long)w * NW + v) * C;
+    for (int v = 0; v < NWG; ++v) {
+        const long long X0v = ((long long)w * NWG + v) * C;
         if ((long long)Hkv * excl <= X0v && X0v < (long long)Hkv * (excl + my)) {
             long long base = (long long)Hkv * excl;
             for (int s = sb; s < se; ++s) {
@@ -336,7 +338,7 @@ __device__ __forceinline__ bool balanced_setup(const DecodeArgs& a, BalancedShar
     }
     __syncthreads();
     r.C = C;
-    r.wv = (long long)w * NW + wave;                 // this wave's range index
+    r.wv = (long long)w * NWG + wave;                 // this wave's range index
     r.X0 = r.wv * C;
     if (r.X0 >= T) return false;                     // uniform across the wave
     r.X1 = min(T, r.X0 + C);
@@ -413,9 +415,9 @@ struct PieceEnd {
 template <class Core>
 __device__ __forceinline__ void decode_balanced(const DecodeArgs& a) {
     constexpr int G = Core::G, D = Core::D;
-    __shared__ BalancedShared sh;
+    __shared__ BalancedShared<NW> sh;
     WaveRange r;
-    if (!balanced_setup<G, D>(a, sh, r)) return;
+    if (!balanced_setup<G, D, NW>(a, sh, r)) return;
     SegPos cur = r.cur;
     Core core(a);
     core.begin_segment(cur.s, cur.g);
@@ -467,11 +469,11 @@ __device__ __forceinline__ void decode_balanced(const DecodeArgs& a) {
 // next segment are waited for there (so the compiler never sees them pending
 // inside the loop), and so are the output stores, which may complete out of
 // order with loads.
-template <class Core>
+template <class Core, int NWG>
 __device__ __forceinline__ void decode_balanced_ring(const DecodeArgs& a) {
     constexpr int G = Core::G, D = Core::D, R = Core::R, SLOT = Core::SLOT, DPC = Core::DPC;
-    __shared__ BalancedShared sh;
-    __shared__ __attribute__((aligned(16))) char ring[NW * R * SLOT];
+    __shared__ BalancedShared<NWG> sh;
+    __shared__ __attribute__((aligned(16))) char ring[NWG * R * SLOT];
     if (a.slot_mapping != nullptr && blockIdx.x == 0) {
         // new tokens of sequences with an empty context: no chunk carries them
         for (int s = threadIdx.x; s < a.num_seqs; s += blockDim.x)
@@ -481,7 +483,7 @@ __device__ __forceinline__ void decode_balanced_ring(const DecodeArgs& a) {
                         Core::write_vector_at(a, s, g, v);
     }
     WaveRange r;
-    if (!balanced_setup<G, D>(a, sh, r)) return;
+    if (!balanced_setup<G, D, NWG>(a, sh, r)) return;
     char* const mine = ring + uniform(threadIdx.x >> 6) * (R * SLOT);
     SegPos cur = r.cur;
     Core core(a);
@@ -509,7 +511,7 @@ __device__ __forceinline__ void decode_balanced_ring(const DecodeArgs& a) {
     for (int i = 0;; ++i) {
         wait_vmcnt<(R - 1) * DPC>();                 // chunk i is in its slot
         char* const sp = mine + slot * SLOT;
-        if (writes && cur.c + 1 == cur.n) core.patch_new_token(sp, cur.s, cur.g, cur.L);
+        if (writes && cur.c + 1 == cur.n) core.patch_new_token(sp, cur.g, cur.L);
         const typename Core::Chunk ch = core.fetch(sp);   // the slot is free again
         issue_next(sp);
         slot = (slot + 1 == R) ? 0 : slot + 1;

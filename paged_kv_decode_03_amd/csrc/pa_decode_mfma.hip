@@ -70,8 +70,8 @@ struct MfmaCore {
     // by ds_read, so the chunks in flight hold no VGPRs -----------------------
     static constexpr int KT = 16 * D * CE;       // bytes of one 16-token K (or V) tile
     static constexpr int NDK = KT / 1024;        // 1 KB load instructions per tile
-    static constexpr int NEW = 2 * KT + (Q8 ? 16 : 0);   // K, V, the int8 scales, then
-    static constexpr int SLOT = NEW + 4 * D;             // a new token's bf16 K and V rows
+    static constexpr int NEW = 2 * KT + (Q8 ? 16 : 0);   // K, V, the int8 scales, then a new
+    static constexpr int SLOT = NEW + 4 * D + 16;        // token's bf16 K and V rows and slot
     static constexpr int DPC = 2 * NDK + (Q8 ? 2 : 0);   // vector memory instructions per chunk
     static constexpr int R = Q8 ? 4 : 2;         // ring slots per wave
     // The K tile is stored with its 16-byte pieces permuted inside each row, so
@@ -124,12 +124,17 @@ struct MfmaCore {
     }
 
     // Start the loads of chunk c of segment (s, g) into ring slot `slot`
-    // (DPC vector memory instructions; one more with `fresh`, which also loads
-    // sequence s's new K and V rows of kv head g from key / value).
+    // (DPC vector memory instructions; two more with `fresh`, which also load
+    // sequence s's new K and V rows of kv head g from key / value, and its
+    // slot_mapping entry).
     __device__ void issue(char* slot, int s, int g, int c, bool fresh) const {
-        if (fresh && lane < 32) {                // lanes 0..15: K, 16..31: V, 16 bytes each
-            const char* src = (const char*)(lane < 16 ? a.key : a.value);
-            dma16(src + (((int64_t)s * a.num_kv_heads + g) * D + 8 * (lane & 15)) * 2, slot + NEW);
+        if (fresh) {
+            if (lane < 32) {                     // lanes 0..15: K, 16..31: V, 16 bytes each
+                const char* src = (const char*)(lane < 16 ? a.key : a.value);
+                dma16(src + (((int64_t)s * a.num_kv_heads + g) * D + 8 * (lane & 15)) * 2,
+                      slot + NEW);
+            }
+            if (lane < 2) dma4((const char*)(a.slot_mapping + s) + 4 * lane, slot + NEW + 4 * D);
         }
         const int phys = ld_uniform(a.block_tables, (int64_t)s * a.max_blocks_per_seq + (c >> shift));
         const int64_t off = phys * block_stride + g * head_stride + (int64_t)(c & shift) * CHUNK * D;
@@ -155,32 +160,30 @@ struct MfmaCore {
 
     // Ring slot `slot` holds the last chunk of segment (s, g), loaded with
     // `fresh`: the chunk as the cache held it, and sequence s's new K and V
-    // rows. Its new token (position L - 1) is written here: into the cache slot
-    // slot_mapping[s] (lanes 0..31, one 16-byte vector each), and into the
-    // chunk in LDS, where each lane overwrites the bytes of that row which its
-    // own loads of the chunk brought in. Both take the bytes the write takes
-    // (a copy, or int8 codes with the block's scales), so the chunk is the one
-    // a load after the write would give. A negative slot writes nothing.
-    __device__ void patch_new_token(char* slot, int s, int g, int L) const {
-        const int64_t sl = ld_uniform(a.slot_mapping, (int64_t)s);
+    // rows and slot. Its new token (position L - 1) is written here: into the
+    // cache slot, and into the chunk in LDS, where each lane overwrites the
+    // bytes of that row which its own loads of the chunk brought in. Both take
+    // the bytes the write takes (a copy, or int8 codes), so the chunk is the one
+    // a load after the write would give. The slot is the one of position L - 1,
+    // in the chunk's block, whose int8 scales are already in the slot. A
+    // negative slot writes nothing.
+    __device__ void patch_new_token(char* slot, int g, int L) const {
+        const uint32_t b = lds_addr(slot), nb = b + NEW;
+        u32x2 sv = ds_read8<4 * D>(nb);
+        u32x2 sc = ds_read8<Q8 ? 2 * KT : 0>(b);
+        lds_wait(sv, sc);
+        const int64_t sl = uniform64((long long)(((uint64_t)sv.y << 32) | sv.x));
         if (sl < 0) return;
         const int o = (L - 1) & (CHUNK - 1);     // the token's row in the chunk
-        const uint32_t b = lds_addr(slot), nb = b + NEW;
-        float ks = 1.0f, vs = 1.0f;
-        if constexpr (Q8) {
-            const int64_t sc = (sl / a.block_size) * a.num_kv_heads + g;
-            ks = ld_uniform(a.k_scale, sc);
-            vs = ld_uniform(a.v_scale, sc);
-        }
-        if (lane < 32) {
-            u32x4 w = ds_read16(nb + 16 * lane);
-            lds_wait(w);
-            const bool isk = lane < 16;
-            put_vector<BF16, CT>(const_cast<void*>(isk ? a.k_cache : a.v_cache),
-                                 slot_row(sl, g, lane & 15, 8, a.num_kv_heads, D, a.block_size),
-                                 make_uint4(w.x, w.y, w.z, w.w), isk ? ks : vs);
-        }
+        const int64_t blk = sl >> (4 + shift), off = sl & (a.block_size - 1);
+        const int64_t row = ((blk * a.num_kv_heads + g) * a.block_size + off) * D;
         if constexpr (!Q8) {
+            if (lane < 32) {                     // lanes 0..15: K, 16..31: V, 16 bytes each
+                u32x4 w = ds_read16(nb + 16 * lane);
+                lds_wait(w);
+                char* dst = (char*)(lane < 16 ? a.k_cache : a.v_cache) + (row + 8 * (lane & 15)) * 2;
+                *reinterpret_cast<uint4*>(dst) = make_uint4(w.x, w.y, w.z, w.w);
+            }
             // load o/4 moves row o: K piece kpiece(t, o/4) and V piece t, lanes 16*(o%4) + t
             if ((lane >> 4) == (o & 3)) {
                 const int i = o >> 2, t = lane & 15;
@@ -191,25 +194,34 @@ struct MfmaCore {
                 ds_write16(b + KT + 1024 * i + 16 * lane, vw);
             }
         } else {
+            // Every lane quantises 4 values once: lane l takes bytes 8*(l/32) ..
+            // of 16-byte vector l%32 of the rows (K for l%32 < 16, else V), dims
+            // e .. e+3 with e = 8*(l%16) + 4*(l/32). It stores the 4 codes into
+            // the cache row, and into LDS over the rows already read: K codes at
+            // nb + e, V codes at nb + D + e.
+            const int v = lane & 31, half = lane >> 5;
+            const bool isk = v < 16;
+            const int e = 8 * (v & 15) + 4 * half;
+            u32x2 w = ds_read8(nb + 16 * v + 8 * half);
+            lds_wait(w);
+            const uint32_t code = codes4(bf16lo(w.x), bf16hi(w.x), bf16lo(w.y), bf16hi(w.y),
+                                         __uint_as_float(isk ? sc.x : sc.y));
+            *reinterpret_cast<uint32_t*>((int8_t*)(isk ? a.k_cache : a.v_cache) + row + e) = code;
+            ds_write4(nb + (isk ? 0 : D) + e, code);
             // load o/8 moves row o. K: lanes 8*rr + t, rr = 2*(o%4) + (o/4)%2,
             // piece t ^ 4*(o/8) ^ 2*(rr%2); V: lanes 8*(o%8) + t, piece t. A
             // piece is 16 codes, dims 16*piece .. +15.
             const int i = o >> 3, t = lane & 7;
             const int rr = 2 * (o & 3) + ((o >> 2) & 1);
             if ((lane >> 3) == rr) {
-                const int pc = t ^ (4 * i) ^ (2 * (rr & 1));
-                u32x4 w0 = ds_read16(nb + 32 * pc), w1 = ds_read16<16>(nb + 32 * pc);
-                lds_wait(w0, w1);
-                const uint2 c0 = codes_bf16x8(make_uint4(w0.x, w0.y, w0.z, w0.w), ks);
-                const uint2 c1 = codes_bf16x8(make_uint4(w1.x, w1.y, w1.z, w1.w), ks);
-                ds_write16(b + 1024 * i + 16 * lane, u32x4{c0.x, c0.y, c1.x, c1.y});
+                u32x4 c = ds_read16(nb + 16 * (t ^ (4 * i) ^ (2 * (rr & 1))));
+                lds_wait(c);
+                ds_write16(b + 1024 * i + 16 * lane, c);
             }
             if ((lane >> 3) == (o & 7)) {
-                u32x4 w0 = ds_read16(nb + 2 * D + 32 * t), w1 = ds_read16<16>(nb + 2 * D + 32 * t);
-                lds_wait(w0, w1);
-                const uint2 c0 = codes_bf16x8(make_uint4(w0.x, w0.y, w0.z, w0.w), vs);
-                const uint2 c1 = codes_bf16x8(make_uint4(w1.x, w1.y, w1.z, w1.w), vs);
-                ds_write16(b + KT + 1024 * i + 16 * lane, u32x4{c0.x, c0.y, c1.x, c1.y});
+                u32x4 c = ds_read16(nb + D + 16 * t);
+                lds_wait(c);
+                ds_write16(b + KT + 1024 * i + 16 * lane, c);
             }
         }
     }
@@ -552,7 +564,7 @@ struct MfmaCore {
 // Register budget per lane of the register-path kernel: 168 (3 waves per SIMD)
 // for G = 4, 256 (2 waves) for G = 8; enough resident waves to keep HBM busy
 // with one chunk in flight. The ring kernel is held to 2 waves per SIMD by its
-// LDS ring (64 KB per workgroup) and may use 256.
+// LDS ring (136-145 KB per 8-wave workgroup) and may use 256.
 template <int G>
 constexpr int kWavesPerEU = G == 4 ? 3 : 2;
 
@@ -562,19 +574,24 @@ void mfma_partitions(DecodeArgs a) {
     decode_partitions<MfmaCore<G, CT>>(a);
 }
 
+// The ring kernel runs one workgroup of 8 waves per CU (2 per SIMD, the LDS
+// ring filling most of the CU's LDS): two 4-wave workgroups on one CU were
+// measured to stream unevenly, the second one slower.
+constexpr int NWR = 8;
+
 template <int G, Dtype CT>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(NWR * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void mfma_balanced(DecodeArgs a) {
-    decode_balanced_ring<MfmaCore<G, CT>>(a);
+    decode_balanced_ring<MfmaCore<G, CT>, NWR>(a);
 }
 
 template <int G, Dtype CT>
 hipError_t launch(const DecodeArgs& a, Schedule sch, hipStream_t st) {
     if (sch == Schedule::Balanced) {
         const void* fn = reinterpret_cast<const void*>(&mfma_balanced<G, CT>);
-        const int grid = balanced_grid(fn, st);
+        const int grid = balanced_grid(fn, NWR * 64, st);
         if (grid <= 0) return hipErrorLaunchFailure;
-        hipLaunchKernelGGL((mfma_balanced<G, CT>), dim3(grid), dim3(NW * 64), 0, st, a);
+        hipLaunchKernelGGL((mfma_balanced<G, CT>), dim3(grid), dim3(NWR * 64), 0, st, a);
     } else {
         const int64_t nwg = (int64_t)a.num_kv_heads * a.num_seqs * a.num_partitions;
         hipLaunchKernelGGL((mfma_partitions<G, CT>), dim3((unsigned)nwg), dim3(NW * 64), 0, st, a);

@@ -263,7 +263,7 @@ template <int D, int G, Dtype QT, Dtype CT>
 hipError_t launch(const DecodeArgs& a, Schedule sch, hipStream_t st) {
     if (sch == Schedule::Balanced) {
         const void* fn = reinterpret_cast<const void*>(&valu_balanced<D, G, QT, CT>);
-        const int grid = balanced_grid(fn, st);
+        const int grid = balanced_grid(fn, NW * 64, st);
         if (grid <= 0) return hipErrorLaunchFailure;
         hipLaunchKernelGGL((valu_balanced<D, G, QT, CT>), dim3(grid), dim3(NW * 64), 0, st, a);
     } else {

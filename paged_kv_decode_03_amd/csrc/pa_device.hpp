@@ -201,12 +201,21 @@ template <int OFF = 0>
 __device__ __forceinline__ void ds_write16(uint32_t addr, u32x4 v) {
     asm volatile("ds_write_b128 %0, %1 offset:%2" : : "v"(addr), "v"(v), "i"(OFF) : "memory");
 }
+__device__ __forceinline__ void ds_write4(uint32_t addr, uint32_t v) {
+    asm volatile("ds_write_b32 %0, %1" : : "v"(addr), "v"(v) : "memory");
+}
 // Wait for the LDS reads above; the operands tie their results to this point so
 // that no use is scheduled before it.
 __device__ __forceinline__ void lds_wait(u32x4& a) {
     asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a) : : "memory");
 }
 __device__ __forceinline__ void lds_wait(u32x4& a, u32x4& b) {
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b) : : "memory");
+}
+__device__ __forceinline__ void lds_wait(u32x2& a) {
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a) : : "memory");
+}
+__device__ __forceinline__ void lds_wait(u32x2& a, u32x2& b) {
     asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b) : : "memory");
 }
 __device__ __forceinline__ void lds_wait(u32x4& a, u32x4& b, u32x4& c, u32x4& d, u32x4& e, u32x4& f,

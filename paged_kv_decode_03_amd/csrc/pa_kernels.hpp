@@ -65,7 +65,7 @@ hipError_t launch_write_kv(const WriteArgs& a, hipStream_t st);
 hipError_t launch_decode_valu(const DecodeArgs& a, Schedule sch, hipStream_t st);
 hipError_t launch_decode_mfma(const DecodeArgs& a, Schedule sch, hipStream_t st);
 // Workgroups of a balanced launch: resident workgroups per CU times CUs.
-int balanced_grid(const void* kernel, hipStream_t st);
+int balanced_grid(const void* kernel, int threads, hipStream_t st);
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t st);
 
 bool valu_supports(const DecodeArgs& a);

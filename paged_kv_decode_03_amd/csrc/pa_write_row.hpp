@@ -15,10 +15,9 @@ namespace pa {
 // clamp(rint(x / s), -127, 127) with the correctly rounded fp32 quotient;
 // a NaN quotient gives 0.
 __device__ __forceinline__ int8_t quantize_i8(float x, float s) {
-    float t = __fdiv_rn(x, s);
+    const float t = __fdiv_rn(x, s);
     if (t != t) return 0;
-    float r = rintf(t);
-    r = fminf(fmaxf(r, -127.0f), 127.0f);
+    const float r = fminf(fmaxf(rintf(t), -127.0f), 127.0f);
     return (int8_t)(int)r;
 }
 

@@ -132,6 +132,62 @@ def test_write_int8_near_ties():
         assert np.array_equal(dev_to_host(k), ok), act
 
 
+# Scales for the quantiser's two paths: ordinary ones (the reciprocal with its
+# boundary test), and ones whose reciprocal leaves the normal range or is not
+# finite (the division).
+INT8_SCALES = [1 / 127, 0.0123, 3.7e-3, 1.0, 0.125, 5.3e-5, 2.0 ** -125, 2.0 ** -126, 1e-39,
+               2.0 ** 125, 2.0 ** 126, 3e38, 0.0, -0.37, float("inf"), float("nan")]
+
+
+def _write_i8(key, value, slots, ks, vs, B, act):
+    T, _, D = key.shape
+    NB = ks.shape[0]
+    k = torch.full((NB, 1, B, D), -128, dtype=torch.int8, device="cuda")
+    v = k.clone()
+    pa.write_kv_cache(host_to_dev(key, act, "cuda"), host_to_dev(value, act, "cuda"), k, v,
+                      torch.from_numpy(slots).cuda(), torch.from_numpy(ks).cuda(),
+                      torch.from_numpy(vs).cuda())
+    ok = np.full((NB, 1, B, D), -128, np.int8)
+    ov = ok.copy()
+    oracle.write_kv_cache(key, value, ok, ov, slots, ks, vs)
+    sync()
+    return dev_to_host(k), dev_to_host(v), ok, ov
+
+
+def test_write_int8_every_bf16_value():
+    """All 65536 bf16 values through the int8 write at each scale, byte-exact."""
+    D, B = 64, 16
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    T = bits.size // D
+    key = bits.reshape(T, 1, D)
+    value = key[::-1].copy()
+    slots = np.arange(T, dtype=np.int64)
+    for sc in INT8_SCALES:
+        ks = np.full((T // B, 1), sc, np.float32)
+        k, v, ok, ov = _write_i8(key, value, slots, ks, ks.copy(), B, "bf16")
+        assert np.array_equal(k, ok) and np.array_equal(v, ov), sc
+
+
+def test_write_int8_fp32_boundaries():
+    """fp32 activations within 8 ulps of every rounding boundary k + 1/2 of
+    the code range (and a little beyond), byte-exact."""
+    D, B = 64, 16
+    for sc in (np.float32(0.0123), np.float32(1 / 127), np.float32(3.0), np.float32(2.0 ** -10)):
+        base = ((np.arange(-130, 130) + 0.5) * np.float64(sc)).astype(np.float32)
+        steps = np.arange(-8, 9, dtype=np.int32)
+        xs = (base.view(np.int32)[:, None] + steps[None, :]).reshape(-1).view(np.float32)
+        T = -(-xs.size // D)
+        T = -(-T // B) * B
+        key = np.zeros(T * D, np.float32)
+        key[:xs.size] = xs
+        key = key.reshape(T, 1, D)
+        value = -key
+        slots = np.arange(T, dtype=np.int64)
+        ks = np.full((T // B, 1), sc, np.float32)
+        k, v, ok, ov = _write_i8(key, value, slots, ks, ks.copy(), B, "f32")
+        assert np.array_equal(k, ok) and np.array_equal(v, ov), float(sc)
+
+
 # ---- decode -----------------------------------------------------------------
 
 PARITY = [(n, 0) for n in SMALL] + [
