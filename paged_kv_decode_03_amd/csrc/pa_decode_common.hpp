@@ -240,7 +240,7 @@ template <int NWG>                   // waves per workgroup
 struct BalancedShared {
     int wave_tot[NWG];
     long long total;
-    int s0[NWG];
+    int s0[NWG], L0[NWG];
     long long base0[NWG];
 };
 
@@ -292,8 +292,12 @@ __device__ __forceinline__ bool balanced_setup(const DecodeArgs& a, BalancedShar
     // 1. chunk counts per sequence: thread t sums its slice of sequences
     const int K = (S + NWG * 64 - 1) / (NWG * 64);
     const int sb = min(S, tid * K), se = min(S, sb + K);
-    int my = 0;
-    for (int s = sb; s < se; ++s) my += (ld_const(a.context_lens, s) + CHUNK - 1) / CHUNK;
+    int my = 0, L1 = 0;                              // L1: length of sequence sb, kept
+    for (int s = sb; s < se; ++s) {
+        const int L = ld_const(a.context_lens, s);
+        if (s == sb) L1 = L;
+        my += (L + CHUNK - 1) / CHUNK;
+    }
     int inc = my;                                    // inclusive scan over the workgroup
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -326,9 +330,11 @@ __device__ __forceinline__ bool balanced_setup(const DecodeArgs& a, BalancedShar
         if ((long long)Hkv * excl <= X0v && X0v < (long long)Hkv * (excl + my)) {
             long long base = (long long)Hkv * excl;
             for (int s = sb; s < se; ++s) {
-                const long long n = (long long)Hkv * ((ld_const(a.context_lens, s) + CHUNK - 1) / CHUNK);
+                const int L = s == sb ? L1 : ld_const(a.context_lens, s);
+                const long long n = (long long)Hkv * ((L + CHUNK - 1) / CHUNK);
                 if (X0v < base + n) {
                     sh.s0[v] = s;
+                    sh.L0[v] = L;
                     sh.base0[v] = base;
                     break;
                 }
@@ -345,7 +351,7 @@ __device__ __forceinline__ bool balanced_setup(const DecodeArgs& a, BalancedShar
     SegPos& cur = r.cur;
     cur.s = uniform(sh.s0[wave]);
     const long long base = uniform64(sh.base0[wave]);
-    cur.L = ld_uniform(a.context_lens, cur.s);
+    cur.L = uniform(sh.L0[wave]);
     cur.n = (cur.L + CHUNK - 1) / CHUNK;
     cur.g = (int)((r.X0 - base) / cur.n);
     cur.c = (int)((r.X0 - base) - (long long)cur.g * cur.n);
