@@ -62,6 +62,7 @@ class Oracle:
         lib.ora_decode_partials.argtypes = [_p, _p, _p, _i, _p, _p, _p, _p, _i, _p, _p, _p, _f,
                                             _i, _i, _i, _i, _i, _i64, _i, _i, _i]
         lib.ora_splitk_reduce.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i]
+        lib.ora_copy_blocks.argtypes = [_p, _p, _p, _p, _p, _i64, _i, _i, _i, _i64, _i]
         lib.ora_num_threads.restype = _i
         lib.ora_set_num_threads.argtypes = [_i]
         self.lib = lib
@@ -91,6 +92,19 @@ class Oracle:
                                          _ptr(slot_mapping), _ptr(k_scale), _ptr(v_scale), T, Hkv,
                                          D, B, NB, _DT[_dtype_of(key)], _DT[_dtype_of(k_cache)])
         self._check(rc, "ora_write_kv_cache")
+
+    def copy_blocks(self, k_cache, v_cache, block_mapping, k_scale=None, v_scale=None):
+        """Copy-on-write block copy, in place: block_mapping [n, 2] int64 (src, dst).
+        int8 pools copy their scales [NB, Hkv] too (pass them as float32 arrays)."""
+        assert k_cache.flags.c_contiguous and v_cache.flags.c_contiguous
+        for sc in (k_scale, v_scale):
+            assert sc is None or (sc.dtype == np.float32 and sc.flags.c_contiguous)
+        mapping = _c(np.asarray(block_mapping).reshape(-1, 2), np.int64)
+        NB, Hkv, B, D = k_cache.shape
+        rc = self.lib.ora_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+                                      _ptr(mapping), mapping.shape[0], Hkv, D, B, NB,
+                                      _DT[_dtype_of(k_cache)])
+        self._check(rc, "ora_copy_blocks")
 
     def decode(self, q, k_cache, v_cache, block_tables, context_lens, scale, k_scale=None,
                v_scale=None):
@@ -193,6 +207,10 @@ def decode_partials(*a, **kw):
 
 def splitk_reduce(*a, **kw):
     return default().splitk_reduce(*a, **kw)
+
+
+def copy_blocks(*a, **kw):
+    return default().copy_blocks(*a, **kw)
 
 
 def fill_cache(case):

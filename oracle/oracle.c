@@ -32,6 +32,13 @@
  *      context partitions of P tokens, each partition's normalised output with
  *      its max and sum, and the log-sum-exp combination of the partitions.
  *
+ *  ora_copy_blocks -- the copy step of the block pool's copy-on-write
+ *      reference counting (Continuous-Batching-LLM-Inference-Engine README,
+ *      feature list): for each (src, dst) pair, every byte of physical block
+ *      src -- the K and V tiles of every kv head and, for an int8 cache, its
+ *      per-(block, kv head) scales -- is copied into block dst. No block may
+ *      be the destination of two pairs or both a source and a destination.
+ *
  * Conventions (readings where the pages are silent): context_lens counts the
  * newly written token; query head h reads kv head h / (Hq / Hkv); the cache is
  * [num_blocks][Hkv][block_size][D] row-major; L = 0 gives zeros; slots < 0 are
@@ -128,6 +135,56 @@ int ora_write_kv_cache(const void *key, const void *value, void *k_cache, void *
                     memcpy((char *)k_cache + dst * esz, (const char *)key + src * esz, esz);
                     memcpy((char *)v_cache + dst * esz, (const char *)value + src * esz, esz);
                 }
+            }
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Copy-on-write block copy                                                 */
+/* ------------------------------------------------------------------------ */
+
+int ora_copy_blocks(void *k_cache, void *v_cache, float *k_scale, float *v_scale,
+                    const int64_t *block_mapping, int64_t num_pairs, int num_kv_heads,
+                    int head_dim, int block_size, int64_t num_blocks, int cache_dtype)
+{
+    if (num_pairs < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+        return -1;
+    if (cache_dtype != ORA_F32 && cache_dtype != ORA_BF16 && cache_dtype != ORA_I8)
+        return -1;
+    if (cache_dtype == ORA_I8 && (!k_scale || !v_scale))
+        return -1;
+    /* every index in range; destinations distinct and never a source */
+    char *role = calloc((size_t)num_blocks, 1);     /* 1 source, 2 destination */
+    if (!role)
+        return -1;
+    for (int64_t i = 0; i < num_pairs; ++i) {
+        int64_t src = block_mapping[2 * i], dst = block_mapping[2 * i + 1];
+        if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks || src == dst) {
+            free(role);
+            return -2;
+        }
+        role[src] |= 1;
+    }
+    for (int64_t i = 0; i < num_pairs; ++i) {
+        int64_t dst = block_mapping[2 * i + 1];
+        if (role[dst]) {
+            free(role);
+            return -2;
+        }
+        role[dst] = 2;
+    }
+    free(role);
+    const int64_t bytes = (int64_t)num_kv_heads * block_size * head_dim * elem_size(cache_dtype);
+    for (int64_t i = 0; i < num_pairs; ++i) {
+        int64_t src = block_mapping[2 * i], dst = block_mapping[2 * i + 1];
+        memcpy((char *)k_cache + dst * bytes, (const char *)k_cache + src * bytes, (size_t)bytes);
+        memcpy((char *)v_cache + dst * bytes, (const char *)v_cache + src * bytes, (size_t)bytes);
+        if (cache_dtype == ORA_I8) {
+            for (int64_t g = 0; g < num_kv_heads; ++g) {
+                k_scale[dst * num_kv_heads + g] = k_scale[src * num_kv_heads + g];
+                v_scale[dst * num_kv_heads + g] = v_scale[src * num_kv_heads + g];
             }
         }
     }

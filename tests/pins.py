@@ -25,6 +25,7 @@ What pins what:
 """
 from __future__ import annotations
 
+import dataclasses
 import math
 from decimal import Decimal, getcontext
 from fractions import Fraction
@@ -32,6 +33,7 @@ from fractions import Fraction
 import numpy as np
 import torch
 
+import oracle
 import synth
 
 # --------------------------------------------------------------------------
@@ -497,5 +499,55 @@ def pin_zero_length(ora):
     assert np.isfinite(got).all()
 
 
+def pin_copy_blocks(ora):
+    """Copy-on-write copy: a sequence that gets private copies of its shared
+    prefix blocks (its table repointed at the copies) attends to the same values,
+    so the oracle's decode must be bit-identical -- whatever the copy drops (V,
+    a kv head, the int8 scales) or misplaces changes it. Every byte outside the
+    destination blocks is untouched, and invalid mappings are refused."""
+    cow = synth.Spec("cow prefix, 2 kv heads", 8, ("uniform", 2, 60), 4, 2, 16, 4, act="bf16",
+                     cache="bf16", max_len=60, prefix_groups=2, prefix_tokens=16)
+    for spec, seed in ((cow, 3), (cow.replace(cache="i8"), 5), (small_specs()[4], 4)):
+        case = synth.make_case(spec, seed)
+        k, v = ora.fill_cache(case)
+        ref = ora.decode_case(case, k, v)
+        B = case.B
+        nblk = -(-case.context_lens.astype(np.int64) // B)
+        used = set(int(b) for s in range(case.S) for b in case.block_tables[s, :nblk[s]])
+        free = [b for b in range(case.num_blocks) if b not in used and b != case.poison_block]
+        pairs, bt = [], case.block_tables.copy()
+        for s in range(case.S):
+            for lb in range(int(nblk[s])):
+                b = int(bt[s, lb])
+                if case.refcount[b] > 1 and free and len(pairs) < 24:
+                    dst = free.pop()
+                    pairs.append((b, dst))
+                    bt[s, lb] = dst
+                    break
+        assert len(pairs) >= 4, "the case must have shared blocks and free ones"
+        k2, v2 = k.copy(), v.copy()
+        ks2 = None if case.k_scale is None else case.k_scale.copy()
+        vs2 = None if case.v_scale is None else case.v_scale.copy()
+        ora.copy_blocks(k2, v2, np.array(pairs), ks2, vs2)
+        moved = dataclasses.replace(case, block_tables=bt, k_scale=ks2, v_scale=vs2)
+        got = ora.decode_case(moved, k2, v2)
+        assert np.array_equal(got, ref), f"{spec.name}: decode changed after the copy"
+        dsts = [d for _, d in pairs]
+        keep = np.ones(case.num_blocks, dtype=bool)
+        keep[dsts] = False
+        assert np.array_equal(k2[keep].view(np.uint8), k[keep].view(np.uint8)), "stray K bytes"
+        assert np.array_equal(v2[keep].view(np.uint8), v[keep].view(np.uint8)), "stray V bytes"
+        src0, dst0 = pairs[0]
+        for bad in ([(src0, dst0), (pairs[1][0], dst0)],          # one destination twice
+                    [(src0, dst0), (dst0, pairs[1][1])],          # a destination is also a source
+                    [(src0, case.num_blocks)], [(src0, src0)]):    # out of range; onto itself
+            try:
+                ora.copy_blocks(k2.copy(), v2.copy(), np.array(bad), ks2, vs2)
+            except oracle.OracleError:
+                continue
+            raise AssertionError(f"invalid mapping {bad} accepted")
+
+
 ALL_PINS = [pin_unpaged_sdpa, pin_decimal_bruteforce, pin_closed_forms, pin_onehot,
-            pin_placement, pin_splitk, pin_write_int8, pin_write_copy, pin_zero_length]
+            pin_placement, pin_splitk, pin_write_int8, pin_write_copy, pin_zero_length,
+            pin_copy_blocks]

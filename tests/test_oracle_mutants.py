@@ -44,6 +44,17 @@ MUTANTS = [
      "int64_t t1 = (j + 1) * P;"),
     ("write ignores skip", "if (slot < 0)\n            continue;\n        int64_t b",
      "if (slot < -1)\n            continue;\n        int64_t b"),
+    ("copy drops V",
+     "memcpy((char *)v_cache + dst * bytes, (const char *)v_cache + src * bytes, (size_t)bytes);",
+     ";"),
+    ("copy moves one kv head",
+     "const int64_t bytes = (int64_t)num_kv_heads * block_size * head_dim * elem_size(cache_dtype);",
+     "const int64_t bytes = (int64_t)block_size * head_dim * elem_size(cache_dtype);"),
+    ("copy keeps the destination's scales",
+     "k_scale[dst * num_kv_heads + g] = k_scale[src * num_kv_heads + g];", ";"),
+    ("copy direction swapped",
+     "int64_t src = block_mapping[2 * i], dst = block_mapping[2 * i + 1];\n        memcpy",
+     "int64_t dst = block_mapping[2 * i], src = block_mapping[2 * i + 1];\n        memcpy"),
 ]
 
 CHILD = r"""
