@@ -100,6 +100,58 @@ def cpu_baseline(case, budget_s: float):
                       f"{reps} repetitions in {el:.1f} s, fp64"}
 
 
+def bench_copy_blocks(args, spec, torch, np, pa, synth):
+    """pa_copy_blocks on the workload's pool: N (src, dst) pairs, sources drawn
+    from the blocks in use, destinations from the free ones (or, past them, from
+    a pool grown to hold them). Algorithmic bytes per pair: read + write of the
+    block in both pools."""
+    from gpu_helpers import fill_pool, to_device
+    case = synth.make_case(spec, args.config)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    dc = to_device(case, dev)
+    k, v = fill_pool(dc, dev)
+    n = args.copy_blocks
+    NB = case.num_blocks
+    if 2 * n > NB:                                   # room for n distinct sources and destinations
+        grow = 2 * n - NB
+        k = torch.cat([k, torch.zeros((grow,) + tuple(k.shape[1:]), dtype=k.dtype, device=dev)])
+        v = torch.cat([v, torch.zeros_like(k[NB:])])
+        NB = k.shape[0]
+    rng = np.random.default_rng(args.config)
+    ids = rng.permutation(NB)
+    mapping = torch.from_numpy(np.stack([ids[:n], ids[n:2 * n]], axis=1).astype(np.int64)).to(dev)
+    ks = vs = None
+    if spec.cache == "i8":
+        ks = torch.ones((NB, case.Hkv), dtype=torch.float32, device=dev)
+        vs = torch.ones_like(ks)
+    block_bytes = case.Hkv * case.B * case.D * k.element_size()
+    nbytes = n * 2 * 2 * block_bytes + n * 16 + (n * 2 * 2 * case.Hkv * 4 if ks is not None else 0)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(max(args.warmup, 10)):
+        pa.copy_blocks(k, v, mapping, ks, vs)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        pa.copy_blocks(k, v, mapping, ks, vs)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "copy-on-write block copy GB/s", "value": round(gbs, 2), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": spec.cache, "data": "synthetic",
+        "config": {"workload": spec.name + " pool", "pairs": n, "block_bytes": block_bytes,
+                   "num_kv_heads": case.Hkv, "block_size": case.B, "head_dim": case.D},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "pa_copy_blocks", "bytes_per_launch": nbytes},
+    }), flush=True)
+
+
 def copy_probe(torch, nbytes=1 << 30, reps=10):
     src = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
     dst = torch.empty_like(src)
@@ -133,6 +185,9 @@ def main():
     ap.add_argument("--rotate-gb", type=float, default=2.0)
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-blocks", type=int, default=0, metavar="N",
+                    help="instead of the decode step, time pa_copy_blocks copying N blocks of "
+                         "the workload's pool (all kv heads, K and V) into free blocks")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only time a device copy of 1 GiB (read 1 GiB + write 1 GiB); the "
                          "reference for calibrating rocprofv3 FETCH_SIZE / WRITE_SIZE")
@@ -155,6 +210,9 @@ def main():
     from gpu_helpers import fill_pool, to_device
 
     spec = synth.CONFIGS[args.config]
+    if args.copy_blocks:
+        bench_copy_blocks(args, spec, torch, np, pa, synth)
+        return
     balanced = args.schedule == "balanced"
     if args.partition is not None:
         P = args.partition

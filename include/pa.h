@@ -222,6 +222,31 @@ int pa_write_decode_balanced(const void *key, const void *value, const int64_t *
                              float *tmp_max, float *tmp_sum, int32_t *counters, pa_dtype q_dtype,
                              pa_dtype cache_dtype, void *stream);
 
+/*
+ * pa_copy_blocks -- the copy step of copy-on-write block sharing
+ * ("Continuous-Batching-LLM-Inference-Engine" README, feature list: the paged
+ * KV cache's block pool with copy-on-write reference counts): before a
+ * sequence writes into a block it shares, the block manager gives it a private
+ * copy. For each pair i, every byte of physical block block_mapping[2i] of
+ * k_cache and of v_cache (all kv heads) -- and, for an int8 cache, its
+ * k_scale / v_scale entries -- is copied into block block_mapping[2i+1].
+ *
+ *   k_cache, v_cache  [num_blocks][num_kv_heads][block_size][head_dim], cache_dtype,
+ *                     16-byte aligned, written in place.
+ *   k_scale, v_scale  [num_blocks][num_kv_heads] fp32, int8 cache only (else ignored).
+ *   block_mapping     [num_pairs][2] int64 (src, dst), device. Every id must be in
+ *                     [0, num_blocks); no block may be the destination of two pairs,
+ *                     both a source and a destination, or its own source (the
+ *                     copies then do not depend on their order). PA_CHECK=1 verifies.
+ * head_dim * element size must be a multiple of 16 bytes; num_pairs <= 65535.
+ * Enqueued on `stream`; num_pairs = 0 does nothing. Rolling a sequence back
+ * (e.g. rejected draft tokens) needs no device work: the caller lowers its
+ * context length and releases the blocks past it.
+ */
+int pa_copy_blocks(void *k_cache, void *v_cache, float *k_scale, float *v_scale,
+                   const int64_t *block_mapping, int num_pairs, int num_kv_heads, int head_dim,
+                   int block_size, int64_t num_blocks, pa_dtype cache_dtype, void *stream);
+
 /* Workspace slots per (sequence, query head) that pa_decode_balanced needs:
  * ceil(ceil(max_context_len / 16) / (min_piece_tokens / 16)) + 1, or 0 when
  * max_context_len <= 0 or min_piece_tokens < 16. */

@@ -12,6 +12,8 @@ Entry points (same names as the C ABI without the ``pa_`` prefix):
   decode                   paged decode attention (one pass or split-K partials)
   decode_splitk_reduce     log-sum-exp reduce of split-K partials
   decode_balanced          work-balanced split-K decode with the reduce fused in
+  write_decode_balanced    the new-token write and decode_balanced in one call
+  copy_blocks              copy-on-write copy of whole blocks (K, V, int8 scales)
 plus ``workspace`` / ``balanced_workspace`` (allocate with torch) and
 ``paged_attention`` (decode into a new output tensor, any schedule).
 """
@@ -47,6 +49,8 @@ _lib.pa_write_decode_balanced.restype = _i
 _lib.pa_write_decode_balanced.argtypes = [_p, _p, _p] + _lib.pa_decode_balanced.argtypes
 _lib.pa_balanced_slots.restype = _i
 _lib.pa_balanced_slots.argtypes = [_i, _i]
+_lib.pa_copy_blocks.restype = _i
+_lib.pa_copy_blocks.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i64, _i, _p]
 _lib.pa_decode_splitk_reduce.restype = _i
 _lib.pa_decode_splitk_reduce.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p]
 
@@ -167,6 +171,28 @@ def decode_splitk_reduce(out, tmp_out, tmp_max, tmp_sum, context_lens, max_conte
                                       _ptr(context_lens), S, Hq, D, int(max_context_len),
                                       int(partition_size), _dt(out), _stream(stream, dev))
     _check("pa_decode_splitk_reduce", rc)
+
+
+def copy_blocks(k_cache, v_cache, block_mapping, k_scale=None, v_scale=None, stream=None):
+    """Copy every byte of block block_mapping[i, 0] into block block_mapping[i, 1]
+    of both pools (and of the int8 scales); block_mapping [n, 2] int64 on the
+    device, destinations distinct and never a source."""
+    dev = _dev(k_cache, v_cache, block_mapping, k_scale, v_scale)
+    if block_mapping.dtype != torch.int64 or block_mapping.dim() != 2 \
+            or block_mapping.shape[1] != 2:
+        raise TypeError("block_mapping must be int64 [n, 2]")
+    if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
+        raise ValueError("k_cache and v_cache must match")
+    NB, Hkv, B, D = k_cache.shape
+    if k_cache.dtype == torch.int8:
+        if k_scale is None or v_scale is None or k_scale.shape != (NB, Hkv) \
+                or v_scale.shape != (NB, Hkv) or k_scale.dtype != torch.float32 \
+                or v_scale.dtype != torch.float32:
+            raise ValueError("an int8 pool needs fp32 k_scale and v_scale [NB, Hkv]")
+    rc = _lib.pa_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+                             _ptr(block_mapping), block_mapping.shape[0], Hkv, D, B, NB,
+                             _dt(k_cache), _stream(stream, dev))
+    _check("pa_copy_blocks", rc)
 
 
 def balanced_slots(max_context_len: int, min_piece_tokens: int) -> int:

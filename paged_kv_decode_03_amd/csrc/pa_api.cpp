@@ -106,6 +106,27 @@ int check_new_slots(const int64_t* slot_mapping, const int32_t* block_tables,
     return PA_OK;
 }
 
+// PA_CHECK=1, block copies: every id in [0, num_blocks); no destination
+// twice, none also a source, none its own source.
+int check_copy_mapping(const int64_t* block_mapping, int num_pairs, int64_t num_blocks,
+                       hipStream_t st) {
+    std::vector<int64_t> m;
+    if (!fetch(m, block_mapping, 2 * (int64_t)num_pairs, st)) return PA_ERR_LAUNCH;
+    std::map<int64_t, int> role;                     // 1 source, 2 destination
+    for (int i = 0; i < num_pairs; ++i) {
+        const int64_t src = m[2 * i], dst = m[2 * i + 1];
+        if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks || src == dst)
+            return PA_ERR_INDEX;
+        role[src] |= 1;
+    }
+    for (int i = 0; i < num_pairs; ++i) {
+        int& r = role[m[2 * i + 1]];
+        if (r) return PA_ERR_INDEX;
+        r = 2;
+    }
+    return PA_OK;
+}
+
 }  // namespace
 
 namespace pa {
@@ -225,6 +246,30 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
     const pa::Schedule sch = pa::Schedule::Partitions;
     return launch_status(mfma ? pa::launch_decode_mfma(a, sch, st)
                               : pa::launch_decode_valu(a, sch, st));
+}
+
+int pa_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale,
+                   const int64_t* block_mapping, int num_pairs, int num_kv_heads, int head_dim,
+                   int block_size, int64_t num_blocks, pa_dtype cache_dtype, void* stream) {
+    if (num_pairs < 0 || num_kv_heads < 1 || head_dim < 1 || block_size < 1 || num_blocks < 1)
+        return PA_ERR_SHAPE;
+    if (!valid_cache(cache_dtype)) return PA_ERR_DTYPE;
+    const int elt = cache_dtype == PA_F32 ? 4 : cache_dtype == PA_BF16 ? 2 : 1;
+    if (((int64_t)head_dim * elt) % 16) return PA_ERR_SHAPE;
+    if (!k_cache || !v_cache || (num_pairs > 0 && !block_mapping)) return PA_ERR_NULL;
+    if (cache_dtype == PA_I8 && (!k_scale || !v_scale)) return PA_ERR_NULL;
+    if (!aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_ALIGN;
+    if (num_pairs > 65535) return PA_ERR_SHAPE;      // one grid row per pair
+    if (num_pairs == 0) return PA_OK;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (check_enabled()) {
+        const int rc = check_copy_mapping(block_mapping, num_pairs, num_blocks, st);
+        if (rc) return rc;
+    }
+    pa::CopyArgs a{k_cache, v_cache, cache_dtype == PA_I8 ? k_scale : nullptr,
+                   cache_dtype == PA_I8 ? v_scale : nullptr, block_mapping, num_pairs,
+                   num_kv_heads, (int64_t)num_kv_heads * block_size * head_dim * elt};
+    return launch_status(pa::launch_copy_blocks(a, st));
 }
 
 int pa_balanced_slots(int max_context_len, int min_piece_tokens) {

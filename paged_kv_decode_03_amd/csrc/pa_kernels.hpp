@@ -48,6 +48,16 @@ struct DecodeArgs {
     const int64_t* slot_mapping = nullptr;
 };
 
+struct CopyArgs {
+    void* k_cache;
+    void* v_cache;
+    float* k_scale;          // int8 cache: [NB][Hkv], copied with the blocks; else null
+    float* v_scale;
+    const int64_t* block_mapping;   // [num_pairs][2] (src, dst)
+    int num_pairs, num_kv_heads;
+    int64_t block_bytes;     // bytes of one block of one pool, a multiple of 16
+};
+
 struct ReduceArgs {
     void* out;
     const float* tmp_out;
@@ -67,6 +77,7 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, Schedule sch, hipStream_t st)
 // Workgroups of a balanced launch: resident workgroups per CU times CUs.
 int balanced_grid(const void* kernel, int threads, hipStream_t st);
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t st);
+hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t st);
 
 bool valu_supports(const DecodeArgs& a);
 bool mfma_supports(const DecodeArgs& a);

@@ -148,3 +148,24 @@ def write_decode(**kw):
 ])
 def test_write_decode_validation(kw, code):
     assert write_decode(**kw) == code
+
+
+def copy(**kw):
+    args = dict(k=FAKE, v=FAKE, ks=None, vs=None, m=FAKE, n=3, Hkv=8, D=128, B=16, NB=64,
+                dt=BF16)
+    args.update(kw)
+    return pa.lib().pa_copy_blocks(args["k"], args["v"], args["ks"], args["vs"], args["m"],
+                                   args["n"], args["Hkv"], args["D"], args["B"], args["NB"],
+                                   args["dt"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(k=None), NULL), (dict(v=None), NULL), (dict(m=None), NULL),
+    (dict(dt=I8), NULL),                         # int8 pool without scales
+    (dict(k=MIS), ALIGN), (dict(n=-1), SHAPE), (dict(Hkv=0), SHAPE), (dict(NB=0), SHAPE),
+    (dict(D=4), SHAPE),                           # 8-byte rows cannot be copied in 16-byte vectors
+    (dict(n=70000), SHAPE), (dict(dt=7), DTYPE),
+    (dict(n=0), OK), (dict(n=0, m=None), OK),    # nothing to copy: no launch
+])
+def test_copy_blocks_validation(kw, code):
+    assert copy(**kw) == code
