@@ -182,6 +182,9 @@ def main():
     ap.add_argument("--schedule", choices=["balanced", "partitions"], default="balanced")
     ap.add_argument("--separate-write", action="store_true",
                     help="balanced schedule: the write kernel, then the decode (two launches)")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture each step (one graph per pool copy) in a HIP graph and time "
+                         "graph replays")
     ap.add_argument("--rotate-gb", type=float, default=2.0)
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -276,12 +279,35 @@ def main():
         if w0 % 16 == 0:
             torch.cuda.synchronize()
     torch.cuda.synchronize()
+    run = step
+    if args.graph:
+        # one graph per pool copy, captured on a side stream (the step's kernels
+        # allocate nothing and clear nothing with memsets, so they capture as is)
+        graphs = []
+        cap = torch.cuda.Stream(dev)
+        cap.wait_stream(stream)
+        for r in range(R):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                step(r)
+            graphs.append(g)
+        torch.cuda.synchronize()
+
+        def run(i, ev=None):
+            if ev is not None:
+                ev[0].record(stream)
+            graphs[i % R].replay()
+            if ev is not None:
+                ev[1].record(stream)
+        for i in range(2 * R):
+            run(i)
+        torch.cuda.synchronize()
     # 1. the step clock: K steps with nothing recorded between the two events
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     t_start.record(stream)
     for i in range(args.steps):
-        step(w0 + i)
+        run(w0 + i)
     t_end.record(stream)
     torch.cuda.synchronize()
     ms_per_step = t_start.elapsed_time(t_end) / args.steps
@@ -290,16 +316,18 @@ def main():
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
     for i in range(args.steps):
-        step(w0 + args.steps + i, evs[i])
+        run(w0 + args.steps + i, evs[i])
     torch.cuda.synchronize()
     pair_ms = np.array([a.elapsed_time(b) for a, b in evs])
     # One launch per step: the launch period of pass 1 bounds the launch's
     # duration from above, and unlike an event pair it carries no marker cost.
-    dec_mean = ms_per_step if fused else float(pair_ms.mean())
+    # with graphs the event pairs wrap a whole replay, so the step clock is used
+    dec_mean = ms_per_step if fused or args.graph else float(pair_ms.mean())
 
     step_bytes = tr["decode"]["total"] + tr["write"]
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    kernel_bytes = tr["decode"]["total"] + (tr["write"] if fused else 0)
+    # the timed unit: the decode launch, or with graphs the whole step's replay
+    kernel_bytes = tr["decode"]["total"] + (tr["write"] if fused or args.graph else 0)
     achieved = kernel_bytes / (dec_mean * 1e-3) / 1e9
     sched = "fused" if fused else args.schedule
     traffic = measured_traffic(args.config, P, sched)
@@ -322,7 +350,8 @@ def main():
             "num_kv_heads": case.Hkv, "head_dim": D, "block_size": case.B,
             "context_lens": list(spec.lens), "sum_context": tr["sum_len"],
             "unique_kv_tokens": tr["unique_tokens"], "partition_size": P, "pool_copies": R,
-            "schedule": args.schedule + ("" if not balanced or fused else " (separate write)"),
+            "schedule": args.schedule + ("" if not balanced or fused else " (separate write)")
+                        + (", HIP graph replays" if args.graph else ""),
             "step": ("write + balanced split-K decode + combine, one launch" if fused else
                      "write; balanced split-K decode (combine fused)" if balanced else
                      "write; split-K decode; reduce" if P else "write; one-pass decode"),
@@ -331,7 +360,8 @@ def main():
         "seq_tokens_per_s": round(S / (ms_per_step * 1e-3), 1),
         "context_tokens_per_s": round(tr["sum_len"] / (ms_per_step * 1e-3), 1),
         "decode_kernel_us": {"mean": round(dec_mean * 1e3, 2),
-                             "clock": "launch period" if fused else "event pairs",
+                             "clock": ("launch period" if fused or args.graph
+                                       else "event pairs"),
                              "event_pairs": {
                                  "mean": round(float(pair_ms.mean()) * 1e3, 2),
                                  "p10": round(float(np.percentile(pair_ms, 10)) * 1e3, 2),
@@ -342,7 +372,8 @@ def main():
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "kernel": ("pa_write_decode_balanced" if fused else "pa_decode_balanced" if balanced
+            "kernel": ("graph replay of the whole step" if args.graph and not fused else
+                       "pa_write_decode_balanced" if fused else "pa_decode_balanced" if balanced
                        else "pa_decode (split-K partials)" if P else "pa_decode"),
             "bytes_per_launch": kernel_bytes,
         },
