@@ -32,6 +32,8 @@ constexpr float kNegInf = -__builtin_huge_valf();
 constexpr int NW = 4;        // waves per workgroup
 constexpr int CHUNK = 16;    // tokens per chunk
 constexpr int kFastShare = 144;   // see balanced_setup
+constexpr int kChunkCost = 16;    // cost units per chunk (see balanced_setup)
+constexpr int kSegCost = 32;      // cost units per segment (see balanced_setup)
 
 template <bool BASE2>
 __device__ __forceinline__ float rel_weight(float m, float M) {
@@ -240,9 +242,10 @@ __device__ __forceinline__ void decode_partitions(const DecodeArgs& a) {
 template <int NWG>                   // waves per workgroup
 struct BalancedShared {
     int wave_tot[NWG];
-    long long total;
-    int s0[NWG], L0[NWG];
-    long long base0[NWG];
+    long long wave_cost[NWG];
+    long long total, total_cost;
+    int s0[NWG + 1], L0[NWG + 1];
+    long long base0[NWG + 1], cbase0[NWG + 1];
 };
 
 // Position of one chunk in the segment list (all fields wave-uniform).
@@ -250,6 +253,7 @@ struct SegPos {
     int s, g, c;      // sequence, kv head, chunk within the segment
     int L, n;         // context length of s and its chunk count
     long long A;      // list index of chunk 0 of segment (s, g)
+    long long Y;      // cost position where chunk 0 of segment (s, g) starts
 };
 
 __device__ __forceinline__ SegPos next_pos(const DecodeArgs& a, SegPos p) {
@@ -258,6 +262,7 @@ __device__ __forceinline__ SegPos next_pos(const DecodeArgs& a, SegPos p) {
         return p;
     }
     p.c = 0;
+    p.Y += (long long)p.n * kChunkCost + kSegCost;
     p.A += p.n;
     if (++p.g < a.num_kv_heads) return p;
     p.g = 0;
@@ -269,25 +274,26 @@ __device__ __forceinline__ SegPos next_pos(const DecodeArgs& a, SegPos p) {
     return p;
 }
 
-// The cut of the chunk list into wave ranges. Workgroup w owns the contiguous
-// run [w * span, (w + 1) * span), span = H * (Cf + Cs): its first H waves take
-// Cf chunks each, the other H waves Cs <= Cf each. With H = 0 every range has
-// Cs chunks.
+// The cut of the cost line (the chunk list weighted as balanced_setup says)
+// into wave ranges. Workgroup w owns the contiguous run [w * span,
+// (w + 1) * span), span = H * (Cf + Cs): its first H waves take Cf units each,
+// the other H waves Cs <= Cf each. With H = 0 every range has Cs units.
 struct Ranges {
-    int Cf, Cs, H;
-    __device__ int span() const { return H ? H * (Cf + Cs) : Cs; }
-    // first chunk of range j (j = w * 2H + v; any j >= 0)
+    long long Cf, Cs;  // range lengths in cost units
+    int H;
+    __device__ long long span() const { return H ? H * (Cf + Cs) : Cs; }
+    // first cost unit of range j (j = w * 2H + v; any j >= 0)
     __device__ long long start(long long j) const {
         if (!H) return j * Cs;
         const long long w = j / (2 * H);
         const int v = (int)(j - w * 2 * H);
         return w * span() + (v < H ? v * Cf : H * Cf + (v - H) * Cs);
     }
-    // range holding chunk X
+    // range holding cost unit X
     __device__ long long of(long long X) const {
         if (!H) return X / Cs;
         const long long w = X / span();
-        const int o = (int)(X - w * span());
+        const long long o = X - w * span();
         return w * 2 * H + (o < H * Cf ? o / Cf : H + (o - H * Cf) / Cs);
     }
 };
@@ -314,27 +320,60 @@ __device__ __forceinline__ bool balanced_setup(const DecodeArgs& a, BalancedShar
     const int w = (W % nx) ? (int)blockIdx.x
                            : (int)(blockIdx.x % nx) * (W / nx) + (int)(blockIdx.x / nx);
 
-    // 1. chunk counts per sequence: thread t sums its slice of sequences
+    // Ranges are cut in cost units, kChunkCost to a chunk, so that the shares
+    // are not rounded to whole chunks. A segment of n chunks costs
+    // n kChunkCost + kSegCost, the kSegCost units standing for its fixed work
+    // (query loads, merge and stores) and sitting before its first chunk. Two
+    // chunks' worth was level with or faster than whole-chunk cuts with no
+    // segment cost on every measured batch (1-3% on the mixed-length ones);
+    // 24 and 48 units were 4-5% slower where all contexts have one length,
+    // as the cuts then fall just off the segment boundaries.
+    // Chunk c of segment (s, g) spans the units from
+    // P = Y_s + g (n_s kChunkCost + kSegCost) + kSegCost + c kChunkCost, Y_s
+    // the cost of the sequences before s, and belongs to the range holding
+    // its last unit P + kChunkCost - 1.
+    constexpr int CC = kChunkCost, SC = kSegCost;
+
+    // 1. chunk counts and costs per sequence: thread t sums its slice
     const int K = (S + NWG * 64 - 1) / (NWG * 64);
     const int sb = min(S, tid * K), se = min(S, sb + K);
     int my = 0, L1 = 0;                              // L1: length of sequence sb, kept
+    long long myc = 0;
     for (int s = sb; s < se; ++s) {
         const int L = ld_const(a.context_lens, s);
         if (s == sb) L1 = L;
-        my += (L + CHUNK - 1) / CHUNK;
+        const int n = (L + CHUNK - 1) / CHUNK;
+        my += n;
+        myc += n ? (long long)n * CC + SC : 0;
     }
-    int inc = my;                                    // inclusive scan over the workgroup
+    int inc = my;                                    // inclusive scans over the workgroup
+    long long incc = myc;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
         const int y = __shfl_up(inc, off);
-        if (lane >= off) inc += y;
+        const long long yc = __shfl_up(incc, off);
+        if (lane >= off) {
+            inc += y;
+            incc += yc;
+        }
     }
-    if (lane == 63) sh.wave_tot[wave] = inc;
+    if (lane == 63) {
+        sh.wave_tot[wave] = inc;
+        sh.wave_cost[wave] = incc;
+    }
     __syncthreads();
     int wbase = 0;
-    for (int v = 0; v < wave; ++v) wbase += sh.wave_tot[v];
+    long long wbasec = 0;
+    for (int v = 0; v < wave; ++v) {
+        wbase += sh.wave_tot[v];
+        wbasec += sh.wave_cost[v];
+    }
     const int excl = wbase + inc - my;               // chunks of sequences before sb
-    if (tid == NWG * 64 - 1) sh.total = (long long)Hkv * (wbase + inc);
+    const long long exclc = wbasec + incc - myc;     // their cost, per kv head
+    if (tid == NWG * 64 - 1) {
+        sh.total = (long long)Hkv * (wbase + inc);
+        sh.total_cost = (long long)Hkv * (wbasec + incc);
+    }
     if (w == 0) {
         // sequences with an empty context get zeros (no piece covers them)
         for (int s = sb; s < se; ++s)
@@ -344,62 +383,79 @@ __device__ __forceinline__ bool balanced_setup(const DecodeArgs& a, BalancedShar
     }
     __syncthreads();
     const long long T = uniform64(sh.total);
+    const long long Tc = uniform64(sh.total_cost);
     const long long Wv = (long long)W * NWG;
-    const int C = (int)((T + Wv - 1) / Wv);         // mean range; T < 2^31
-    const int cmin = max(1, a.partition_size / CHUNK);
+    const long long C = (Tc + Wv - 1) / Wv;          // mean range (cost units)
+    const long long cmin = (long long)max(1, a.partition_size / CHUNK) * CC;
     // Age-weighted ranges. The first NWG/2 waves of an 8-wave workgroup are
     // dispatched first, one per SIMD, and the second half shares those SIMDs.
     // Under load the older wave of a SIMD wins the arbitration for memory
     // instruction issue: with equal ranges it finished 1.2-1.35x sooner, then
     // sat idle while the younger one ran alone. It gets a share kFastShare/256
-    // of the pair's chunks. (The CU's waves share one bandwidth, so this mostly
+    // of the pair's cost. (The CU's waves share one bandwidth, so this mostly
     // shortens the idle time rather than the launch: 0-4% faster measured.)
-    // Every range keeps at least cmin chunks.
+    // Every range keeps at least the cost of a minimum piece, cmin.
     Ranges rg;
     if (NWG == 8) {
         rg.H = NWG / 2;
-        rg.Cs = max(cmin, (int)((2LL * C * (256 - kFastShare)) / 256));
+        rg.Cs = max(cmin, 2 * C * (256 - kFastShare) / 256);
         rg.Cf = max(rg.Cs, 2 * C - rg.Cs);
     } else {
         rg.H = 0;
         rg.Cs = rg.Cf = max(cmin, C);
     }
 
-    // 2. locate the sequence holding the first chunk of each wave's range
-    auto locate = [&](long long X, int* ss, int* Ls, long long* bs) {
-        if ((long long)Hkv * excl <= X && X < (long long)Hkv * (excl + my)) {
-            long long base = (long long)Hkv * excl;
+    // 2. locate the sequence holding the cost position where each wave's
+    // range starts (v = NWG: the next workgroup's first, where the last ends)
+    auto locate = [&](long long Y, int v) {
+        if ((long long)Hkv * exclc <= Y && Y < (long long)Hkv * (exclc + myc)) {
+            long long base = (long long)Hkv * excl, cbase = (long long)Hkv * exclc;
             for (int s = sb; s < se; ++s) {
                 const int L = s == sb ? L1 : ld_const(a.context_lens, s);
-                const long long n = (long long)Hkv * ((L + CHUNK - 1) / CHUNK);
-                if (X < base + n) {
-                    *ss = s;
-                    *Ls = L;
-                    *bs = base;
+                const int n = (L + CHUNK - 1) / CHUNK;
+                const long long cost = n ? (long long)Hkv * ((long long)n * CC + SC) : 0;
+                if (Y < cbase + cost) {
+                    sh.s0[v] = s;
+                    sh.L0[v] = L;
+                    sh.base0[v] = base;
+                    sh.cbase0[v] = cbase;
                     break;
                 }
-                base += n;
+                base += (long long)Hkv * n;
+                cbase += cost;
             }
         }
     };
-    for (int v = 0; v < NWG; ++v)
-        locate(rg.start((long long)w * NWG + v), &sh.s0[v], &sh.L0[v], &sh.base0[v]);
+    for (int v = 0; v <= NWG; ++v) locate(rg.start((long long)w * NWG + v), v);
     __syncthreads();
+    // chunk list index of the first chunk whose last unit is at or after Y
+    auto chunk_at = [&](long long Y, int v, SegPos* p) -> long long {
+        if (Y >= Tc) return T;
+        const int s = uniform(sh.s0[v]), L = uniform(sh.L0[v]);
+        const long long base = uniform64(sh.base0[v]), cbase = uniform64(sh.cbase0[v]);
+        const int n = (L + CHUNK - 1) / CHUNK;
+        const long long sc = (long long)n * CC + SC;
+        const int g = (int)((Y - cbase) / sc);
+        const long long off = (Y - cbase) - (long long)g * sc;    // < sc, so c < n
+        const int c = off < SC ? 0 : (int)((off - SC) / CC);
+        if (p) {
+            p->s = s;
+            p->L = L;
+            p->n = n;
+            p->g = g;
+            p->c = c;
+            p->A = base + (long long)g * n;
+            p->Y = cbase + (long long)g * sc + SC;
+        }
+        return base + (long long)g * n + c;
+    };
     r.rg = rg;
     r.wv = (long long)w * NWG + wave;                 // this wave's range index
-    r.X0 = rg.start(r.wv);
-    if (r.X0 >= T) return false;                     // uniform across the wave
-    r.X1 = min(T, rg.start(r.wv + 1));
-    auto pos = [&](long long X, int s, int L, long long base, SegPos& p) {
-        p.s = s;
-        p.L = L;
-        p.n = (L + CHUNK - 1) / CHUNK;
-        p.g = (int)((X - base) / p.n);
-        p.c = (int)((X - base) - (long long)p.g * p.n);
-        p.A = base + (long long)p.g * p.n;
-    };
-    pos(r.X0, uniform(sh.s0[wave]), uniform(sh.L0[wave]), uniform64(sh.base0[wave]), r.cur);
-    return true;
+    const long long Y0 = rg.start(r.wv);
+    if (Y0 >= Tc) return false;                      // uniform across the wave
+    r.X0 = chunk_at(Y0, wave, &r.cur);
+    r.X1 = chunk_at(min(Tc, rg.start(r.wv + 1)), wave + 1, nullptr);
+    return r.X0 < r.X1;                              // a range inside a segment's fixed part is empty
 }
 
 // End of the piece of segment p held in St (this wave's chunks of it are all
@@ -436,8 +492,9 @@ struct PieceEnd {
         if (p.A >= r.X0 && B <= r.X1) {
             core.store_final(St, p.s, p.g);
         } else {
-            const long long first = r.rg.of(p.A);
-            const int pieces = (int)(r.rg.of(B - 1) - first) + 1;
+            const long long first = r.rg.of(p.Y + kChunkCost - 1);
+            const int pieces =
+                (int)(r.rg.of(p.Y + (long long)p.n * kChunkCost - 1) - first) + 1;
             const int64_t seg = (int64_t)p.s * a.num_kv_heads + p.g;
             core.store_slot(St, seg * a.num_partitions + (r.wv - first));
             if (!last) {
