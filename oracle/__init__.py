@@ -62,6 +62,8 @@ class Oracle:
         lib.ora_decode_partials.argtypes = [_p, _p, _p, _i, _p, _p, _p, _p, _i, _p, _p, _p, _f,
                                             _i, _i, _i, _i, _i, _i64, _i, _i, _i]
         lib.ora_splitk_reduce.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i]
+        lib.ora_prefill.argtypes = [_p, _p, _p, _p, _p, _i, _p, _p, _p, _p, _f, _i, _i, _i, _i,
+                                    _i, _i, _i64, _i, _i]
         lib.ora_copy_blocks.argtypes = [_p, _p, _p, _p, _p, _i64, _i, _i, _i, _i64, _i]
         lib.ora_num_threads.restype = _i
         lib.ora_set_num_threads.argtypes = [_i]
@@ -121,6 +123,28 @@ class Oracle:
                                  _ptr(k_scale), _ptr(v_scale), float(scale), S, Hq, Hkv, D, B, NB,
                                  _DT[_dtype_of(q)], _DT[_dtype_of(k_cache)])
         self._check(rc, "ora_decode")
+        return out
+
+    def prefill(self, q, k_cache, v_cache, block_tables, context_lens, query_start_loc, scale,
+                k_scale=None, v_scale=None):
+        """Several query tokens per sequence (the newest n_s tokens of sequence
+        s, rows query_start_loc[s] .. [s+1]-1 of q), causal over the cached
+        context: returns out [num_query_tokens, Hq, D] float64."""
+        q = _c(q)
+        block_tables, context_lens = _c(block_tables, np.int32), _c(context_lens, np.int32)
+        query_start_loc = _c(query_start_loc, np.int32)
+        k_scale, v_scale = _c(k_scale, np.float32), _c(v_scale, np.float32)
+        T, Hq, D = q.shape
+        NB, Hkv, B, D2 = k_cache.shape
+        S = context_lens.shape[0]
+        assert D2 == D and block_tables.shape[0] == S and query_start_loc.shape == (S + 1,)
+        out = np.empty((T, Hq, D), dtype=np.float64)
+        rc = self.lib.ora_prefill(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                  _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
+                                  _ptr(query_start_loc), _ptr(k_scale), _ptr(v_scale),
+                                  float(scale), S, T, Hq, Hkv, D, B, NB, _DT[_dtype_of(q)],
+                                  _DT[_dtype_of(k_cache)])
+        self._check(rc, "ora_prefill")
         return out
 
     def decode_partials(self, q, k_cache, v_cache, block_tables, context_lens, scale,
@@ -199,6 +223,10 @@ def write_kv_cache(*a, **kw):
 
 def decode(*a, **kw):
     return default().decode(*a, **kw)
+
+
+def prefill(*a, **kw):
+    return default().prefill(*a, **kw)
 
 
 def decode_partials(*a, **kw):

@@ -32,6 +32,17 @@
  *      context partitions of P tokens, each partition's normalised output with
  *      its max and sum, and the log-sum-exp combination of the partitions.
  *
+ *  ora_prefill -- several new query tokens per sequence at once: the target
+ *      model's scoring of K drafted tokens in one batched pass for
+ *      speculative decoding (Continuous-Batching-LLM-Inference-Engine README,
+ *      feature list) and the prefill chunks that continuous batches mix with
+ *      decode tokens ("How brave30/mini-inference-engine works", summary and
+ *      Model Compute: prefill attention). The n_s query tokens of sequence s
+ *      are its newest tokens, already written to the cache, so query j sits
+ *      at position L_s - n_s + j and attends to the cached tokens 0 .. that
+ *      position: the causal reading of a prefix followed by new tokens. Each
+ *      row is plain decode attention over a truncated context.
+ *
  *  ora_copy_blocks -- the copy step of the block pool's copy-on-write
  *      reference counting (Continuous-Batching-LLM-Inference-Engine README,
  *      feature list): for each (src, dst) pair, every byte of physical block
@@ -228,23 +239,25 @@ static double cache_value(const problem *p, const void *cache, const float *sc,
     return x;
 }
 
-/* logit of query (s, h) against logical token t: scale * sum_d q[d] k_t[d]. */
-static double logit(const problem *p, int64_t s, int64_t h, int64_t t, int64_t b)
+/* logit of query row r, head h against logical token t held in physical
+ * block b: scale * sum_d q[r][h][d] k_t[d]. */
+static double logit(const problem *p, int64_t r, int64_t h, int64_t t, int64_t b)
 {
     int64_t g = h / (p->Hq / p->Hkv);
     int64_t o = t % p->B;
     double acc = 0.0;
     for (int64_t d = 0; d < p->D; ++d)
-        acc += load_elem(p->q, (s * p->Hq + h) * p->D + d, p->q_dtype) *
+        acc += load_elem(p->q, (r * p->Hq + h) * p->D + d, p->q_dtype) *
                cache_value(p, p->k_cache, p->k_scale, b, g, o, d);
     return p->scale * acc;
 }
 
-/* Attention of (s, h) over logical tokens [t0, t1): writes the normalised
- * output to o_out[D] and returns the max logit and the sum of exponentials.
- * Returns 0, or -2 on a bad block id. */
-static int attend_range(const problem *p, int64_t s, int64_t h, int64_t t0, int64_t t1,
-                        double *o_out, double *m_out, double *l_out, double *x)
+/* Attention of query row r, head h over logical tokens [t0, t1) of sequence
+ * s: writes the normalised output to o_out[D] and returns the max logit and
+ * the sum of exponentials. Returns 0, or -2 on a bad block id. (Decode: the
+ * query row of sequence s is row s.) */
+static int attend_range(const problem *p, int64_t s, int64_t r, int64_t h, int64_t t0,
+                        int64_t t1, double *o_out, double *m_out, double *l_out, double *x)
 {
     int64_t g = h / (p->Hq / p->Hkv);
     /* pass 1: logits and their max */
@@ -253,7 +266,7 @@ static int attend_range(const problem *p, int64_t s, int64_t h, int64_t t0, int6
         int64_t b = phys_block(p, s, t);
         if (b < 0)
             return -2;
-        x[t - t0] = logit(p, s, h, t, b);
+        x[t - t0] = logit(p, r, h, t, b);
         if (x[t - t0] > M)
             M = x[t - t0];
     }
@@ -327,7 +340,7 @@ int ora_decode(double *out, const void *q, const void *k_cache, const void *v_ca
                     o[d] = 0.0;
                 continue;
             }
-            if (attend_range(&p, s, h, 0, L, o, &m, &l, x)) {
+            if (attend_range(&p, s, s, h, 0, L, o, &m, &l, x)) {
 #pragma omp atomic write
                 err = -2;
             }
@@ -367,7 +380,7 @@ int ora_decode_partials(double *o_part, double *m_part, double *l_part, int num_
             int64_t L = context_lens[s];
             for (int64_t j = 0; j * P < L; ++j) {
                 int64_t t1 = (j + 1) * P < L ? (j + 1) * P : L;
-                if (attend_range(&p, s, h, j * P, t1, o_part + (sh * NP + j) * p.D,
+                if (attend_range(&p, s, s, h, j * P, t1, o_part + (sh * NP + j) * p.D,
                                  m_part + sh * NP + j, l_part + sh * NP + j, x)) {
 #pragma omp atomic write
                     err = -2;
@@ -415,4 +428,57 @@ int ora_splitk_reduce(double *out, const double *o_part, const double *m_part,
             o[d] /= Wsum;
     }
     return 0;
+}
+
+/* Several query tokens per sequence. Rows query_start_loc[s] ..
+ * query_start_loc[s + 1] - 1 of q and out belong to sequence s; with n_s
+ * rows and L_s = context_lens[s] (which counts them), row query_start_loc[s]
+ * + j attends to the tokens 0 .. L_s - n_s + j. Requires 0 = qsl[0] <= qsl[1]
+ * <= ... <= qsl[S] = num_query_tokens and n_s <= L_s. */
+int ora_prefill(double *out, const void *q, const void *k_cache, const void *v_cache,
+                const int32_t *block_tables, int max_blocks_per_seq, const int32_t *context_lens,
+                const int32_t *query_start_loc, const float *k_scale, const float *v_scale,
+                float scale, int num_seqs, int num_query_tokens, int num_heads,
+                int num_kv_heads, int head_dim, int block_size, int64_t num_blocks, int q_dtype,
+                int cache_dtype)
+{
+    problem p = {q, k_cache, v_cache, block_tables, context_lens, k_scale, v_scale,
+                 (double)scale, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                 max_blocks_per_seq, num_blocks, q_dtype, cache_dtype};
+    int rc = check_problem(&p);
+    if (rc)
+        return rc;
+    if (!query_start_loc || num_query_tokens < 0 || query_start_loc[0] != 0 ||
+        query_start_loc[num_seqs] != num_query_tokens)
+        return -1;
+    for (int64_t s = 0; s < p.S; ++s) {
+        int64_t n = (int64_t)query_start_loc[s + 1] - query_start_loc[s];
+        if (n < 0 || n > context_lens[s])
+            return -1;
+    }
+    int64_t maxL = 0;
+    for (int64_t s = 0; s < p.S; ++s)
+        if (context_lens[s] > maxL)
+            maxL = context_lens[s];
+    int err = 0;
+#pragma omp parallel
+    {
+        double *x = malloc(sizeof(double) * (size_t)(maxL > 0 ? maxL : 1));
+        double m, l;
+#pragma omp for schedule(dynamic)
+        for (int64_t rh = 0; rh < (int64_t)num_query_tokens * p.Hq; ++rh) {
+            int64_t r = rh / p.Hq, h = rh % p.Hq;
+            int64_t s = 0;
+            while (query_start_loc[s + 1] <= r)        /* the sequence holding row r */
+                ++s;
+            int64_t n = query_start_loc[s + 1] - query_start_loc[s];
+            int64_t pos = context_lens[s] - n + (r - query_start_loc[s]);
+            if (attend_range(&p, s, r, h, 0, pos + 1, out + rh * p.D, &m, &l, x)) {
+#pragma omp atomic write
+                err = -2;
+            }
+        }
+        free(x);
+    }
+    return err;
 }

@@ -401,6 +401,53 @@ def make_case(spec: Spec, seed: int) -> Case:
     return case
 
 
+@dataclasses.dataclass
+class Queries:
+    """Several new query tokens per sequence: rows query_start_loc[s] ..
+    query_start_loc[s + 1] - 1 of ``q`` are the newest n_s tokens of sequence
+    s (positions L_s - n_s .. L_s - 1, already in its context)."""
+    query_start_loc: np.ndarray    # int32 [S + 1]
+    q: np.ndarray                  # [T, Hq, D], activation storage dtype
+    q_lens: np.ndarray             # int64 [S], n_s
+
+    @property
+    def num_tokens(self) -> int:
+        return int(self.query_start_loc[-1])
+
+
+def make_queries(case: Case, q_lens, seed: int) -> Queries:
+    """Queries for a multi-token step over ``case``'s cache.
+
+    ``q_lens``: ("const", n), ("uniform", lo, hi) (inclusive) or a sequence
+    of per-sequence counts; each count is clipped to [0, L_s]. Q ~ N(0, 1)
+    times the spec's q_std, cast to the activation dtype."""
+    rng = np.random.default_rng(seed)
+    S, L = case.S, case.context_lens.astype(np.int64)
+    if isinstance(q_lens, tuple) and q_lens[0] == "const":
+        n = np.full(S, int(q_lens[1]), dtype=np.int64)
+    elif isinstance(q_lens, tuple) and q_lens[0] == "uniform":
+        n = rng.integers(q_lens[1], q_lens[2] + 1, size=S).astype(np.int64)
+    else:
+        n = np.asarray(q_lens, dtype=np.int64).reshape(S)
+    n = np.clip(n, 0, L)
+    qsl = np.zeros(S + 1, dtype=np.int32)
+    qsl[1:] = np.cumsum(n)
+    q32 = rng.standard_normal((int(qsl[-1]), case.Hq, case.D), dtype=np.float32)
+    if case.spec.q_std != 1.0:
+        q32 = q32 * np.float32(case.spec.q_std)
+    return Queries(query_start_loc=qsl, q=_cast(q32, case.spec.act), q_lens=n)
+
+
+# Multi-token workloads over paged caches: the speculative verify of K + 1 = 4
+# tokens per sequence on the Llama-shaped batch, and 512-token prefill chunks
+# appended to 8 cached 3584-token prefixes (contexts of 4096).
+MULTI_QUERY = {
+    "verify": (CONFIGS[2], ("const", 4)),
+    "prefill": (Spec("chunked prefill bf16", 8, ("const", 4096), 32, 8, 128, 16,
+                     act="bf16", cache="bf16", max_len=4096), ("const", 512)),
+}
+
+
 def absmax_scales(case: Case):
     """Caller-side int8 scales: absmax/127 over everything written into each
     (block, kv head), in fp32; 1.0 where absmax is 0 or the block is unused."""

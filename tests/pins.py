@@ -21,7 +21,10 @@ What pins what:
 * split-K: each partition's (o, m, l) equals dense attention over that token
   range and logsumexp; the reduce equals a logsumexp-weighted mix;
 * int8 write: every code equals exact-rational rounding (fp32 quotient with
-  ties to even, then integer with ties to even, clamp to +-127).
+  ties to even, then integer with ties to even, clamp to +-127);
+* several query tokens per sequence: torch SDPA over the dense source K/V with
+  an explicit causal mask aligned to the end of the context, and, row by row,
+  one-token decode over the context cut after the row's position.
 """
 from __future__ import annotations
 
@@ -548,6 +551,62 @@ def pin_copy_blocks(ora):
             raise AssertionError(f"invalid mapping {bad} accepted")
 
 
+def _query_mixes(case, seed):
+    """Query counts per sequence: a few tokens each, and each whole context."""
+    return [synth.make_queries(case, ("uniform", 0, 6), seed),
+            synth.make_queries(case, case.context_lens.astype(np.int64), seed + 1)]
+
+
+def pin_prefill_causal_sdpa(ora, seeds=(0, 1)):
+    """Several query tokens per sequence against torch SDPA (float64) over the
+    dense source K/V with an explicit mask: query j of n at position L - n + j
+    sees tokens 0 .. L - n + j."""
+    for spec in small_specs():
+        for seed in seeds:
+            case = synth.make_case(spec, seed)
+            k, v = ora.fill_cache(case)
+            dense = dense_kv(case, k, v)
+            for qs in _query_mixes(case, 10 * seed):
+                got = ora.prefill(qs.q, k, v, case.block_tables, case.context_lens,
+                                  qs.query_start_loc, case.scale, case.k_scale, case.v_scale)
+                q = synth.as_f32(qs.q, spec.act).astype(np.float64)
+                for s in range(case.S):
+                    a, b = int(qs.query_start_loc[s]), int(qs.query_start_loc[s + 1])
+                    n, L = b - a, int(case.context_lens[s])
+                    if n == 0:
+                        continue
+                    kk, vv = dense[s]
+                    Hq, D, Hkv = case.Hq, case.D, case.Hkv
+                    qt = torch.from_numpy(np.ascontiguousarray(q[a:b].transpose(1, 0, 2)))
+                    kt = torch.from_numpy(np.ascontiguousarray(kk.transpose(1, 0, 2)))
+                    vt = torch.from_numpy(np.ascontiguousarray(vv.transpose(1, 0, 2)))
+                    pos = L - n + np.arange(n)
+                    mask = torch.from_numpy(np.arange(L)[None, :] <= pos[:, None])
+                    ref = torch.nn.functional.scaled_dot_product_attention(
+                        qt[None], kt[None], vt[None], attn_mask=mask, scale=float(case.scale),
+                        enable_gqa=(Hq != Hkv))[0].numpy().transpose(1, 0, 2)
+                    err = np.abs(got[a:b] - ref).max()
+                    assert err <= 1e-12, f"{spec.name} seed {seed} seq {s}: |oracle - sdpa| = {err}"
+
+
+def pin_prefill_rows_are_decode(ora):
+    """Row j of sequence s equals one-token decode of that query over the
+    context truncated after its position (the decode oracle is pinned by the
+    pins above)."""
+    for spec in small_specs()[:4]:
+        case = synth.make_case(spec, 3)
+        k, v = ora.fill_cache(case)
+        for qs in _query_mixes(case, 7):
+            got = ora.prefill(qs.q, k, v, case.block_tables, case.context_lens,
+                              qs.query_start_loc, case.scale, case.k_scale, case.v_scale)
+            seq = np.repeat(np.arange(case.S), qs.q_lens)
+            j = np.arange(qs.num_tokens) - qs.query_start_loc[seq]
+            pos = case.context_lens[seq] - qs.q_lens[seq] + j
+            ref = ora.decode(qs.q, k, v, case.block_tables[seq], (pos + 1).astype(np.int32),
+                             case.scale, case.k_scale, case.v_scale)
+            assert np.array_equal(got, ref), f"{spec.name}: prefill rows differ from decode"
+
+
 ALL_PINS = [pin_unpaged_sdpa, pin_decimal_bruteforce, pin_closed_forms, pin_onehot,
             pin_placement, pin_splitk, pin_write_int8, pin_write_copy, pin_zero_length,
-            pin_copy_blocks]
+            pin_copy_blocks, pin_prefill_causal_sdpa, pin_prefill_rows_are_decode]

@@ -28,8 +28,19 @@ MUTANTS = [
     ("kv head index swapped with block", "return ((b * p->Hkv + g) * p->B + o) * p->D + d;",
      "return ((g * p->NB + b) * p->B + o) * p->D + d;"),
     ("no normalisation", "o_out[d] /= Z;", "o_out[d] /= 1.0;"),
-    ("last token dropped", "attend_range(&p, s, h, 0, L, o, &m, &l, x)",
-     "attend_range(&p, s, h, 0, L > 1 ? L - 1 : L, o, &m, &l, x)"),
+    ("last token dropped", "attend_range(&p, s, s, h, 0, L, o, &m, &l, x)",
+     "attend_range(&p, s, s, h, 0, L > 1 ? L - 1 : L, o, &m, &l, x)"),
+    ("prefill drops the diagonal", "attend_range(&p, s, r, h, 0, pos + 1,",
+     "attend_range(&p, s, r, h, 0, pos > 0 ? pos : 1,"),
+    ("prefill sees one token ahead", "attend_range(&p, s, r, h, 0, pos + 1,",
+     "attend_range(&p, s, r, h, 0, pos + 1 < context_lens[s] ? pos + 2 : pos + 1,"),
+    ("prefill rows counted from the front",
+     "int64_t pos = context_lens[s] - n + (r - query_start_loc[s]);",
+     "int64_t pos = r - query_start_loc[s];"),
+    ("prefill reads the sequence's first query row", "attend_range(&p, s, r, h, 0, pos + 1,",
+     "attend_range(&p, s, query_start_loc[s], h, 0, pos + 1,"),
+    ("prefill row to sequence off by one", "while (query_start_loc[s + 1] <= r)",
+     "while (query_start_loc[s + 1] < r)"),
     ("dequant scale dropped", "x *= (double)sc[b * p->Hkv + g];", "x *= 1.0;"),
     ("int8 truncation", "float r = nearbyintf(t);", "float r = truncf(t);"),
     ("int8 ties away from zero", "float r = nearbyintf(t);", "float r = roundf(t);"),
