@@ -47,6 +47,7 @@ sys.path.insert(0, os.path.join(ROOT, "tests"))
 
 METRIC = "decode attention GB/s and % of HBM peak; seq-tokens/sec at bf16 GQA"
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFS = 2500.0      # dense bf16 MFMA peak of MI355X
 # smallest piece (tokens) of the balanced schedule: a few 16-token chunks per
 # wave range keeps every wave of the persistent grid busy on short batches
 BALANCED_MIN_PIECE = 128
@@ -152,6 +153,131 @@ def bench_copy_blocks(args, spec, torch, np, pa, synth):
     }), flush=True)
 
 
+def multi_query_counts(case, qs, np):
+    """Algorithmic bytes and flops of one pa_prefill launch. Bytes: K and V of
+    every token of every context once per kv head (the rows of a kv head share
+    its loads), the block-table entries read, Q and the output, the lengths,
+    query starts and int8 scales. Flops: 4 D (p + 1) per query row and head (Q K^T
+    and P V over the p + 1 tokens the row sees)."""
+    L = case.context_lens.astype(np.int64)
+    Hq, Hkv, D, B = case.Hq, case.Hkv, case.D, case.B
+    elt = 1 if case.spec.cache == "i8" else 2
+    act = 4 if case.spec.act == "f32" else 2
+    nblk = (L + B - 1) // B
+    kv = int(2 * Hkv * L.sum() * D * elt)
+    scales = int(2 * Hkv * nblk.sum() * 4) if case.spec.cache == "i8" else 0
+    T = qs.num_tokens
+    nbytes = kv + scales + int(Hkv * nblk.sum() * 4) + 2 * T * Hq * D * act + 8 * case.S + 4
+    seq = np.repeat(np.arange(case.S), qs.q_lens)
+    pos = L[seq] - qs.q_lens[seq] + (np.arange(T) - qs.query_start_loc[seq])
+    flops = int(4 * D * Hq * (pos + 1).sum())
+    return nbytes, kv, flops
+
+
+def bench_multi_query(args, torch, np, pa, synth):
+    """pa_prefill on a multi-token workload: the speculative verify of 4 tokens
+    per sequence on the Llama-shaped batch (HBM-bound: roofline against 8 TB/s)
+    or 512-token prefill chunks after 3584 cached tokens (a dense contraction:
+    roofline against the 2.5 PFLOP/s dense bf16 MFMA peak)."""
+    from gpu_helpers import fill_pool, host_to_dev, to_device
+    spec, ql = synth.MULTI_QUERY[args.multi_query]
+    case = synth.make_case(spec, 2)
+    qs = synth.make_queries(case, ql, 3)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    dc = to_device(case, dev)
+    k0, v0 = fill_pool(dc, dev)
+    pool_bytes = 2 * k0.numel() * k0.element_size()
+    R = max(2, math.ceil(args.rotate_gb * 1e9 / pool_bytes))
+    pools = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(R - 1)]
+    q = host_to_dev(qs.q, spec.act, dev)
+    qsl = torch.from_numpy(qs.query_start_loc).to(dev)
+    out = torch.empty_like(q)
+    mq = int(qs.q_lens.max())
+    nbytes, kv, flops = multi_query_counts(case, qs, np)
+
+    def step(i):
+        k, v = pools[i % R]
+        pa.prefill(out, q, k, v, dc.block_tables, dc.context_lens, qsl, float(case.scale), mq,
+                   case.max_context_len, dc.k_scale, dc.v_scale)
+
+    stream = torch.cuda.current_stream(dev)
+    i, t0 = 0, time.perf_counter()
+    while i < args.warmup or time.perf_counter() - t0 < WARMUP_S:
+        step(i)
+        i += 1
+        if i % 16 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for j in range(args.steps):
+        step(i + j)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    tfs = flops / (ms * 1e-3) / 1e12
+    verify = args.multi_query == "verify"
+    if verify:
+        roof = {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(tfs, 2), "peak": MFMA_BF16_PEAK_TFS,
+                "unit": "TFLOP/s", "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4)}
+    roof.update({"traffic": None, "kernel": "pa_prefill", "bytes_per_launch": nbytes,
+                 "flops_per_launch": flops})
+    line = {
+        "metric": ("speculative verify attention GB/s" if verify
+                   else "chunked-prefill attention TFLOP/s"),
+        "value": round(gbs if verify else tfs, 2), "unit": "GB/s" if verify else "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": spec.name + (" verify, 4 query tokens per sequence" if verify
+                                            else ", 512-token chunks"),
+                   "num_seqs": case.S, "query_tokens": qs.num_tokens,
+                   "num_heads": case.Hq, "num_kv_heads": case.Hkv, "head_dim": case.D,
+                   "block_size": case.B, "sum_context": int(case.context_lens.sum()),
+                   "pool_copies": R},
+        "gbs": round(gbs, 2), "tflops": round(tfs, 2), "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = multi_query_cpu_baseline(case, qs, args.cpu_budget, verify, np)
+    print(json.dumps(line), flush=True)
+
+
+def multi_query_cpu_baseline(case, qs, budget_s, verify, np):
+    """The fp64 oracle's ora_prefill over whole sequences (the first ones, then
+    repeated) for about `budget_s` seconds, in the bench line's unit."""
+    import oracle
+    import synth
+    k, v = oracle.fill_cache(case)
+    done_b = done_f = 0
+    reps, t0, s = 0, time.perf_counter(), 0
+    while True:
+        n = np.zeros(case.S, dtype=np.int64)
+        n[s] = qs.q_lens[s]
+        one = synth.Queries(query_start_loc=np.array([0] * (s + 1) + [int(n[s])] * (case.S - s),
+                                                     dtype=np.int32),
+                            q=qs.q[qs.query_start_loc[s]:qs.query_start_loc[s + 1]], q_lens=n)
+        oracle.prefill(one.q, k, v, case.block_tables, case.context_lens, one.query_start_loc,
+                       case.scale, case.k_scale, case.v_scale)
+        b, _, f = multi_query_counts(case, one, np)
+        done_b += b
+        done_f += f
+        reps += 1
+        s = (s + 1) % case.S
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    val = done_b / el / 1e9 if verify else done_f / el / 1e12
+    return {"value": round(val, 6), "unit": "GB/s" if verify else "TFLOP/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{reps} single-sequence calls of the oracle (sequences 0.., all their "
+                      f"query rows) in {el:.1f} s, fp64"}
+
+
 def copy_probe(torch, nbytes=1 << 30, reps=10):
     src = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
     dst = torch.empty_like(src)
@@ -191,6 +317,10 @@ def main():
     ap.add_argument("--copy-blocks", type=int, default=0, metavar="N",
                     help="instead of the decode step, time pa_copy_blocks copying N blocks of "
                          "the workload's pool (all kv heads, K and V) into free blocks")
+    ap.add_argument("--multi-query", choices=["verify", "prefill"], default=None,
+                    help="instead of the decode step, time pa_prefill: the speculative verify "
+                         "of 4 tokens per sequence on the Llama-shaped batch, or 512-token "
+                         "prefill chunks after 3584 cached tokens (8 sequences)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only time a device copy of 1 GiB (read 1 GiB + write 1 GiB); the "
                          "reference for calibrating rocprofv3 FETCH_SIZE / WRITE_SIZE")
@@ -212,6 +342,9 @@ def main():
     import synth
     from gpu_helpers import fill_pool, to_device
 
+    if args.multi_query:
+        bench_multi_query(args, torch, np, pa, synth)
+        return
     spec = synth.CONFIGS[args.config]
     if args.copy_blocks:
         bench_copy_blocks(args, spec, torch, np, pa, synth)

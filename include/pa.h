@@ -247,6 +247,49 @@ int pa_copy_blocks(void *k_cache, void *v_cache, float *k_scale, float *v_scale,
                    const int64_t *block_mapping, int num_pairs, int num_kv_heads, int head_dim,
                    int block_size, int64_t num_blocks, pa_dtype cache_dtype, void *stream);
 
+/*
+ * pa_prefill -- attention of several new query tokens per sequence over its
+ * paged context: the target model scoring K drafted tokens in one batched
+ * pass for speculative decoding (Continuous-Batching-LLM-Inference-Engine
+ * README, feature list; the verify pass has K + 1 query tokens) and the
+ * prefill chunks that continuous batches mix with decode tokens ("How
+ * brave30/mini-inference-engine works", summary; Model Compute: prefill
+ * attention). The new tokens' K/V are already in the cache (pa_write_kv_cache
+ * with one slot per new token), and context_lens counts them.
+ *
+ * Sequence s owns rows qsl[s] .. qsl[s+1]-1 of q and out (qsl =
+ * query_start_loc), n_s = qsl[s+1] - qsl[s] rows. Row qsl[s] + j is the new
+ * token at position p = L_s - n_s + j and, for each query head h (kv head
+ * h / (Hq / Hkv)), attends causally to the cached tokens 0 .. p:
+ *   out[r][h][:] = sum_{t <= p} exp(x_t - max x) v_t / sum_{t <= p} exp(x_t - max x),
+ *   x_t = scale * q[r][h] . k_t,
+ * with k_t, v_t gathered through block_tables and dequantised as in pa_decode.
+ * With n_s = 1 this is pa_decode of that sequence.
+ *
+ *   out             [num_query_tokens][num_heads][head_dim], q_dtype, 16-byte aligned
+ *   q               [num_query_tokens][num_heads][head_dim], q_dtype
+ *   k_cache, v_cache, block_tables, context_lens, k_scale, v_scale, scale:
+ *                   as in pa_decode (context_lens[s] >= n_s)
+ *   query_start_loc [num_seqs + 1] int32, device: 0 = qsl[0] <= qsl[1] <= ... <=
+ *                   qsl[num_seqs] = num_query_tokens
+ *   max_query_len   host-side bound on every n_s, at most max_context_len; it sizes
+ *                   the launch (rows of sequences with more are not written)
+ * Precision: Q K^T and P V run on bf16 MFMAs with fp32 accumulation; the
+ * softmax weights are rounded to bf16 for the P V product (the row sums use
+ * the fp32 weights).
+ * Supported instances (others return PA_ERR_UNSUPPORTED): q BF16; cache BF16 or
+ * I8; head_dim 128; block_size 16 or 32; group size Hq / Hkv in {1, 2, 4, 8, 16}.
+ * num_seqs and num_kv_heads <= 65535. num_query_tokens = 0 does nothing (q and out
+ * may then be NULL).
+ * PA_CHECK=1 also verifies query_start_loc and n_s <= min(max_query_len, L_s).
+ */
+int pa_prefill(void *out, const void *q, const void *k_cache, const void *v_cache,
+               const int32_t *block_tables, int max_blocks_per_seq, const int32_t *context_lens,
+               const int32_t *query_start_loc, const float *k_scale, const float *v_scale,
+               float scale, int num_seqs, int num_query_tokens, int max_query_len,
+               int num_heads, int num_kv_heads, int head_dim, int block_size, int64_t num_blocks,
+               int max_context_len, pa_dtype q_dtype, pa_dtype cache_dtype, void *stream);
+
 /* Workspace slots per (sequence, query head) that pa_decode_balanced needs:
  * ceil(ceil(max_context_len / 16) / (min_piece_tokens / 16)) + 1, or 0 when
  * max_context_len <= 0 or min_piece_tokens < 16. */

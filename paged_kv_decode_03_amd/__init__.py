@@ -52,6 +52,9 @@ _lib.pa_balanced_slots.argtypes = [_i, _i]
 _lib.pa_copy_blocks.restype = _i
 _lib.pa_copy_blocks.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i64, _i, _p]
 _lib.pa_decode_splitk_reduce.restype = _i
+_lib.pa_prefill.argtypes = [_p, _p, _p, _p, _p, _i, _p, _p, _p, _p, _f, _i, _i, _i, _i, _i, _i,
+                            _i, _i64, _i, _i, _i, _p]
+_lib.pa_prefill.restype = _i
 _lib.pa_decode_splitk_reduce.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p]
 
 PA_F32, PA_BF16, PA_I8 = 0, 1, 2
@@ -160,6 +163,33 @@ def decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_cont
                         int(partition_size), _ptr(tmp_out), _ptr(tmp_max), _ptr(tmp_sum),
                         _dt(q), _dt(k_cache), _stream(stream, dev))
     _check("pa_decode", rc)
+
+
+def prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_start_loc, scale,
+            max_query_len, max_context_len, k_scale=None, v_scale=None, stream=None):
+    """Causal attention of several new query tokens per sequence over the pool:
+    q and out [T, Hq, D]; rows query_start_loc[s] .. [s+1]-1 are the newest
+    tokens of sequence s (already written to the cache and counted by
+    context_lens)."""
+    dev = _dev(out, q, k_cache, v_cache, block_tables, context_lens, query_start_loc, k_scale,
+               v_scale)
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32 \
+            or query_start_loc.dtype != torch.int32:
+        raise TypeError("block_tables, context_lens and query_start_loc must be int32")
+    T, Hq, D = q.shape
+    NB, Hkv, B, D2 = k_cache.shape
+    S = context_lens.shape[0]
+    if D2 != D or v_cache.shape != k_cache.shape or block_tables.shape[0] != S \
+            or query_start_loc.shape != (S + 1,) or out.shape != q.shape:
+        raise ValueError("shape mismatch")
+    if out.dtype != q.dtype:
+        raise TypeError("out must have the dtype of q")
+    rc = _lib.pa_prefill(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                         block_tables.shape[1], _ptr(context_lens), _ptr(query_start_loc),
+                         _ptr(k_scale), _ptr(v_scale), float(scale), S, T, int(max_query_len),
+                         Hq, Hkv, D, B, NB, int(max_context_len), _dt(q), _dt(k_cache),
+                         _stream(stream, dev))
+    _check("pa_prefill", rc)
 
 
 def decode_splitk_reduce(out, tmp_out, tmp_max, tmp_sum, context_lens, max_context_len,

@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libpa.so")
 ARCH = "gfx950"
 SOURCES = ["pa_api.cpp", "pa_write.hip", "pa_decode_valu.hip", "pa_decode_mfma.hip",
-           "pa_reduce.hip", "pa_copy.hip"]
+           "pa_reduce.hip", "pa_copy.hip", "pa_prefill.hip"]
 CXXFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
     "-fno-fast-math", "-fhip-fp32-correctly-rounded-divide-sqrt",

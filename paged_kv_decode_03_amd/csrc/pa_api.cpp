@@ -127,6 +127,23 @@ int check_copy_mapping(const int64_t* block_mapping, int num_pairs, int64_t num_
     return PA_OK;
 }
 
+// PA_CHECK=1, several query tokens per sequence: query_start_loc runs from 0
+// to num_query_tokens without decreasing, and every count n_s is at most
+// max_query_len and at most L_s.
+int check_query_starts(const int32_t* query_start_loc, const int32_t* context_lens,
+                       int num_seqs, int num_query_tokens, int max_query_len, hipStream_t st) {
+    std::vector<int32_t> qsl, lens;
+    if (!fetch(qsl, query_start_loc, (int64_t)num_seqs + 1, st) ||
+        !fetch(lens, context_lens, num_seqs, st))
+        return PA_ERR_LAUNCH;
+    if (qsl[0] != 0 || qsl[num_seqs] != num_query_tokens) return PA_ERR_INDEX;
+    for (int s = 0; s < num_seqs; ++s) {
+        const int n = qsl[s + 1] - qsl[s];
+        if (n < 0 || n > max_query_len || n > lens[s]) return PA_ERR_INDEX;
+    }
+    return PA_OK;
+}
+
 }  // namespace
 
 namespace pa {
@@ -270,6 +287,42 @@ int pa_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale,
                    cache_dtype == PA_I8 ? v_scale : nullptr, block_mapping, num_pairs,
                    num_kv_heads, (int64_t)num_kv_heads * block_size * head_dim * elt};
     return launch_status(pa::launch_copy_blocks(a, st));
+}
+
+int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
+               const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
+               const int32_t* query_start_loc, const float* k_scale, const float* v_scale,
+               float scale, int num_seqs, int num_query_tokens, int max_query_len,
+               int num_heads, int num_kv_heads, int head_dim, int block_size, int64_t num_blocks,
+               int max_context_len, pa_dtype q_dtype, pa_dtype cache_dtype, void* stream) {
+    // with no query rows, q and out are never read and may be NULL
+    const void* qc = num_query_tokens == 0 && !q ? k_cache : q;
+    int rc = check_decode(qc, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                          k_scale, v_scale, num_seqs, num_heads, num_kv_heads, head_dim,
+                          block_size, num_blocks, max_context_len, 0, q_dtype, cache_dtype);
+    if (rc) return rc;
+    if (num_query_tokens < 0 || max_query_len < 0 || max_query_len > max_context_len ||
+        num_seqs > 65535 || num_kv_heads > 65535 ||
+        (int64_t)max_query_len * (num_heads / num_kv_heads) > 0x7fffffff)
+        return PA_ERR_SHAPE;
+    if (!query_start_loc) return PA_ERR_NULL;
+    if (num_query_tokens > 0 && (!out || !aligned16(out))) return out ? PA_ERR_ALIGN : PA_ERR_NULL;
+    pa::PrefillArgs a{out, q, k_cache, v_cache, block_tables, context_lens, query_start_loc,
+                      k_scale, v_scale, scale, num_seqs, num_heads, num_kv_heads, head_dim,
+                      block_size, max_blocks_per_seq, max_query_len, (pa::Dtype)q_dtype,
+                      (pa::Dtype)cache_dtype};
+    if (!pa::prefill_supports(a)) return PA_ERR_UNSUPPORTED;
+    if (num_seqs == 0 || num_query_tokens == 0) return PA_OK;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (check_enabled()) {
+        rc = check_indices(block_tables, max_blocks_per_seq, context_lens, num_seqs, block_size,
+                           num_blocks, max_context_len, st);
+        if (rc) return rc;
+        rc = check_query_starts(query_start_loc, context_lens, num_seqs, num_query_tokens,
+                                max_query_len, st);
+        if (rc) return rc;
+    }
+    return launch_status(pa::launch_prefill(a, st));
 }
 
 int pa_balanced_slots(int max_context_len, int min_piece_tokens) {

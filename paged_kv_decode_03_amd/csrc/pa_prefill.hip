@@ -1,0 +1,370 @@
+// Several new query tokens per sequence over the paged KV cache: the target
+// model scoring K drafted tokens in one pass (speculative decoding,
+// Continuous-Batching-LLM-Inference-Engine README, feature list) and the
+// prefill chunks that continuous batches mix with decode tokens ("How
+// brave30/mini-inference-engine works", summary; Model Compute: prefill
+// attention). The n new tokens of a sequence of L cached tokens are its last
+// n; new token j sits at position L - n + j and attends to tokens 0 .. L-n+j.
+//
+// With several query rows per kv head the product is a real contraction, so it
+// runs on 16x16x32 bf16 MFMAs:
+//   S^T = K Q^T   A = K tile (16 tokens x 32 dims), B = Q^T (32 dims x 16 rows)
+//   O^T += V^T P^T  A = V^T (16 dims x 32 tokens), B = P^T (32 tokens x 16 rows)
+// A query row is a (new token, head of the group) pair, so the G heads that
+// share a kv head share every K/V load. Computing S^T rather than S leaves
+// each lane with one query row (lane % 16) and eight tokens, so the row max
+// and sum need only the exchange between the four lanes of that row, and the
+// S^T registers are already the P^T operand of the next MFMA: the k slots
+// 8q..8q+7 of lane group q = lane / 16 stand for tokens 4q..4q+3 and
+// 16+4q..16+4q+3 of the 32-token tile, and the V^T operand is read with the
+// same pairing.
+//
+// Lane layout of v_mfma_f32_16x16x32_bf16: lane l holds A[l % 16][8q .. 8q+7],
+// B[8q .. 8q+7][l % 16] and D[4q .. 4q+3][l % 16], q = l / 16.
+// ds_read_b64_tr_b16 (LDS read with a transpose inside each 16-lane group):
+// lane i of a group receives, as element k, element i % 4 of the 8 bytes that
+// lane 4k + i / 4 of its group addressed. So V stays row-major in LDS, like
+// K, and the V^T operand of lane (i, q) -- V[4q + k][d0 + i], k = 0..3 -- is
+// one such read in which lane j of group q addresses row 4q + j / 4, columns
+// d0 + 4 (j % 4) .. +3 (and a second one 16 rows further down).
+//
+// Workgroup: 4 waves for one (sequence, kv head, tile of query rows), as NR
+// row groups x NT = 4 / NR token groups. A row group owns MB blocks of 16
+// rows; a token group streams every NT-th 32-token KV tile through its own
+// LDS buffer (K and V row-major), filled by the NR waves that consume it. Token groups merge their
+// softmax states through LDS at the end. Few rows (the verify pass): NR = 1,
+// and four waves split the context; many rows (prefill chunks): NR = 4, and
+// each KV tile read from HBM feeds 128 rows.
+#include "pa_device.hpp"
+#include "pa_kernels.hpp"
+
+namespace pa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int PD = 128;               // head_dim
+constexpr int TK = 32;                // tokens per KV tile
+constexpr int KSTR = PD * 2 + 16;     // K and V tile row stride in LDS (bytes), padded
+constexpr int KBYTES = TK * KSTR;
+constexpr int TGBYTES = 2 * KBYTES;   // a token group's K and V tiles
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+typedef short i16x4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 ds_read_tr16(const char* p) {
+    const i16x4v r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4v*)(p));
+    return __builtin_bit_cast(uint2, r);
+}
+
+// Sixteen int8 codes -> sixteen bf16 (exact: |code| < 2^8).
+__device__ __forceinline__ void i8_to_bf16(uint4 v, uint4& lo, uint4& hi) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t o[8];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        o[2 * k] = pack_bf16_trunc(i8_at(w[k], 0), i8_at(w[k], 1));
+        o[2 * k + 1] = pack_bf16_trunc(i8_at(w[k], 2), i8_at(w[k], 3));
+    }
+    lo = make_uint4(o[0], o[1], o[2], o[3]);
+    hi = make_uint4(o[4], o[5], o[6], o[7]);
+}
+
+template <int NR, int MB, bool I8>
+__global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
+    constexpr int NT = 4 / NR;
+    constexpr int RT = NR * MB * 16;                  // query rows per workgroup
+    constexpr int TPT = NR * 64;                      // threads filling one token group's tile
+    constexpr int EPP = I8 ? 16 : 8;                  // cache elements per 16-byte piece
+    constexpr int PPR = PD / EPP;                     // pieces per token row
+    constexpr int NLD = TK * PPR / TPT;               // pieces per thread per tile (K, and V)
+    static_assert(TK * PPR % TPT == 0, "tile split");
+    constexpr int ELT = I8 ? 1 : 2;
+    __shared__ __attribute__((aligned(16))) char lds[NT * TGBYTES];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int rg = wave % NR, tg = wave / NR;
+    const int col = lane & 15, quad = lane >> 4;
+    const int s = blockIdx.z, g = blockIdx.y;
+    const int Hq = a.num_heads, Hkv = a.num_kv_heads, B = a.block_size;
+    const int G = Hq / Hkv;
+    const int q0 = ld_const(a.query_start_loc, s);
+    const int n = ld_const(a.query_start_loc, s + 1) - q0;
+    const int tiles = (n * G + RT - 1) / RT;
+    if ((int)blockIdx.x >= tiles) return;
+    const int tile = tiles - 1 - (int)blockIdx.x;    // the tiles with the longest context first
+    const int TQ = RT / G;                            // query tokens per tile (G divides 16)
+    const int tok0 = tile * TQ;
+    const int L = ld_const(a.context_lens, s);
+    const int p_first = L - n + tok0;                 // position of the tile's first new token
+    const int limit = p_first + min(TQ, n - tok0);    // the tile reads tokens [0, limit)
+    const int nkt = limit > 0 ? (limit + TK - 1) / TK : 0;
+    const int nit = (nkt + NT - 1) / NT;
+    const float sl2 = a.scale * kLog2e;
+    const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+
+    // query rows of this lane: Q^T operands and positions (-1: a padding row)
+    int rpos[MB];
+    bf16x8 qop[MB][4];
+    int64_t orow[MB];                                 // element offset of the row in q / out
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        const int r = (rg * MB + mb) * 16 + col;
+        const int j = r / G, h = r - j * G;
+        const bool valid = tok0 + j < n;
+        rpos[mb] = valid ? p_first + j : -1;
+        orow[mb] = ((int64_t)(q0 + tok0 + j) * Hq + g * G + h) * PD;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (valid)
+                v = ld16(reinterpret_cast<const uint16_t*>(a.q) + orow[mb] + 32 * ks + 8 * quad);
+            qop[mb][ks] = as_bf16x8(v);
+        }
+    }
+
+    float m[MB], l[MB];
+    f32x4 o[MB][8];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        m[mb] = -__builtin_huge_valf();
+        l[mb] = 0.0f;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) o[mb][dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+
+    // this thread's pieces of a tile: piece p = ti + k TPT is token p / PPR,
+    // elements (p % PPR) * EPP ..
+    const int ti = rg * 64 + lane;
+    uint4 kr[NLD], vr[NLD];
+    auto load_tile = [&](int kt) {
+        // the tile's (at most two) block ids as scalar loads: a vector load of
+        // a block id would have to wait for every K/V load issued before it
+        int64_t blk[2] = {0, 0};
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+            if (kt * TK + 16 * hf < limit) blk[hf] = ld_uniform(bt, (kt * TK + 16 * hf) / B);
+#pragma unroll
+        for (int k = 0; k < NLD; ++k) {
+            const int p = ti + k * TPT, t = p / PPR, e = (p % PPR) * EPP;
+            const int T = kt * TK + t;
+            kr[k] = vr[k] = make_uint4(0, 0, 0, 0);
+            if (T < limit) {
+                const int64_t b = t < 16 ? blk[0] : blk[1];
+                const int64_t off = (((b * Hkv + g) * B + T % B) * PD + e) * ELT;
+                kr[k] = ld16(reinterpret_cast<const char*>(a.k_cache) + off);
+                vr[k] = ld16(reinterpret_cast<const char*>(a.v_cache) + off);
+            }
+        }
+    };
+    char* kl = lds + tg * TGBYTES;
+    char* vl = kl + KBYTES;
+    // this lane's address in the transposed V reads (see the file comment)
+    const int vtr = (4 * quad + col / 4) * KSTR + 8 * (col % 4);
+    auto store_tile = [&]() {
+#pragma unroll
+        for (int k = 0; k < NLD; ++k) {
+            const int p = ti + k * TPT, t = p / PPR, e = (p % PPR) * EPP;
+            uint4 kv[2], vv[2];
+            if (I8) {
+                i8_to_bf16(kr[k], kv[0], kv[1]);
+                i8_to_bf16(vr[k], vv[0], vv[1]);
+            } else {
+                kv[0] = kr[k];
+                vv[0] = vr[k];
+            }
+#pragma unroll
+            for (int hlf = 0; hlf < EPP / 8; ++hlf) {
+                *reinterpret_cast<uint4*>(kl + t * KSTR + (e + 8 * hlf) * 2) = kv[hlf];
+                *reinterpret_cast<uint4*>(vl + t * KSTR + (e + 8 * hlf) * 2) = vv[hlf];
+            }
+        }
+    };
+
+    auto compute = [&](int kt) {
+        // int8: per-(block, kv head) scales of the two 16-token halves
+        float ksc[2] = {1.0f, 1.0f}, vsc[2] = {1.0f, 1.0f};
+        if (I8) {
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+                const int T = kt * TK + tt * 16;
+                if (T < limit) {
+                    const int64_t b = ld_uniform(bt, T / B);
+                    ksc[tt] = ld_uniform(a.k_scale, b * Hkv + g);
+                    vsc[tt] = ld_uniform(a.v_scale, b * Hkv + g);
+                }
+            }
+        }
+        bf16x8 kop[2][4];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                kop[tt][ks] = as_bf16x8(*reinterpret_cast<const uint4*>(
+                    kl + (tt * 16 + col) * KSTR + (32 * ks + 8 * quad) * 2));
+        bf16x8 vop[8];
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+            const uint2 x0 = ds_read_tr16(vl + vtr + 32 * dt);
+            const uint2 x1 = ds_read_tr16(vl + vtr + 16 * KSTR + 32 * dt);
+            vop[dt] = as_bf16x8(make_uint4(x0.x, x0.y, x1.x, x1.y));
+        }
+        const bool edge = kt * TK + TK - 1 > p_first;   // some row of the tile masks some token
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            float x[2][4];
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+                f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) acc = mfma16x16x32(kop[tt][ks], qop[mb][ks], acc);
+                const float f = I8 ? sl2 * ksc[tt] : sl2;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    x[tt][i] = acc[i] * f;
+                    if (edge && kt * TK + tt * 16 + 4 * quad + i > rpos[mb])
+                        x[tt][i] = -__builtin_huge_valf();
+                }
+            }
+            float mx = x[0][0];
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) mx = fmaxf(mx, x[tt][i]);
+            mx = fmaxf(mx, lane_xor16(mx));
+            mx = fmaxf(mx, lane_xor32(mx));
+            const float mn = fmaxf(m[mb], mx);
+            const float mu = mn == -__builtin_huge_valf() ? 0.0f : mn;
+            const float alpha = __builtin_amdgcn_exp2f(m[mb] - mu);
+            m[mb] = mn;
+            float sum = 0.0f;
+            bf16x8 pop;
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float pr = __builtin_amdgcn_exp2f(x[tt][i] - mu);
+                    sum += pr;
+                    pop[4 * tt + i] = (__bf16)(I8 ? pr * vsc[tt] : pr);
+                }
+            l[mb] = l[mb] * alpha + sum;
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o[mb][dt][i] *= alpha;
+                o[mb][dt] = mfma16x16x32(vop[dt], pop, o[mb][dt]);
+            }
+        }
+    };
+
+    if (nit > 0) load_tile(tg);
+    for (int it = 0; it < nit; ++it) {
+        const int kt = it * NT + tg;
+        __syncthreads();                              // the previous tile's reads are done
+        store_tile();
+        __syncthreads();
+        if (it + 1 < nit) load_tile(kt + NT);         // in flight while this tile is computed
+        if (kt < nkt) compute(kt);
+    }
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        l[mb] += lane_xor16(l[mb]);
+        l[mb] += lane_xor32(l[mb]);
+    }
+
+    if (NT > 1) {
+        // token groups 1 .. NT-1 hand their states to token group 0 of their row group
+        __syncthreads();
+        float* st = reinterpret_cast<float*>(lds);
+        constexpr int SLOT = MB * (8 * 64 * 4 + 2 * 64);   // floats per handed-over wave state
+        static_assert((NT - 1) * NR * SLOT * 4 <= NT * TGBYTES, "merge states fit the tiles' LDS");
+        if (tg > 0) {
+            float* w = st + ((tg - 1) * NR + rg) * SLOT;
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+                for (int dt = 0; dt < 8; ++dt)
+                    *reinterpret_cast<f32x4*>(w + ((mb * 8 + dt) * 64 + lane) * 4) = o[mb][dt];
+                w[MB * 8 * 64 * 4 + mb * 64 + lane] = m[mb];
+                w[MB * 8 * 64 * 4 + (MB + mb) * 64 + lane] = l[mb];
+            }
+        }
+        __syncthreads();
+        if (tg > 0) return;
+#pragma unroll
+        for (int u = 1; u < NT; ++u) {
+            const float* w = st + ((u - 1) * NR + rg) * SLOT;
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                const float m2 = w[MB * 8 * 64 * 4 + mb * 64 + lane];
+                const float l2 = w[MB * 8 * 64 * 4 + (MB + mb) * 64 + lane];
+                const float M = fmaxf(m[mb], m2);
+                const float a1 = m[mb] == -__builtin_huge_valf() ? 0.0f : __builtin_amdgcn_exp2f(m[mb] - M);
+                const float a2 = m2 == -__builtin_huge_valf() ? 0.0f : __builtin_amdgcn_exp2f(m2 - M);
+                m[mb] = M;
+                l[mb] = l[mb] * a1 + l2 * a2;
+#pragma unroll
+                for (int dt = 0; dt < 8; ++dt) {
+                    const f32x4 v = *reinterpret_cast<const f32x4*>(w + ((mb * 8 + dt) * 64 + lane) * 4);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) o[mb][dt][i] = o[mb][dt][i] * a1 + v[i] * a2;
+                }
+            }
+        }
+    }
+
+    // out[row][d], d = 16 dt + 4 quad + i: four bf16 per store
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        if (rpos[mb] < 0) continue;
+        const float inv = 1.0f / l[mb];
+        uint16_t* dst = reinterpret_cast<uint16_t*>(a.out) + orow[mb] + 4 * quad;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+            const uint32_t w0 = f32_to_bf16(o[mb][dt][0] * inv) |
+                                ((uint32_t)f32_to_bf16(o[mb][dt][1] * inv) << 16);
+            const uint32_t w1 = f32_to_bf16(o[mb][dt][2] * inv) |
+                                ((uint32_t)f32_to_bf16(o[mb][dt][3] * inv) << 16);
+            *reinterpret_cast<uint2*>(dst + 16 * dt) = make_uint2(w0, w1);
+        }
+    }
+}
+
+template <int NR, int MB>
+hipError_t launch_shape(const PrefillArgs& a, int tiles, hipStream_t st) {
+    const dim3 grid(tiles, a.num_kv_heads, a.num_seqs);
+    if (a.cache == Dtype::I8)
+        hipLaunchKernelGGL((prefill_kernel<NR, MB, true>), grid, dim3(256), 0, st, a);
+    else
+        hipLaunchKernelGGL((prefill_kernel<NR, MB, false>), grid, dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool prefill_supports(const PrefillArgs& a) {
+    const int G = a.num_kv_heads > 0 ? a.num_heads / a.num_kv_heads : 0;
+    return a.head_dim == PD && (a.block_size == 16 || a.block_size == 32) &&
+           a.q_dtype == Dtype::BF16 && (a.cache == Dtype::BF16 || a.cache == Dtype::I8) &&
+           G >= 1 && G <= 16 && 16 % G == 0;
+}
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
+    if (!prefill_supports(a)) return hipErrorNotSupported;
+    if (a.num_seqs == 0 || a.max_query_len == 0) return hipSuccess;
+    const int64_t rows = (int64_t)a.max_query_len * (a.num_heads / a.num_kv_heads);
+    if (rows <= 16) return launch_shape<1, 1>(a, 1, st);
+    if (rows <= 32) return launch_shape<1, 2>(a, 1, st);
+    if (rows <= 64) return launch_shape<2, 2>(a, 1, st);
+    return launch_shape<4, 2>(a, (int)((rows + 127) / 128), st);
+}
+
+}  // namespace pa

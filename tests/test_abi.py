@@ -169,3 +169,31 @@ def copy(**kw):
 ])
 def test_copy_blocks_validation(kw, code):
     assert copy(**kw) == code
+
+
+def prefill(**kw):
+    args = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, MB=8, lens=FAKE, qsl=FAKE, ks=None,
+                vs=None, scale=0.125, S=4, T=16, maxq=4, Hq=32, Hkv=8, D=128, B=16, NB=64,
+                maxL=128, qdt=BF16, cdt=BF16)
+    args.update(kw)
+    a = args
+    return pa.lib().pa_prefill(
+        a["out"], a["q"], a["k"], a["v"], a["bt"], a["MB"], a["lens"], a["qsl"], a["ks"], a["vs"],
+        a["scale"], a["S"], a["T"], a["maxq"], a["Hq"], a["Hkv"], a["D"], a["B"], a["NB"],
+        a["maxL"], a["qdt"], a["cdt"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(qsl=None), NULL), (dict(out=None), NULL), (dict(q=None), NULL),
+    (dict(cdt=I8), NULL),                         # int8 pool without scales
+    (dict(out=MIS), ALIGN), (dict(q=MIS), ALIGN),
+    (dict(T=-1), SHAPE), (dict(maxq=-1), SHAPE), (dict(maxq=129), SHAPE),
+    (dict(S=70000), SHAPE), (dict(Hq=30), SHAPE),
+    (dict(qdt=F32, cdt=F32), UNSUP), (dict(D=64), UNSUP), (dict(B=8, MB=16), UNSUP),
+    (dict(Hq=24), UNSUP),                   # group size 3
+    (dict(Hq=256, Hkv=8), UNSUP),           # group size 32
+    (dict(qdt=BF16, cdt=F32), DTYPE),
+    (dict(T=0), OK), (dict(S=0, T=0), OK), (dict(T=0, out=None, q=None), OK),
+])
+def test_prefill_validation(kw, code):
+    assert prefill(**kw) == code

@@ -1,0 +1,146 @@
+"""pa_prefill (several new query tokens per sequence: speculative verify and
+chunked prefill) against the fp64 oracle, through the C ABI.
+
+Small batches are compared element by element with ``oracle.prefill``. The
+full-size workloads compare sampled rows with one-token decode over the
+context cut after the row's position, which the oracle's own pins tie to
+``oracle.prefill`` row by row. Tolerances are those of the decode path
+(bf16 2e-2, int8 3e-2 max abs)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_helpers import as_f64, fill_pool, host_to_dev, run_decode, to_device, tol
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import paged_kv_decode_03_amd as pa
+
+S_ = synth.Spec
+CASES = {
+    # name: (spec, query counts)
+    "verify_g4": (synth.CONFIGS[2].replace(num_seqs=12, lens=("uniform", 1, 1100), max_len=1100),
+                  ("const", 4)),
+    "verify_g4_i8": (synth.CONFIGS[4].replace(num_seqs=10, lens=("uniform", 1, 1300),
+                                              max_len=1300), ("const", 4)),
+    "verify_g8_b32": (S_("G=8 B=32", 8, ("uniform", 1, 900), 32, 4, 128, 32, act="bf16",
+                         cache="bf16", max_len=900), ("uniform", 1, 8)),
+    "g2_i8_b32": (S_("G=2 int8 B=32", 6, ("uniform", 1, 700), 8, 4, 128, 32, act="bf16",
+                     cache="i8", max_len=700), ("uniform", 0, 20)),
+    "g16": (S_("G=16", 5, ("uniform", 1, 600), 16, 1, 128, 16, act="bf16", cache="bf16",
+               max_len=600), ("uniform", 1, 3)),
+    "mixed_g4": (S_("G=4 mixed counts", 9, ("uniform", 1, 800), 16, 4, 128, 16, act="bf16",
+                    cache="bf16", max_len=800), ("uniform", 0, 40)),
+    "chunk_g4": (S_("G=4 prefill chunk", 2, ("const", 1500), 8, 2, 128, 16, act="bf16",
+                    cache="bf16", max_len=1500), ("const", 300)),
+    "chunk_i8_g8": (S_("G=8 int8 prefill chunk", 2, ("uniform", 600, 1000), 16, 2, 128, 32,
+                       act="bf16", cache="i8", max_len=1000), ("const", 100)),
+    "whole_mha": (S_("MHA whole-context prefill", 3, ("uniform", 1, 200), 4, 4, 128, 16,
+                     act="bf16", cache="bf16", max_len=200), "whole"),
+    "cow_g8": (synth.CONFIGS[5].replace(num_seqs=16, lens=("lognormal", 200, 1.0, 1, 1500),
+                                        max_len=1500, prefix_groups=2, prefix_tokens=256),
+               ("uniform", 1, 5)),
+}
+
+
+def prepare(name, seed=11):
+    spec, ql = CASES[name]
+    case = synth.make_case(spec, seed)
+    if ql == "whole":
+        ql = case.context_lens.astype(np.int64)
+    qs = synth.make_queries(case, ql, seed + 1)
+    dc = to_device(case)
+    fill_pool(dc)
+    return case, qs, dc
+
+
+def run_prefill(case, qs, dc, max_query_len=None):
+    q = host_to_dev(qs.q, case.spec.act, "cuda")
+    qsl = torch.from_numpy(qs.query_start_loc).cuda()
+    out = torch.full_like(q, float("nan"))
+    mq = int(qs.q_lens.max()) if max_query_len is None else max_query_len
+    pa.prefill(out, q, dc.k_cache, dc.v_cache, dc.block_tables, dc.context_lens, qsl,
+               float(case.scale), mq, case.max_context_len, dc.k_scale, dc.v_scale)
+    torch.cuda.synchronize()
+    return as_f64(out)
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_prefill_parity(name):
+    case, qs, dc = prepare(name)
+    print(f"[prefill] {name}: {qs.num_tokens} query rows, max {int(qs.q_lens.max())} per seq",
+          flush=True)
+    got = run_prefill(case, qs, dc)
+    ok, ov = oracle.fill_cache(case)
+    ref = oracle.prefill(qs.q, ok, ov, case.block_tables, case.context_lens, qs.query_start_loc,
+                         case.scale, case.k_scale, case.v_scale)
+    assert np.isfinite(got).all()
+    err = np.abs(got - ref).max()
+    print(f"[prefill] {name}: max |gpu - oracle| = {err:.3e}", flush=True)
+    assert err <= tol(case), f"{name}: max |gpu - oracle| = {err}"
+
+
+def test_prefill_one_token_matches_decode():
+    """n_s = 1 is decode: the same rows as the decode kernels, to tolerance."""
+    spec = synth.CONFIGS[2].replace(num_seqs=8, lens=("uniform", 1, 700), max_len=700)
+    case = synth.make_case(spec, 5)
+    dc = to_device(case)
+    fill_pool(dc)
+    qs = synth.Queries(query_start_loc=np.arange(case.S + 1, dtype=np.int32), q=case.q,
+                       q_lens=np.ones(case.S, dtype=np.int64))
+    got = run_prefill(case, qs, dc)
+    dec = as_f64(run_decode(dc, 0))
+    assert np.abs(got - dec).max() <= tol(case)
+
+
+def test_prefill_loose_max_query_len():
+    """A max_query_len above every count launches more row tiles; the extra
+    tiles find no rows and the result is the same."""
+    case, qs, dc = prepare("mixed_g4")
+    a = run_prefill(case, qs, dc)
+    b = run_prefill(case, qs, dc, max_query_len=case.max_context_len)
+    assert np.array_equal(a, b)
+
+
+def test_prefill_no_rows():
+    """Sequences with no new tokens, and a batch with none at all."""
+    case, qs, dc = prepare("verify_g4")
+    n = qs.q_lens.copy()
+    n[::2] = 0
+    qz = synth.make_queries(case, n, 3)
+    got = run_prefill(case, qz, dc)
+    ok, ov = oracle.fill_cache(case)
+    ref = oracle.prefill(qz.q, ok, ov, case.block_tables, case.context_lens,
+                         qz.query_start_loc, case.scale)
+    assert np.abs(got - ref).max() <= tol(case)
+    empty = synth.make_queries(case, np.zeros(case.S, dtype=np.int64), 3)
+    assert run_prefill(case, empty, dc, max_query_len=0).size == 0
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", ["verify", "prefill"])
+def test_prefill_full_size_sampled(name):
+    spec, ql = synth.MULTI_QUERY[name]
+    print(f"[prefill full] {name}: generating", flush=True)
+    case = synth.make_case(spec, 2)
+    qs = synth.make_queries(case, ql, 3)
+    dc = to_device(case)
+    fill_pool(dc)
+    print(f"[prefill full] {name}: gpu, {qs.num_tokens} rows", flush=True)
+    got = run_prefill(case, qs, dc)
+    assert np.isfinite(got).all()
+    rng = np.random.default_rng(4)
+    rows = np.unique(np.concatenate([rng.choice(qs.num_tokens, size=24, replace=False),
+                                     qs.query_start_loc[1:] - 1, [0]]))
+    seq = np.searchsorted(qs.query_start_loc, rows, side="right") - 1
+    pos = case.context_lens[seq] - qs.q_lens[seq] + (rows - qs.query_start_loc[seq])
+    ok, ov = oracle.fill_cache(case)
+    print(f"[prefill full] {name}: oracle on {len(rows)} rows", flush=True)
+    ref = oracle.decode(qs.q[rows], ok, ov, case.block_tables[seq], (pos + 1).astype(np.int32),
+                        case.scale, case.k_scale, case.v_scale)
+    err = np.abs(got[rows] - ref).max()
+    print(f"[prefill full] {name}: max err {err:.3e}", flush=True)
+    assert err <= tol(case)
