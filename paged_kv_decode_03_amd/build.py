@@ -38,9 +38,16 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libpa.so)")
 
 
+# Per-source flags. pa_prefill.hip: MFMA accumulators in VGPRs (its output
+# accumulators would otherwise live in AGPRs and be copied to VGPRs and back on
+# every KV tile around the softmax rescale).
+SOURCE_FLAGS = {"pa_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def _compile(src: str, obj: str) -> None:
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
-    cmd = [hipcc(), *CXXFLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *CXXFLAGS, *SOURCE_FLAGS.get(src, []), *lang, "-c",
+           os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile of {src} failed:\n{r.stderr}")

@@ -83,6 +83,7 @@ struct PrefillArgs {
     int num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq;
     int max_query_len;               // bound on every qsl[s+1] - qsl[s]
     Dtype q_dtype, cache;
+    int row_tiles = 0;               // set by the launcher: row tiles per (sequence, kv head)
 };
 
 enum class Schedule { Partitions, Balanced };

@@ -49,6 +49,10 @@ constexpr int KSTR = PD * 2 + 16;     // K and V tile row stride in LDS (bytes),
 constexpr int KBYTES = TK * KSTR;
 constexpr int TGBYTES = 2 * KBYTES;   // a token group's K and V tiles
 constexpr float kLog2e = 1.4426950408889634f;
+// The running output and sum are rescaled to a row's new max only once the
+// max has grown by more than this (log2 units) over the max they refer to;
+// until then the weights exp2(x - m) stay below 2^kLazy.
+constexpr float kLazy = 8.0f;
 
 __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -78,7 +82,7 @@ __device__ __forceinline__ void i8_to_bf16(uint4 v, uint4& lo, uint4& hi) {
     hi = make_uint4(o[4], o[5], o[6], o[7]);
 }
 
-template <int NR, int MB, bool I8>
+template <int NR, int MB, bool I8, int BS>
 __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     constexpr int NT = 4 / NR;
     constexpr int RT = NR * MB * 16;                  // query rows per workgroup
@@ -93,14 +97,22 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int rg = wave % NR, tg = wave / NR;
     const int col = lane & 15, quad = lane >> 4;
-    const int s = blockIdx.z, g = blockIdx.y;
-    const int Hq = a.num_heads, Hkv = a.num_kv_heads, B = a.block_size;
+    const int Hq = a.num_heads, Hkv = a.num_kv_heads;
+    constexpr int B = BS;                             // block size (16 or 32)
+    // workgroup -> (row tile, kv head, sequence), XCD-contiguous: consecutive
+    // workgroups go to the 8 XCDs in turn, so the logical index runs through
+    // each XCD's share first, and the row tiles of one (sequence, kv head) --
+    // which read the same KV -- share one XCD's L2
+    const int W = gridDim.x, w0 = blockIdx.x;
+    const int w = (W % 8) ? w0 : (w0 % 8) * (W / 8) + w0 / 8;
+    const int rt = w % a.row_tiles, sg = w / a.row_tiles;
+    const int g = sg % Hkv, s = sg / Hkv;
     const int G = Hq / Hkv;
     const int q0 = ld_const(a.query_start_loc, s);
     const int n = ld_const(a.query_start_loc, s + 1) - q0;
     const int tiles = (n * G + RT - 1) / RT;
-    if ((int)blockIdx.x >= tiles) return;
-    const int tile = tiles - 1 - (int)blockIdx.x;    // the tiles with the longest context first
+    if (rt >= tiles) return;
+    const int tile = tiles - 1 - rt;                  // the tiles with the longest context first
     const int TQ = RT / G;                            // query tokens per tile (G divides 16)
     const int tok0 = tile * TQ;
     const int L = ld_const(a.context_lens, s);
@@ -144,32 +156,45 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     // this thread's pieces of a tile: piece p = ti + k TPT is token p / PPR,
     // elements (p % PPR) * EPP ..
     const int ti = rg * 64 + lane;
-    uint4 kr[NLD], vr[NLD];
-    auto load_tile = [&](int kt) {
+    // tiles in flight in registers: PF of them (buffers 0 and 1 alternate).
+    // Few rows per wave: one, so that two waves fit on a SIMD.
+    constexpr int PF = 1;
+    uint4 kr0[NLD], vr0[NLD], kr1[PF == 2 ? NLD : 1], vr1[PF == 2 ? NLD : 1];
+    // A piece's address: the (block, kv head) tile's base, a scalar, plus
+    // the lane's offset inside the tile (a tile starts on a block boundary,
+    // so token t of the tile is row t % B of its block).
+    constexpr int64_t TILE_BYTES = (int64_t)B * PD * ELT;     // one (block, kv head) tile
+    const int64_t blk_stride = (int64_t)Hkv * TILE_BYTES, head_off = (int64_t)g * TILE_BYTES;
+    // tokens of one load instruction: all in the same 16-token half?
+    constexpr int TOK_PER_LD = TPT / PPR;
+    constexpr bool HALF_UNIFORM = TOK_PER_LD <= 16;
+    auto load_tile = [&](int kt, uint4 (&kr)[NLD], uint4 (&vr)[NLD]) {
         // the tile's (at most two) block ids as scalar loads: a vector load of
         // a block id would have to wait for every K/V load issued before it
-        int64_t blk[2] = {0, 0};
+        int64_t base[2] = {0, 0};
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf)
-            if (kt * TK + 16 * hf < limit) blk[hf] = ld_uniform(bt, (kt * TK + 16 * hf) / B);
+            if (kt * TK + 16 * hf < limit)
+                base[hf] = (int64_t)ld_uniform(bt, (kt * TK + 16 * hf) / B) * blk_stride + head_off;
 #pragma unroll
         for (int k = 0; k < NLD; ++k) {
             const int p = ti + k * TPT, t = p / PPR, e = (p % PPR) * EPP;
-            const int T = kt * TK + t;
-            kr[k] = vr[k] = make_uint4(0, 0, 0, 0);
-            if (T < limit) {
-                const int64_t b = t < 16 ? blk[0] : blk[1];
-                const int64_t off = (((b * Hkv + g) * B + T % B) * PD + e) * ELT;
-                kr[k] = ld16(reinterpret_cast<const char*>(a.k_cache) + off);
-                vr[k] = ld16(reinterpret_cast<const char*>(a.v_cache) + off);
-            }
+            // a token at or past `limit` reads the tile's first token instead
+            // (cached, so finite): every row masks it (x = -inf, weight 0)
+            const bool in = kt * TK + t < limit;
+            const uint32_t lo = (uint32_t)(((in ? t % B : 0) * PD + e) * ELT);
+            const int64_t bb = !in ? base[0]
+                             : HALF_UNIFORM ? base[(k * TOK_PER_LD) / 16]
+                                            : (t < 16 ? base[0] : base[1]);
+            kr[k] = ld16(at(reinterpret_cast<const char*>(a.k_cache) + bb, lo));
+            vr[k] = ld16(at(reinterpret_cast<const char*>(a.v_cache) + bb, lo));
         }
     };
     char* kl = lds + tg * TGBYTES;
     char* vl = kl + KBYTES;
     // this lane's address in the transposed V reads (see the file comment)
     const int vtr = (4 * quad + col / 4) * KSTR + 8 * (col % 4);
-    auto store_tile = [&]() {
+    auto store_tile = [&](const uint4 (&kr)[NLD], const uint4 (&vr)[NLD]) {
 #pragma unroll
         for (int k = 0; k < NLD; ++k) {
             const int p = ti + k * TPT, t = p / PPR, e = (p % PPR) * EPP;
@@ -189,7 +214,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
         }
     };
 
-    auto compute = [&](int kt) {
+    // EDGE: some row of the tile must mask some token of this KV tile
+    auto compute = [&](int kt, auto edge_tag) {
+        constexpr bool EDGE = decltype(edge_tag)::value;
         // int8: per-(block, kv head) scales of the two 16-token halves
         float ksc[2] = {1.0f, 1.0f}, vsc[2] = {1.0f, 1.0f};
         if (I8) {
@@ -203,34 +230,34 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
                 }
             }
         }
-        bf16x8 kop[2][4];
+        // S^T for every row block; each K operand is read right before its
+        // MFMAs (all row blocks use it), which keeps few operands live
+        f32x4 acc[MB][2];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) acc[mb][tt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-                kop[tt][ks] = as_bf16x8(*reinterpret_cast<const uint4*>(
+            for (int ks = 0; ks < 4; ++ks) {
+                const bf16x8 kop = as_bf16x8(*reinterpret_cast<const uint4*>(
                     kl + (tt * 16 + col) * KSTR + (32 * ks + 8 * quad) * 2));
-        bf16x8 vop[8];
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-            const uint2 x0 = ds_read_tr16(vl + vtr + 32 * dt);
-            const uint2 x1 = ds_read_tr16(vl + vtr + 16 * KSTR + 32 * dt);
-            vop[dt] = as_bf16x8(make_uint4(x0.x, x0.y, x1.x, x1.y));
-        }
-        const bool edge = kt * TK + TK - 1 > p_first;   // some row of the tile masks some token
+                for (int mb = 0; mb < MB; ++mb)
+                    acc[mb][tt] = mfma16x16x32(kop, qop[mb][ks], acc[mb][tt]);
+            }
+        bf16x8 pop[MB];
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
             float x[2][4];
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) {
-                f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks) acc = mfma16x16x32(kop[tt][ks], qop[mb][ks], acc);
                 const float f = I8 ? sl2 * ksc[tt] : sl2;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    x[tt][i] = acc[i] * f;
-                    if (edge && kt * TK + tt * 16 + 4 * quad + i > rpos[mb])
+                    x[tt][i] = acc[mb][tt][i] * f;
+                    if (EDGE && kt * TK + tt * 16 + 4 * quad + i > rpos[mb])
                         x[tt][i] = -__builtin_huge_valf();
                 }
             }
@@ -242,37 +269,64 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
             mx = fmaxf(mx, lane_xor16(mx));
             mx = fmaxf(mx, lane_xor32(mx));
             const float mn = fmaxf(m[mb], mx);
-            const float mu = mn == -__builtin_huge_valf() ? 0.0f : mn;
-            const float alpha = __builtin_amdgcn_exp2f(m[mb] - mu);
-            m[mb] = mn;
+            if (__builtin_amdgcn_ballot_w64(mn > m[mb] + kLazy) != 0) {   // wave-uniform
+                const float mu = mn == -__builtin_huge_valf() ? 0.0f : mn;
+                const float alpha = __builtin_amdgcn_exp2f(m[mb] - mu);
+                m[mb] = mn;
+                l[mb] *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) o[mb][dt][i] *= alpha;
+            }
+            const float mu = m[mb] == -__builtin_huge_valf() ? 0.0f : m[mb];
             float sum = 0.0f;
-            bf16x8 pop;
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const float pr = __builtin_amdgcn_exp2f(x[tt][i] - mu);
                     sum += pr;
-                    pop[4 * tt + i] = (__bf16)(I8 ? pr * vsc[tt] : pr);
+                    pop[mb][4 * tt + i] = (__bf16)(I8 ? pr * vsc[tt] : pr);
                 }
-            l[mb] = l[mb] * alpha + sum;
+            l[mb] += sum;
+        }
+        // O^T += V^T P^T, each V^T operand read right before its MFMAs
 #pragma unroll
-            for (int dt = 0; dt < 8; ++dt) {
+        for (int dt = 0; dt < 8; ++dt) {
+            const uint2 x0 = ds_read_tr16(vl + vtr + 32 * dt);
+            const uint2 x1 = ds_read_tr16(vl + vtr + 16 * KSTR + 32 * dt);
+            const bf16x8 vop = as_bf16x8(make_uint4(x0.x, x0.y, x1.x, x1.y));
 #pragma unroll
-                for (int i = 0; i < 4; ++i) o[mb][dt][i] *= alpha;
-                o[mb][dt] = mfma16x16x32(vop[dt], pop, o[mb][dt]);
-            }
+            for (int mb = 0; mb < MB; ++mb) o[mb][dt] = mfma16x16x32(vop, pop[mb], o[mb][dt]);
         }
     };
 
-    if (nit > 0) load_tile(tg);
-    for (int it = 0; it < nit; ++it) {
+    // one iteration: tile `it` (held in kr/vr) to LDS, tile it + PF into
+    // kr/vr, then tile `it` computed (the barrier counts are the same in every
+    // wave)
+    auto step = [&](int it, uint4 (&kr)[NLD], uint4 (&vr)[NLD]) {
         const int kt = it * NT + tg;
         __syncthreads();                              // the previous tile's reads are done
-        store_tile();
+        store_tile(kr, vr);
         __syncthreads();
-        if (it + 1 < nit) load_tile(kt + NT);         // in flight while this tile is computed
-        if (kt < nkt) compute(kt);
+        if (it + PF < nit) load_tile(kt + PF * NT, kr, vr);
+        if (kt < nkt) {
+            if (kt * TK + TK - 1 > p_first)
+                compute(kt, std::true_type{});
+            else
+                compute(kt, std::false_type{});
+        }
+    };
+    if (nit > 0) load_tile(tg, kr0, vr0);
+    if constexpr (PF == 2) {
+        if (nit > 1) load_tile(tg + NT, kr1, vr1);
+        for (int it = 0; it < nit; it += 2) {
+            step(it, kr0, vr0);
+            if (it + 1 < nit) step(it + 1, kr1, vr1);
+        }
+    } else {
+        for (int it = 0; it < nit; ++it) step(it, kr0, vr0);
     }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
@@ -338,13 +392,24 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     }
 }
 
-template <int NR, int MB>
-hipError_t launch_shape(const PrefillArgs& a, int tiles, hipStream_t st) {
-    const dim3 grid(tiles, a.num_kv_heads, a.num_seqs);
+template <int NR, int MB, int BS>
+void launch_bs(const PrefillArgs& a, dim3 grid, hipStream_t st) {
     if (a.cache == Dtype::I8)
-        hipLaunchKernelGGL((prefill_kernel<NR, MB, true>), grid, dim3(256), 0, st, a);
+        hipLaunchKernelGGL((prefill_kernel<NR, MB, true, BS>), grid, dim3(256), 0, st, a);
     else
-        hipLaunchKernelGGL((prefill_kernel<NR, MB, false>), grid, dim3(256), 0, st, a);
+        hipLaunchKernelGGL((prefill_kernel<NR, MB, false, BS>), grid, dim3(256), 0, st, a);
+}
+
+template <int NR, int MB>
+hipError_t launch_shape(PrefillArgs a, int tiles, hipStream_t st) {
+    const int64_t total = (int64_t)tiles * a.num_kv_heads * a.num_seqs;
+    if (total > 0x7fffffff) return hipErrorInvalidValue;
+    a.row_tiles = tiles;
+    const dim3 grid((unsigned)total);
+    if (a.block_size == 16)
+        launch_bs<NR, MB, 16>(a, grid, st);
+    else
+        launch_bs<NR, MB, 32>(a, grid, st);
     return hipGetLastError();
 }
 
