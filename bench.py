@@ -56,6 +56,17 @@ KERNEL_SOURCES = ["pa_decode_mfma.hip", "pa_decode_valu.hip", "pa_decode_common.
                   "pa_device.hpp", "pa_kernels.hpp", "pa_write_row.hpp"]
 
 
+PREFILL_SOURCES = ["pa_prefill.hip", "pa_device.hpp", "pa_kernels.hpp"]
+
+
+def source_hash(files) -> str:
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "paged_kv_decode_03_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
 def kernel_hash() -> str:
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
@@ -225,7 +236,14 @@ def bench_multi_query(args, torch, np, pa, synth):
     else:
         roof = {"bound": "mfma", "achieved": round(tfs, 2), "peak": MFMA_BF16_PEAK_TFS,
                 "unit": "TFLOP/s", "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4)}
-    roof.update({"traffic": None, "kernel": "pa_prefill", "bytes_per_launch": nbytes,
+    traffic = None
+    path = os.path.join(ROOT, "profiles", "decode_traffic.json")
+    if os.path.exists(path):
+        with open(path) as fh:
+            ent = json.load(fh).get(f"multi_query_{args.multi_query}")
+        if ent and ent.get("kernel_hash") == source_hash(PREFILL_SOURCES):
+            traffic = ent["bytes_per_launch"]
+    roof.update({"traffic": traffic, "kernel": "pa_prefill", "bytes_per_launch": nbytes,
                  "flops_per_launch": flops})
     line = {
         "metric": ("speculative verify attention GB/s" if verify
