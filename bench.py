@@ -206,11 +206,21 @@ def bench_multi_query(args, torch, np, pa, synth):
     out = torch.empty_like(q)
     mq = int(qs.q_lens.max())
     nbytes, kv, flops = multi_query_counts(case, qs, np)
+    # long contexts: split-K over 512-token partitions, then the log-sum-exp reduce
+    P = spec.partition_size if args.multi_query == "verify_long" else 0
+    maxL = case.max_context_len
+    ws = pa.prefill_workspace(qs.num_tokens, case.Hq, case.D, maxL, P, dev) if P else None
 
     def step(i):
         k, v = pools[i % R]
-        pa.prefill(out, q, k, v, dc.block_tables, dc.context_lens, qsl, float(case.scale), mq,
-                   case.max_context_len, dc.k_scale, dc.v_scale)
+        if P:
+            pa.prefill(None, q, k, v, dc.block_tables, dc.context_lens, qsl, float(case.scale),
+                       mq, maxL, dc.k_scale, dc.v_scale, partition_size=P, tmp_out=ws[0],
+                       tmp_max=ws[1], tmp_sum=ws[2], row_lens=ws[3])
+            pa.decode_splitk_reduce(out, ws[0], ws[1], ws[2], ws[3], maxL, P)
+        else:
+            pa.prefill(out, q, k, v, dc.block_tables, dc.context_lens, qsl, float(case.scale),
+                       mq, maxL, dc.k_scale, dc.v_scale)
 
     stream = torch.cuda.current_stream(dev)
     i, t0 = 0, time.perf_counter()
@@ -229,7 +239,7 @@ def bench_multi_query(args, torch, np, pa, synth):
     ms = e0.elapsed_time(e1) / args.steps
     gbs = nbytes / (ms * 1e-3) / 1e9
     tfs = flops / (ms * 1e-3) / 1e12
-    verify = args.multi_query == "verify"
+    verify = args.multi_query.startswith("verify")
     if verify:
         roof = {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(gbs / HBM_PEAK_GBS, 4)}
@@ -254,6 +264,7 @@ def bench_multi_query(args, torch, np, pa, synth):
         "data": "synthetic",
         "config": {"workload": spec.name + (" verify, 4 query tokens per sequence" if verify
                                             else ", 512-token chunks"),
+                   "partition_size": P,
                    "num_seqs": case.S, "query_tokens": qs.num_tokens,
                    "num_heads": case.Hq, "num_kv_heads": case.Hkv, "head_dim": case.D,
                    "block_size": case.B, "sum_context": int(case.context_lens.sum()),
@@ -335,10 +346,11 @@ def main():
     ap.add_argument("--copy-blocks", type=int, default=0, metavar="N",
                     help="instead of the decode step, time pa_copy_blocks copying N blocks of "
                          "the workload's pool (all kv heads, K and V) into free blocks")
-    ap.add_argument("--multi-query", choices=["verify", "prefill"], default=None,
+    ap.add_argument("--multi-query", choices=["verify", "verify_long", "prefill"], default=None,
                     help="instead of the decode step, time pa_prefill: the speculative verify "
-                         "of 4 tokens per sequence on the Llama-shaped batch, or 512-token "
-                         "prefill chunks after 3584 cached tokens (8 sequences)")
+                         "of 4 tokens per sequence on the Llama-shaped batch (verify) or on the "
+                         "8 x 32768 batch with 512-token split-K and the reduce (verify_long), "
+                         "or 512-token prefill chunks after 3584 cached tokens (8 sequences)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only time a device copy of 1 GiB (read 1 GiB + write 1 GiB); the "
                          "reference for calibrating rocprofv3 FETCH_SIZE / WRITE_SIZE")

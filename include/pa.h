@@ -266,7 +266,8 @@ int pa_copy_blocks(void *k_cache, void *v_cache, float *k_scale, float *v_scale,
  * with k_t, v_t gathered through block_tables and dequantised as in pa_decode.
  * With n_s = 1 this is pa_decode of that sequence.
  *
- *   out             [num_query_tokens][num_heads][head_dim], q_dtype, 16-byte aligned
+ *   out             [num_query_tokens][num_heads][head_dim], q_dtype, 16-byte aligned;
+ *                   written only when partition_size == 0
  *   q               [num_query_tokens][num_heads][head_dim], q_dtype
  *   k_cache, v_cache, block_tables, context_lens, k_scale, v_scale, scale:
  *                   as in pa_decode (context_lens[s] >= n_s)
@@ -274,6 +275,23 @@ int pa_copy_blocks(void *k_cache, void *v_cache, float *k_scale, float *v_scale,
  *                   qsl[num_seqs] = num_query_tokens
  *   max_query_len   host-side bound on every n_s, at most max_context_len; it sizes
  *                   the launch (rows of sequences with more are not written)
+ *   partition_size  0: one pass, result in `out`. > 0 (a multiple of 32): split-K
+ *                   over each row's tokens. Partition j of row r (position p) covers
+ *                   tokens [j P, min(p + 1, (j+1) P)) and stores, for j < ceil((p+1)/P),
+ *                     tmp_out[r][h][j][:] = its normalised output,
+ *                     tmp_max[r][h][j] = a reference max in natural units (at most
+ *                                        ln 256 below its largest logit),
+ *                     tmp_sum[r][h][j] = sum_t exp(x_t - tmp_max),
+ *                   and row_lens[r] = p + 1; `out` is not touched. Then
+ *                   pa_decode_splitk_reduce(out, tmp_out, tmp_max, tmp_sum, row_lens,
+ *                   num_query_tokens, num_heads, head_dim, max_context_len,
+ *                   partition_size, q_dtype, stream) gives the result: it treats each
+ *                   query row as a sequence of length p + 1.
+ *   tmp_out         [num_query_tokens][num_heads][NP][head_dim] fp32 (16-byte aligned),
+ *   tmp_max, tmp_sum  [num_query_tokens][num_heads][NP] fp32, row_lens
+ *                   [num_query_tokens] int32, NP = pa_num_partitions(max_context_len,
+ *                   partition_size): caller-owned workspace, required iff
+ *                   partition_size > 0 (and num_query_tokens > 0).
  * Precision: Q K^T and P V run on bf16 MFMAs with fp32 accumulation; the
  * softmax weights are rounded to bf16 for the P V product (the row sums use
  * the fp32 weights).
@@ -288,7 +306,9 @@ int pa_prefill(void *out, const void *q, const void *k_cache, const void *v_cach
                const int32_t *query_start_loc, const float *k_scale, const float *v_scale,
                float scale, int num_seqs, int num_query_tokens, int max_query_len,
                int num_heads, int num_kv_heads, int head_dim, int block_size, int64_t num_blocks,
-               int max_context_len, pa_dtype q_dtype, pa_dtype cache_dtype, void *stream);
+               int max_context_len, int partition_size, float *tmp_out, float *tmp_max,
+               float *tmp_sum, int32_t *row_lens, pa_dtype q_dtype, pa_dtype cache_dtype,
+               void *stream);
 
 /* Workspace slots per (sequence, query head) that pa_decode_balanced needs:
  * ceil(ceil(max_context_len / 16) / (min_piece_tokens / 16)) + 1, or 0 when

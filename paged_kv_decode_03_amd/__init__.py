@@ -53,7 +53,7 @@ _lib.pa_copy_blocks.restype = _i
 _lib.pa_copy_blocks.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i64, _i, _p]
 _lib.pa_decode_splitk_reduce.restype = _i
 _lib.pa_prefill.argtypes = [_p, _p, _p, _p, _p, _i, _p, _p, _p, _p, _f, _i, _i, _i, _i, _i, _i,
-                            _i, _i64, _i, _i, _i, _p]
+                            _i, _i64, _i, _i, _p, _p, _p, _p, _i, _i, _p]
 _lib.pa_prefill.restype = _i
 _lib.pa_decode_splitk_reduce.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p]
 
@@ -166,13 +166,16 @@ def decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_cont
 
 
 def prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_start_loc, scale,
-            max_query_len, max_context_len, k_scale=None, v_scale=None, stream=None):
+            max_query_len, max_context_len, k_scale=None, v_scale=None, partition_size=0,
+            tmp_out=None, tmp_max=None, tmp_sum=None, row_lens=None, stream=None):
     """Causal attention of several new query tokens per sequence over the pool:
     q and out [T, Hq, D]; rows query_start_loc[s] .. [s+1]-1 are the newest
     tokens of sequence s (already written to the cache and counted by
-    context_lens)."""
+    context_lens). partition_size > 0: split-K partials into the workspace
+    (``prefill_workspace``) instead of ``out``; combine them with
+    ``decode_splitk_reduce(out, tmp_out, tmp_max, tmp_sum, row_lens, ...)``."""
     dev = _dev(out, q, k_cache, v_cache, block_tables, context_lens, query_start_loc, k_scale,
-               v_scale)
+               v_scale, tmp_out, tmp_max, tmp_sum, row_lens)
     if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32 \
             or query_start_loc.dtype != torch.int32:
         raise TypeError("block_tables, context_lens and query_start_loc must be int32")
@@ -180,16 +183,28 @@ def prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_start_lo
     NB, Hkv, B, D2 = k_cache.shape
     S = context_lens.shape[0]
     if D2 != D or v_cache.shape != k_cache.shape or block_tables.shape[0] != S \
-            or query_start_loc.shape != (S + 1,) or out.shape != q.shape:
+            or query_start_loc.shape != (S + 1,) or (out is not None and out.shape != q.shape):
         raise ValueError("shape mismatch")
-    if out.dtype != q.dtype:
+    if out is not None and out.dtype != q.dtype:
         raise TypeError("out must have the dtype of q")
     rc = _lib.pa_prefill(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
                          block_tables.shape[1], _ptr(context_lens), _ptr(query_start_loc),
                          _ptr(k_scale), _ptr(v_scale), float(scale), S, T, int(max_query_len),
-                         Hq, Hkv, D, B, NB, int(max_context_len), _dt(q), _dt(k_cache),
-                         _stream(stream, dev))
+                         Hq, Hkv, D, B, NB, int(max_context_len), int(partition_size),
+                         _ptr(tmp_out), _ptr(tmp_max), _ptr(tmp_sum), _ptr(row_lens), _dt(q),
+                         _dt(k_cache), _stream(stream, dev))
     _check("pa_prefill", rc)
+
+
+def prefill_workspace(num_query_tokens, num_heads, head_dim, max_context_len, partition_size,
+                      device):
+    """(tmp_out, tmp_max, tmp_sum, row_lens) for pa_prefill's split-K."""
+    NP = max(1, num_partitions(max_context_len, partition_size))
+    T, H, D = num_query_tokens, num_heads, head_dim
+    return (torch.empty((T, H, NP, D), dtype=torch.float32, device=device),
+            torch.empty((T, H, NP), dtype=torch.float32, device=device),
+            torch.empty((T, H, NP), dtype=torch.float32, device=device),
+            torch.empty((T,), dtype=torch.int32, device=device))
 
 
 def decode_splitk_reduce(out, tmp_out, tmp_max, tmp_sum, context_lens, max_context_len,

@@ -294,7 +294,9 @@ int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cach
                const int32_t* query_start_loc, const float* k_scale, const float* v_scale,
                float scale, int num_seqs, int num_query_tokens, int max_query_len,
                int num_heads, int num_kv_heads, int head_dim, int block_size, int64_t num_blocks,
-               int max_context_len, pa_dtype q_dtype, pa_dtype cache_dtype, void* stream) {
+               int max_context_len, int partition_size, float* tmp_out, float* tmp_max,
+               float* tmp_sum, int32_t* row_lens, pa_dtype q_dtype, pa_dtype cache_dtype,
+               void* stream) {
     // with no query rows, q and out are never read and may be NULL
     const void* qc = num_query_tokens == 0 && !q ? k_cache : q;
     int rc = check_decode(qc, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
@@ -305,12 +307,28 @@ int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cach
         num_seqs > 65535 || num_kv_heads > 65535 ||
         (int64_t)max_query_len * (num_heads / num_kv_heads) > 0x7fffffff)
         return PA_ERR_SHAPE;
+    if (partition_size < 0 || (partition_size > 0 && partition_size % 32)) return PA_ERR_SHAPE;
     if (!query_start_loc) return PA_ERR_NULL;
-    if (num_query_tokens > 0 && (!out || !aligned16(out))) return out ? PA_ERR_ALIGN : PA_ERR_NULL;
+    const bool split = partition_size > 0;
+    if (num_query_tokens > 0) {
+        if (!split && !out) return PA_ERR_NULL;
+        if (!split && !aligned16(out)) return PA_ERR_ALIGN;
+        if (split && (!tmp_out || !tmp_max || !tmp_sum || !row_lens)) return PA_ERR_NULL;
+        if (split && !aligned16(tmp_out)) return PA_ERR_ALIGN;
+    }
     pa::PrefillArgs a{out, q, k_cache, v_cache, block_tables, context_lens, query_start_loc,
                       k_scale, v_scale, scale, num_seqs, num_heads, num_kv_heads, head_dim,
                       block_size, max_blocks_per_seq, max_query_len, (pa::Dtype)q_dtype,
                       (pa::Dtype)cache_dtype};
+    if (split) {
+        a.partition_size = partition_size;
+        a.num_partitions = pa_num_partitions(max_context_len, partition_size);
+        if (a.num_partitions < 1) a.num_partitions = 1;
+        a.tmp_out = tmp_out;
+        a.tmp_max = tmp_max;
+        a.tmp_sum = tmp_sum;
+        a.row_lens = row_lens;
+    }
     if (!pa::prefill_supports(a)) return PA_ERR_UNSUPPORTED;
     if (num_seqs == 0 || num_query_tokens == 0) return PA_OK;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);

@@ -83,6 +83,14 @@ struct PrefillArgs {
     int num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq;
     int max_query_len;               // bound on every qsl[s+1] - qsl[s]
     Dtype q_dtype, cache;
+    // split-K (partition_size > 0, a multiple of 32): partition j of a row's
+    // tokens goes to slot (row * Hq + h) * num_partitions + j of the
+    // workspace, and row_lens[row] = position + 1 (the reduce's lengths)
+    int partition_size = 0, num_partitions = 1;
+    float* tmp_out = nullptr;
+    float* tmp_max = nullptr;
+    float* tmp_sum = nullptr;
+    int32_t* row_lens = nullptr;
     int row_tiles = 0;               // set by the launcher: row tiles per (sequence, kv head)
 };
 

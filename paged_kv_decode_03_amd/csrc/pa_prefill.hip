@@ -105,7 +105,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     // which read the same KV -- share one XCD's L2
     const int W = gridDim.x, w0 = blockIdx.x;
     const int w = (W % 8) ? w0 : (w0 % 8) * (W / 8) + w0 / 8;
-    const int rt = w % a.row_tiles, sg = w / a.row_tiles;
+    const int NP = a.num_partitions;                  // 1 without split-K
+    const int rt = w % a.row_tiles, rest = w / a.row_tiles;
+    const int part = rest % NP, sg = rest / NP;
     const int g = sg % Hkv, s = sg / Hkv;
     const int G = Hq / Hkv;
     const int q0 = ld_const(a.query_start_loc, s);
@@ -118,8 +120,14 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     const int L = ld_const(a.context_lens, s);
     const int p_first = L - n + tok0;                 // position of the tile's first new token
     const int limit = p_first + min(TQ, n - tok0);    // the tile reads tokens [0, limit)
-    const int nkt = limit > 0 ? (limit + TK - 1) / TK : 0;
-    const int nit = (nkt + NT - 1) / NT;
+    // split-K: this workgroup takes the tokens [t_begin, min(t_begin + P, limit));
+    // P is a multiple of the tile, so no tile straddles two partitions
+    const int P = a.partition_size;
+    const int t_begin = P > 0 ? part * P : 0;
+    if (t_begin >= limit) return;
+    const int kt0 = t_begin / TK;
+    const int nkt = P > 0 ? (min(limit, t_begin + P) + TK - 1) / TK : (limit + TK - 1) / TK;
+    const int nit = (nkt - kt0 + NT - 1) / NT;
     const float sl2 = a.scale * kLog2e;
     const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
 
@@ -306,7 +314,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     // kr/vr, then tile `it` computed (the barrier counts are the same in every
     // wave)
     auto step = [&](int it, uint4 (&kr)[NLD], uint4 (&vr)[NLD]) {
-        const int kt = it * NT + tg;
+        const int kt = kt0 + it * NT + tg;
         __syncthreads();                              // the previous tile's reads are done
         store_tile(kr, vr);
         __syncthreads();
@@ -318,9 +326,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
                 compute(kt, std::false_type{});
         }
     };
-    if (nit > 0) load_tile(tg, kr0, vr0);
+    if (nit > 0) load_tile(kt0 + tg, kr0, vr0);
     if constexpr (PF == 2) {
-        if (nit > 1) load_tile(tg + NT, kr1, vr1);
+        if (nit > 1) load_tile(kt0 + tg + NT, kr1, vr1);
         for (int it = 0; it < nit; it += 2) {
             step(it, kr0, vr0);
             if (it + 1 < nit) step(it + 1, kr1, vr1);
@@ -375,6 +383,34 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
         }
     }
 
+    if (P > 0) {
+        // the partition's normalised output, its reference max in natural units
+        // (within ln 2^kLazy below its largest logit) and its sum; rows that
+        // see no token of the partition write nothing
+        constexpr float kLn2 = 0.6931471805599453f;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            if (rpos[mb] < t_begin) continue;
+            const int64_t slot = orow[mb] / PD * NP + part;
+            const float inv = 1.0f / l[mb];
+            float* dst = a.tmp_out + slot * PD + 4 * quad;
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) {
+                const f32x4 v = {o[mb][dt][0] * inv, o[mb][dt][1] * inv, o[mb][dt][2] * inv,
+                                 o[mb][dt][3] * inv};
+                *reinterpret_cast<f32x4*>(dst + 16 * dt) = v;
+            }
+            if (quad == 0) {
+                a.tmp_max[slot] = m[mb] * kLn2;
+                a.tmp_sum[slot] = l[mb];
+                // the reduce's length of this query token: its position + 1
+                // (written once: kv head 0, the token's first head, partition 0)
+                if (part == 0 && g == 0 && col % G == 0)
+                    a.row_lens[orow[mb] / PD / Hq] = rpos[mb] + 1;
+            }
+        }
+        return;
+    }
     // out[row][d], d = 16 dt + 4 quad + i: four bf16 per store
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
@@ -402,7 +438,7 @@ void launch_bs(const PrefillArgs& a, dim3 grid, hipStream_t st) {
 
 template <int NR, int MB>
 hipError_t launch_shape(PrefillArgs a, int tiles, hipStream_t st) {
-    const int64_t total = (int64_t)tiles * a.num_kv_heads * a.num_seqs;
+    const int64_t total = (int64_t)tiles * a.num_partitions * a.num_kv_heads * a.num_seqs;
     if (total > 0x7fffffff) return hipErrorInvalidValue;
     a.row_tiles = tiles;
     const dim3 grid((unsigned)total);

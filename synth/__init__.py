@@ -439,10 +439,12 @@ def make_queries(case: Case, q_lens, seed: int) -> Queries:
 
 
 # Multi-token workloads over paged caches: the speculative verify of K + 1 = 4
-# tokens per sequence on the Llama-shaped batch, and 512-token prefill chunks
-# appended to 8 cached 3584-token prefixes (contexts of 4096).
+# tokens per sequence on the Llama-shaped batch and on the long-context batch
+# (split over 512-token partitions), and 512-token prefill chunks appended to 8
+# cached 3584-token prefixes (contexts of 4096).
 MULTI_QUERY = {
     "verify": (CONFIGS[2], ("const", 4)),
+    "verify_long": (CONFIGS[3], ("const", 4)),
     "prefill": (Spec("chunked prefill bf16", 8, ("const", 4096), 32, 8, 128, 16,
                      act="bf16", cache="bf16", max_len=4096), ("const", 512)),
 }

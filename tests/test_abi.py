@@ -174,13 +174,13 @@ def test_copy_blocks_validation(kw, code):
 def prefill(**kw):
     args = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, MB=8, lens=FAKE, qsl=FAKE, ks=None,
                 vs=None, scale=0.125, S=4, T=16, maxq=4, Hq=32, Hkv=8, D=128, B=16, NB=64,
-                maxL=128, qdt=BF16, cdt=BF16)
+                maxL=128, P=0, to=None, tm=None, ts=None, rl=None, qdt=BF16, cdt=BF16)
     args.update(kw)
     a = args
     return pa.lib().pa_prefill(
         a["out"], a["q"], a["k"], a["v"], a["bt"], a["MB"], a["lens"], a["qsl"], a["ks"], a["vs"],
         a["scale"], a["S"], a["T"], a["maxq"], a["Hq"], a["Hkv"], a["D"], a["B"], a["NB"],
-        a["maxL"], a["qdt"], a["cdt"], None)
+        a["maxL"], a["P"], a["to"], a["tm"], a["ts"], a["rl"], a["qdt"], a["cdt"], None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -194,6 +194,11 @@ def prefill(**kw):
     (dict(Hq=256, Hkv=8), UNSUP),           # group size 32
     (dict(qdt=BF16, cdt=F32), DTYPE),
     (dict(T=0), OK), (dict(S=0, T=0), OK), (dict(T=0, out=None, q=None), OK),
+    (dict(P=16), SHAPE), (dict(P=-32), SHAPE),   # split-K partitions are multiples of 32
+    (dict(P=64), NULL),                          # split-K without its workspace
+    (dict(P=64, to=FAKE, tm=FAKE, ts=FAKE), NULL),
+    (dict(P=64, to=MIS, tm=FAKE, ts=FAKE, rl=FAKE), ALIGN),
+    (dict(P=64, T=0), OK),
 ])
 def test_prefill_validation(kw, code):
     assert prefill(**kw) == code

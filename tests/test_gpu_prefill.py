@@ -57,13 +57,25 @@ def prepare(name, seed=11):
     return case, qs, dc
 
 
-def run_prefill(case, qs, dc, max_query_len=None):
+def run_prefill(case, qs, dc, max_query_len=None, partition_size=0):
+    """pa_prefill in one pass, or split-K partials then pa_decode_splitk_reduce."""
     q = host_to_dev(qs.q, case.spec.act, "cuda")
     qsl = torch.from_numpy(qs.query_start_loc).cuda()
     out = torch.full_like(q, float("nan"))
     mq = int(qs.q_lens.max()) if max_query_len is None else max_query_len
-    pa.prefill(out, q, dc.k_cache, dc.v_cache, dc.block_tables, dc.context_lens, qsl,
-               float(case.scale), mq, case.max_context_len, dc.k_scale, dc.v_scale)
+    maxL = case.max_context_len
+    if partition_size:
+        ws = pa.prefill_workspace(qs.num_tokens, case.Hq, case.D, maxL, partition_size, "cuda")
+        for t in ws[:3]:
+            t.fill_(float("nan"))
+        pa.prefill(None, q, dc.k_cache, dc.v_cache, dc.block_tables, dc.context_lens, qsl,
+                   float(case.scale), mq, maxL, dc.k_scale, dc.v_scale,
+                   partition_size=partition_size, tmp_out=ws[0], tmp_max=ws[1], tmp_sum=ws[2],
+                   row_lens=ws[3])
+        pa.decode_splitk_reduce(out, ws[0], ws[1], ws[2], ws[3], maxL, partition_size)
+    else:
+        pa.prefill(out, q, dc.k_cache, dc.v_cache, dc.block_tables, dc.context_lens, qsl,
+                   float(case.scale), mq, maxL, dc.k_scale, dc.v_scale)
     torch.cuda.synchronize()
     return as_f64(out)
 
@@ -81,6 +93,39 @@ def test_prefill_parity(name):
     err = np.abs(got - ref).max()
     print(f"[prefill] {name}: max |gpu - oracle| = {err:.3e}", flush=True)
     assert err <= tol(case), f"{name}: max |gpu - oracle| = {err}"
+
+
+@pytest.mark.parametrize("name,P", [("verify_g4", 64), ("verify_g4_i8", 512),
+                                    ("verify_g8_b32", 32), ("g2_i8_b32", 96),
+                                    ("mixed_g4", 128), ("chunk_g4", 256), ("whole_mha", 32),
+                                    ("cow_g8", 512)])
+def test_prefill_splitk_parity(name, P):
+    """Split-K over each row's tokens, combined by the decode reduce with the
+    rows' own lengths, against the oracle; also the row lengths themselves."""
+    case, qs, dc = prepare(name)
+    got = run_prefill(case, qs, dc, partition_size=P)
+    ok, ov = oracle.fill_cache(case)
+    ref = oracle.prefill(qs.q, ok, ov, case.block_tables, case.context_lens, qs.query_start_loc,
+                         case.scale, case.k_scale, case.v_scale)
+    assert np.isfinite(got).all()
+    err = np.abs(got - ref).max()
+    print(f"[prefill split-K] {name} P={P}: max |gpu - oracle| = {err:.3e}", flush=True)
+    assert err <= tol(case), f"{name} P={P}: max |gpu - oracle| = {err}"
+
+
+def test_prefill_splitk_row_lens():
+    case, qs, dc = prepare("mixed_g4")
+    q = host_to_dev(qs.q, case.spec.act, "cuda")
+    qsl = torch.from_numpy(qs.query_start_loc).cuda()
+    ws = pa.prefill_workspace(qs.num_tokens, case.Hq, case.D, case.max_context_len, 64, "cuda")
+    ws[3].fill_(-1)
+    pa.prefill(None, q, dc.k_cache, dc.v_cache, dc.block_tables, dc.context_lens, qsl,
+               float(case.scale), int(qs.q_lens.max()), case.max_context_len,
+               partition_size=64, tmp_out=ws[0], tmp_max=ws[1], tmp_sum=ws[2], row_lens=ws[3])
+    seq = np.repeat(np.arange(case.S), qs.q_lens)
+    pos = case.context_lens[seq] - qs.q_lens[seq] + (np.arange(qs.num_tokens)
+                                                      - qs.query_start_loc[seq])
+    assert np.array_equal(ws[3].cpu().numpy(), (pos + 1).astype(np.int32))
 
 
 def test_prefill_one_token_matches_decode():
@@ -121,16 +166,17 @@ def test_prefill_no_rows():
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("name", ["verify", "prefill"])
+@pytest.mark.parametrize("name", ["verify", "prefill", "verify_long"])
 def test_prefill_full_size_sampled(name):
     spec, ql = synth.MULTI_QUERY[name]
+    P = spec.partition_size if name == "verify_long" else 0
     print(f"[prefill full] {name}: generating", flush=True)
     case = synth.make_case(spec, 2)
     qs = synth.make_queries(case, ql, 3)
     dc = to_device(case)
     fill_pool(dc)
     print(f"[prefill full] {name}: gpu, {qs.num_tokens} rows", flush=True)
-    got = run_prefill(case, qs, dc)
+    got = run_prefill(case, qs, dc, partition_size=P)
     assert np.isfinite(got).all()
     rng = np.random.default_rng(4)
     rows = np.unique(np.concatenate([rng.choice(qs.num_tokens, size=24, replace=False),
