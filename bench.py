@@ -56,7 +56,7 @@ KERNEL_SOURCES = ["pa_decode_mfma.hip", "pa_decode_valu.hip", "pa_decode_common.
                   "pa_device.hpp", "pa_kernels.hpp", "pa_write_row.hpp"]
 
 
-PREFILL_SOURCES = ["pa_prefill.hip", "pa_device.hpp", "pa_kernels.hpp"]
+PREFILL_SOURCES = ["pa_prefill.hip", "pa_prefill.hpp", "pa_device.hpp", "pa_kernels.hpp"]
 
 
 def source_hash(files) -> str:

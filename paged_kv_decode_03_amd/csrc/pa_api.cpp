@@ -13,6 +13,7 @@
 
 #include "pa.h"
 #include "pa_kernels.hpp"
+#include "pa_prefill.hpp"
 
 namespace {
 

@@ -68,32 +68,6 @@ struct ReduceArgs {
     Dtype out_dtype;
 };
 
-// Several new query tokens per sequence (prefill chunks, speculative verify).
-struct PrefillArgs {
-    void* out;                       // [T][Hq][D], q dtype
-    const void* q;                   // [T][Hq][D]
-    const void* k_cache;
-    const void* v_cache;
-    const int32_t* block_tables;
-    const int32_t* context_lens;     // [S], counts the new tokens
-    const int32_t* query_start_loc;  // [S + 1]: rows of sequence s are [qsl[s], qsl[s+1])
-    const float* k_scale;
-    const float* v_scale;
-    float scale;
-    int num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq;
-    int max_query_len;               // bound on every qsl[s+1] - qsl[s]
-    Dtype q_dtype, cache;
-    // split-K (partition_size > 0, a multiple of 32): partition j of a row's
-    // tokens goes to slot (row * Hq + h) * num_partitions + j of the
-    // workspace, and row_lens[row] = position + 1 (the reduce's lengths)
-    int partition_size = 0, num_partitions = 1;
-    float* tmp_out = nullptr;
-    float* tmp_max = nullptr;
-    float* tmp_sum = nullptr;
-    int32_t* row_lens = nullptr;
-    int row_tiles = 0;               // set by the launcher: row tiles per (sequence, kv head)
-};
-
 enum class Schedule { Partitions, Balanced };
 
 hipError_t launch_write_kv(const WriteArgs& a, hipStream_t st);
@@ -104,8 +78,6 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, Schedule sch, hipStream_t st)
 int balanced_grid(const void* kernel, int threads, hipStream_t st);
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t st);
 hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t st);
-bool prefill_supports(const PrefillArgs& a);
-hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st);
 
 bool valu_supports(const DecodeArgs& a);
 bool mfma_supports(const DecodeArgs& a);

@@ -36,7 +36,7 @@
 // and four waves split the context; many rows (prefill chunks): NR = 4, and
 // each KV tile read from HBM feeds 128 rows.
 #include "pa_device.hpp"
-#include "pa_kernels.hpp"
+#include "pa_prefill.hpp"
 
 namespace pa {
 namespace {

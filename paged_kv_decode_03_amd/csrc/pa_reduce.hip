@@ -2,49 +2,124 @@
 //
 // For one (sequence s, query head h) with n = ceil(L_s / P) partitions:
 //   M = max_j m_j, W_j = l_j e^{m_j - M}, out = sum_j W_j o_j / sum_j W_j.
-// One wave per (s, h); lane d handles dims d, d + 64, ...; the per-partition
-// max and sum are wave-uniform scalar loads.
+// One 256-thread workgroup per (s, h). The maxima and weights of all n
+// partitions are computed in parallel (weights kept in LDS); the four waves
+// then take every fourth partition, lane d holding dims d, d + 64, ..., with
+// several partitions' loads in flight, and add their sums in LDS. (A single
+// wave walking the partitions one after another waits a full memory latency
+// per partition.)
 #include "pa_decode_common.hpp"
 
 namespace pa {
 namespace {
 
-__global__ __launch_bounds__(64) void reduce_kernel(ReduceArgs a) {
+constexpr int RW = 4;                     // waves per workgroup
+constexpr int WMAX = 4096;                // partitions whose weights fit in LDS
+
+__device__ __forceinline__ float block_max(float v, float* red) {
+    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+    const int wave = threadIdx.x >> 6;
+    __syncthreads();                      // red is free
+    if ((threadIdx.x & 63) == 0) red[wave] = v;
+    __syncthreads();
+    v = red[0];
+#pragma unroll
+    for (int w = 1; w < RW; ++w) v = fmaxf(v, red[w]);
+    return v;
+}
+
+__device__ __forceinline__ float block_sum(float v, float* red) {
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+    const int wave = threadIdx.x >> 6;
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[wave] = v;
+    __syncthreads();
+    v = red[0];
+#pragma unroll
+    for (int w = 1; w < RW; ++w) v += red[w];
+    return v;
+}
+
+// NV: dims per lane (head_dim <= 64 NV)
+template <int NV>
+__global__ __launch_bounds__(RW * 64) void reduce_kernel(ReduceArgs a) {
+    __shared__ float wts[WMAX];
+    __shared__ float red[RW];
+    __shared__ float part[RW - 1][NV * 64];
     const int sh_i = blockIdx.x;
     const int s = sh_i / a.num_heads;
     const int64_t sh = sh_i;
     const int L = a.context_lens[s];
     const int n = (L + a.partition_size - 1) / a.partition_size;
-    const int lane = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int D = a.head_dim;
     if (n == 0) {
-        for (int d = lane; d < D; d += 64) store_out(a.out, sh * D + d, 0.0f, a.out_dtype);
+        for (int d = tid; d < D; d += RW * 64) store_out(a.out, sh * D + d, 0.0f, a.out_dtype);
         return;
     }
     const float* mp = a.tmp_max + sh * a.num_partitions;
     const float* lp = a.tmp_sum + sh * a.num_partitions;
     const float* op = a.tmp_out + sh * a.num_partitions * D;
     float M = kNegInf;
-    for (int jj = 0; jj < n; ++jj) M = fmaxf(M, mp[jj]);
-    constexpr int MAXV = 16;              // head_dim <= 1024
-    float acc[MAXV];
+    for (int j = tid; j < n; j += RW * 64) M = fmaxf(M, mp[j]);
+    M = block_max(M, red);
+    const bool in_lds = n <= WMAX;
+    float ws = 0.0f;
+    for (int j = tid; j < n; j += RW * 64) {
+        const float W = lp[j] * __builtin_amdgcn_exp2f((mp[j] - M) * kLog2e);
+        ws += W;
+        if (in_lds) wts[j] = W;
+    }
+    const float wsum = block_sum(ws, red);  // its barriers also publish wts
+    auto weight = [&](int j) {
+        return in_lds ? wts[j] : lp[j] * __builtin_amdgcn_exp2f((mp[j] - M) * kLog2e);
+    };
+
+    float acc[NV];
 #pragma unroll
-    for (int k = 0; k < MAXV; ++k) acc[k] = 0.0f;
-    float wsum = 0.0f;
-    for (int jj = 0; jj < n; ++jj) {
-        const float W = lp[jj] * __builtin_amdgcn_exp2f((mp[jj] - M) * kLog2e);
-        wsum += W;
-        const float* o = op + (int64_t)jj * D;
+    for (int k = 0; k < NV; ++k) acc[k] = 0.0f;
+    // wave w: partitions w, w + RW, ...; four of them per round, loads first
+    constexpr int U = 4;
+    int j = wave;
+    for (; j + (U - 1) * RW < n; j += U * RW) {
+        float x[U][NV];
 #pragma unroll
-        for (int k = 0; k < MAXV; ++k) {
-            const int d = lane + 64 * k;
-            if (d < D) acc[k] = fmaf(W, o[d], acc[k]);
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int k = 0; k < NV; ++k) {
+                const int d = lane + 64 * k;
+                x[u][k] = d < D ? op[(int64_t)(j + u * RW) * D + d] : 0.0f;
+            }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const float W = weight(j + u * RW);
+#pragma unroll
+            for (int k = 0; k < NV; ++k) acc[k] = fmaf(W, x[u][k], acc[k]);
         }
     }
+    for (; j < n; j += RW) {
+        const float W = weight(j);
 #pragma unroll
-    for (int k = 0; k < MAXV; ++k) {
+        for (int k = 0; k < NV; ++k) {
+            const int d = lane + 64 * k;
+            if (d < D) acc[k] = fmaf(W, op[(int64_t)j * D + d], acc[k]);
+        }
+    }
+    if (wave > 0) {
+#pragma unroll
+        for (int k = 0; k < NV; ++k) part[wave - 1][k * 64 + lane] = acc[k];
+    }
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
         const int d = lane + 64 * k;
-        if (d < D) store_out(a.out, sh * D + d, acc[k] / wsum, a.out_dtype);
+        if (d < D) {
+            float v = acc[k];
+#pragma unroll
+            for (int w = 0; w < RW - 1; ++w) v += part[w][k * 64 + lane];
+            store_out(a.out, sh * D + d, v / wsum, a.out_dtype);
+        }
     }
 }
 
@@ -53,7 +128,17 @@ __global__ __launch_bounds__(64) void reduce_kernel(ReduceArgs a) {
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t st) {
     const int64_t nwg = (int64_t)a.num_seqs * a.num_heads;
     if (nwg == 0) return hipSuccess;
-    hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)nwg), dim3(64), 0, st, a);
+    const dim3 grid((unsigned)nwg), block(RW * 64);
+    if (a.head_dim <= 64)
+        hipLaunchKernelGGL(reduce_kernel<1>, grid, block, 0, st, a);
+    else if (a.head_dim <= 128)
+        hipLaunchKernelGGL(reduce_kernel<2>, grid, block, 0, st, a);
+    else if (a.head_dim <= 256)
+        hipLaunchKernelGGL(reduce_kernel<4>, grid, block, 0, st, a);
+    else if (a.head_dim <= 512)
+        hipLaunchKernelGGL(reduce_kernel<8>, grid, block, 0, st, a);
+    else
+        hipLaunchKernelGGL(reduce_kernel<16>, grid, block, 0, st, a);
     return hipGetLastError();
 }
 
