@@ -45,7 +45,10 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int PD = 128;               // head_dim
 constexpr int TK = 32;                // tokens per KV tile
-constexpr int KSTR = PD * 2 + 16;     // K and V tile row stride in LDS (bytes), padded
+// K and V tile row stride in LDS (bytes): 72 dwords, 8 banks further per row,
+// so the transposing V reads (4 rows x 32 bytes per 16-lane group) and the K
+// operand reads (8 rows x 16 bytes per pass) hit distinct banks
+constexpr int KSTR = PD * 2 + 32;
 constexpr int KBYTES = TK * KSTR;
 constexpr int TGBYTES = 2 * KBYTES;   // a token group's K and V tiles
 constexpr float kLog2e = 1.4426950408889634f;
@@ -245,10 +248,12 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) acc[mb][tt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        // k slices outermost: the 2 MB accumulators take turns, so no MFMA
+        // waits for the one before it
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
+        for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
+            for (int tt = 0; tt < 2; ++tt) {
                 const bf16x8 kop = as_bf16x8(*reinterpret_cast<const uint4*>(
                     kl + (tt * 16 + col) * KSTR + (32 * ks + 8 * quad) * 2));
 #pragma unroll
