@@ -2,15 +2,20 @@
 
 One step = the whole decode hot path over one batch resident in HBM: the
 slot-mapped write of every sequence's new token, then decode attention over
-every context. Default: pa_write_decode_balanced, both in one launch
-(work-balanced split-K with the log-sum-exp combine in the same kernel);
---separate-write: pa_write_kv_cache then pa_decode_balanced; --schedule
-partitions: pa_write_kv_cache, pa_decode over fixed partitions, then
-pa_decode_splitk_reduce.
+every context. Schedules (--schedule):
+  multi-query: pa_write_prefill with one query row per sequence -- the write
+    and the attention in one launch of the 16x16x32-MFMA kernel, one
+    workgroup per (sequence, kv head) or, with --partition, per 2048-token
+    (or other) partition followed by pa_decode_splitk_reduce;
+  balanced: pa_write_decode_balanced, both in one launch (work-balanced
+    split-K with the log-sum-exp combine in the same kernel); with
+    --separate-write, pa_write_kv_cache then pa_decode_balanced;
+  partitions: pa_write_kv_cache, pa_decode over fixed partitions, then
+    pa_decode_splitk_reduce;
+  auto (default): the fastest measured one for the workload (AUTO_SCHEDULE).
 Default workload: the Llama-3-8B-shaped bf16 GQA batch (64 sequences,
 context lengths U[128, 2048], 32 query / 8 kv heads, head_dim 128, block 16,
-shuffled pool sized 1.25x the need). Split-K partitions are 512 tokens (the
-workload's own); the balanced schedule cuts pieces of at least 128 tokens.
+shuffled pool sized 1.25x the need), on the multi-query schedule.
 
 The KV pool is replicated R times (R x pool >= 2 GB, far above the 256 MB
 last-level cache) and step i uses copy i mod R, so every step streams its KV
@@ -56,7 +61,15 @@ KERNEL_SOURCES = ["pa_decode_mfma.hip", "pa_decode_valu.hip", "pa_decode_common.
                   "pa_device.hpp", "pa_kernels.hpp", "pa_write_row.hpp"]
 
 
-PREFILL_SOURCES = ["pa_prefill.hip", "pa_prefill.hpp", "pa_device.hpp", "pa_kernels.hpp"]
+PREFILL_SOURCES = ["pa_prefill.hip", "pa_prefill.hpp", "pa_device.hpp", "pa_kernels.hpp",
+                   "pa_write_row.hpp"]
+# The step each workload is timed with by default: the fastest measured schedule
+# (the multi-query kernel with the new tokens written in the same launch for the
+# bf16 workloads, split over 2048-token partitions for the long contexts; the
+# balanced schedule for the int8 and the mixed copy-on-write batches, and for
+# the fp32 one, which the multi-query kernel does not cover).
+AUTO_SCHEDULE = {1: ("balanced", None), 2: ("multi-query", 0), 3: ("multi-query", 2048),
+                 4: ("balanced", None), 5: ("balanced", None)}
 
 
 def source_hash(files) -> str:
@@ -77,14 +90,16 @@ def kernel_hash() -> str:
 
 def measured_traffic(cfg: int, partition: int, schedule: str):
     """HBM bytes per decode launch from committed rocprofv3 counter runs, if
-    they were taken on the current kernel source; else None."""
+    they were taken on the current source of the kernel that runs; else None."""
     path = os.path.join(ROOT, "profiles", "decode_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as fh:
         rec = json.load(fh)
     ent = rec.get(f"cfg{cfg}_P{partition}_{schedule}")
-    if not ent or ent.get("kernel_hash") != kernel_hash():
+    want = (source_hash(PREFILL_SOURCES) if schedule.startswith("multi-query")
+            else kernel_hash())
+    if not ent or ent.get("kernel_hash") != want:
         return None
     return ent.get("bytes_per_launch")
 
@@ -334,7 +349,14 @@ def main():
     ap.add_argument("--partition", type=int, default=None,
                     help="split-K partition (default: the workload's), or the smallest "
                          f"balanced piece in tokens (default {BALANCED_MIN_PIECE})")
-    ap.add_argument("--schedule", choices=["balanced", "partitions"], default="balanced")
+    ap.add_argument("--schedule", choices=["auto", "balanced", "partitions", "multi-query"],
+                    default="auto",
+                    help="balanced: pa_write_decode_balanced (one launch); partitions: "
+                         "pa_write_kv_cache, pa_decode, pa_decode_splitk_reduce; multi-query: "
+                         "pa_write_prefill with one query row per sequence (bf16; int8: "
+                         "pa_write_kv_cache then pa_prefill), split-K and the reduce with "
+                         "--partition; auto (default): the fastest measured one for the "
+                         "workload")
     ap.add_argument("--separate-write", action="store_true",
                     help="balanced schedule: the write kernel, then the decode (two launches)")
     ap.add_argument("--graph", action="store_true",
@@ -379,11 +401,16 @@ def main():
     if args.copy_blocks:
         bench_copy_blocks(args, spec, torch, np, pa, synth)
         return
+    if args.schedule == "auto":
+        args.schedule, auto_p = AUTO_SCHEDULE[args.config]
+        if args.partition is None and auto_p is not None:
+            args.partition = auto_p
     balanced = args.schedule == "balanced"
+    mq = args.schedule == "multi-query"
     if args.partition is not None:
         P = args.partition
     else:
-        P = BALANCED_MIN_PIECE if balanced else spec.partition_size
+        P = BALANCED_MIN_PIECE if balanced else 0 if mq else spec.partition_size
     case = synth.make_case(spec, args.config)
     tr = synth.traffic(case)
     dev = torch.device("cuda:0")
@@ -397,16 +424,38 @@ def main():
     S, Hq, D = case.S, case.Hq, case.D
     if balanced:
         ws = pa.balanced_workspace(S, Hq, case.Hkv, D, maxL, P, dev)
+    elif mq:
+        ws = pa.prefill_workspace(S, Hq, D, maxL, P, dev) if P > 0 else None
+        qsl = torch.arange(S + 1, dtype=torch.int32, device=dev)
     else:
         ws = pa.workspace(S, Hq, D, maxL, max(P, 1), dev)
     out = torch.empty_like(dc.q)
     scale = float(case.scale)
     stream = torch.cuda.current_stream(dev)
 
-    fused = balanced and not args.separate_write
+    # the new tokens written by the decode launch itself (the multi-query kernel
+    # does this for bf16 caches)
+    fused = (balanced or (mq and spec.cache == "bf16")) and not args.separate_write
+    one_launch = fused and not (mq and P > 0)      # split-K adds the reduce launch
 
     def step(i, ev=None):
         k, v = pools[i % R]
+        if fused and mq:
+            if ev is not None:
+                ev[0].record(stream)
+            if P > 0:
+                pa.write_prefill(dc.key, dc.value, dc.slot_mapping, None, dc.q, k, v,
+                                 dc.block_tables, dc.context_lens, qsl, scale, 1, maxL,
+                                 partition_size=P, tmp_out=ws[0], tmp_max=ws[1], tmp_sum=ws[2],
+                                 row_lens=ws[3])
+            else:
+                pa.write_prefill(dc.key, dc.value, dc.slot_mapping, out, dc.q, k, v,
+                                 dc.block_tables, dc.context_lens, qsl, scale, 1, maxL)
+            if ev is not None:
+                ev[1].record(stream)
+            if P > 0:
+                pa.decode_splitk_reduce(out, *ws[:3], ws[3], maxL, P)
+            return
         if fused:
             if ev is not None:
                 ev[0].record(stream)
@@ -422,6 +471,13 @@ def main():
         if balanced:
             pa.decode_balanced(out, dc.q, k, v, dc.block_tables, dc.context_lens, scale, maxL, P,
                                *ws, k_scale=dc.k_scale, v_scale=dc.v_scale)
+        elif mq and P > 0:
+            pa.prefill(None, dc.q, k, v, dc.block_tables, dc.context_lens, qsl, scale, 1, maxL,
+                       dc.k_scale, dc.v_scale, partition_size=P, tmp_out=ws[0], tmp_max=ws[1],
+                       tmp_sum=ws[2], row_lens=ws[3])
+        elif mq:
+            pa.prefill(out, dc.q, k, v, dc.block_tables, dc.context_lens, qsl, scale, 1, maxL,
+                       dc.k_scale, dc.v_scale)
         elif P > 0:
             pa.decode(None, dc.q, k, v, dc.block_tables, dc.context_lens, scale, maxL, P, *ws,
                       k_scale=dc.k_scale, v_scale=dc.v_scale)
@@ -430,7 +486,9 @@ def main():
                       k_scale=dc.k_scale, v_scale=dc.v_scale)
         if ev is not None:
             ev[1].record(stream)
-        if not balanced and P > 0:
+        if mq and P > 0:
+            pa.decode_splitk_reduce(out, *ws[:3], ws[3], maxL, P)
+        elif not balanced and P > 0:
             pa.decode_splitk_reduce(out, *ws, dc.context_lens, maxL, P)
 
     # W warm-up steps, continued until WARMUP_S of steps have run: under load
@@ -485,14 +543,14 @@ def main():
     # One launch per step: the launch period of pass 1 bounds the launch's
     # duration from above, and unlike an event pair it carries no marker cost.
     # with graphs the event pairs wrap a whole replay, so the step clock is used
-    dec_mean = ms_per_step if fused or args.graph else float(pair_ms.mean())
+    dec_mean = ms_per_step if one_launch or args.graph else float(pair_ms.mean())
 
     step_bytes = tr["decode"]["total"] + tr["write"]
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     # the timed unit: the decode launch, or with graphs the whole step's replay
     kernel_bytes = tr["decode"]["total"] + (tr["write"] if fused or args.graph else 0)
     achieved = kernel_bytes / (dec_mean * 1e-3) / 1e9
-    sched = "fused" if fused else args.schedule
+    sched = ("fused" if balanced else "multi-query-fused") if fused else args.schedule
     traffic = measured_traffic(args.config, P, sched)
     res = {
         "metric": METRIC,
@@ -515,15 +573,19 @@ def main():
             "unique_kv_tokens": tr["unique_tokens"], "partition_size": P, "pool_copies": R,
             "schedule": args.schedule + ("" if not balanced or fused else " (separate write)")
                         + (", HIP graph replays" if args.graph else ""),
-            "step": ("write + balanced split-K decode + combine, one launch" if fused else
+            "step": ("write + balanced split-K decode + combine, one launch" if fused and balanced
+                     else "write + multi-query kernel with one row per sequence, one launch" +
+                     ("; reduce" if P else "") if fused else
                      "write; balanced split-K decode (combine fused)" if balanced else
+                     "write; multi-query kernel with one row per sequence" +
+                     ("; reduce" if P else "") if mq else
                      "write; split-K decode; reduce" if P else "write; one-pass decode"),
         },
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "seq_tokens_per_s": round(S / (ms_per_step * 1e-3), 1),
         "context_tokens_per_s": round(tr["sum_len"] / (ms_per_step * 1e-3), 1),
         "decode_kernel_us": {"mean": round(dec_mean * 1e3, 2),
-                             "clock": ("launch period" if fused or args.graph
+                             "clock": ("launch period" if one_launch or args.graph
                                        else "event pairs"),
                              "event_pairs": {
                                  "mean": round(float(pair_ms.mean()) * 1e3, 2),
@@ -536,8 +598,11 @@ def main():
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
             "kernel": ("graph replay of the whole step" if args.graph and not fused else
-                       "pa_write_decode_balanced" if fused else "pa_decode_balanced" if balanced
-                       else "pa_decode (split-K partials)" if P else "pa_decode"),
+                       "pa_write_decode_balanced" if fused and balanced else
+                       "pa_write_prefill" + (" (split-K partials)" if P else "") if fused else
+                       "pa_decode_balanced" if balanced else
+                       "pa_prefill" + (" (split-K partials)" if P else "") if mq else
+                       "pa_decode (split-K partials)" if P else "pa_decode"),
             "bytes_per_launch": kernel_bytes,
         },
         "cpu_baseline": None,

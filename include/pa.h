@@ -310,6 +310,29 @@ int pa_prefill(void *out, const void *q, const void *k_cache, const void *v_cach
                float *tmp_sum, int32_t *row_lens, pa_dtype q_dtype, pa_dtype cache_dtype,
                void *stream);
 
+/*
+ * pa_write_prefill -- pa_write_kv_cache of the new tokens followed by
+ * pa_prefill, in one launch. Row r = qsl[s] + j of key and value (the layout of
+ * q: [num_query_tokens][num_kv_heads][head_dim], q_dtype) is new token j of
+ * sequence s, at position L_s - n_s + j, and goes to slot slot_mapping[r]
+ * (int64; negative: not written). The kernel reads those positions from key
+ * and value, never from the cache, and stores them to their slots, so the
+ * cache holds them afterwards exactly as after pa_write_kv_cache, and the
+ * result equals pa_write_kv_cache then pa_prefill. context_lens counts the
+ * new tokens. Other arguments and the split-K option as in pa_prefill.
+ * Supported: bf16 q and cache (an int8 cache returns PA_ERR_UNSUPPORTED; use
+ * pa_write_kv_cache then pa_prefill). key and value 16-byte aligned; PA_CHECK=1
+ * also verifies each slot against its position.
+ */
+int pa_write_prefill(const void *key, const void *value, const int64_t *slot_mapping, void *out,
+                     const void *q, void *k_cache, void *v_cache, const int32_t *block_tables,
+                     int max_blocks_per_seq, const int32_t *context_lens,
+                     const int32_t *query_start_loc, float scale, int num_seqs,
+                     int num_query_tokens, int max_query_len, int num_heads, int num_kv_heads,
+                     int head_dim, int block_size, int64_t num_blocks, int max_context_len,
+                     int partition_size, float *tmp_out, float *tmp_max, float *tmp_sum,
+                     int32_t *row_lens, pa_dtype q_dtype, pa_dtype cache_dtype, void *stream);
+
 /* Workspace slots per (sequence, query head) that pa_decode_balanced needs:
  * ceil(ceil(max_context_len / 16) / (min_piece_tokens / 16)) + 1, or 0 when
  * max_context_len <= 0 or min_piece_tokens < 16. */

@@ -145,6 +145,34 @@ int check_query_starts(const int32_t* query_start_loc, const int32_t* context_le
     return PA_OK;
 }
 
+// PA_CHECK=1, prefill steps that write their new tokens: each row's slot is
+// negative (skipped) or the slot of its position L_s - n_s + j.
+int check_prefill_slots(const int64_t* slot_mapping, const int32_t* query_start_loc,
+                        const int32_t* block_tables, int max_blocks_per_seq,
+                        const int32_t* context_lens, int num_seqs, int num_query_tokens,
+                        int block_size, hipStream_t st) {
+    std::vector<int64_t> slots;
+    std::vector<int32_t> qsl, lens, tables;
+    if (!fetch(slots, slot_mapping, num_query_tokens, st) ||
+        !fetch(qsl, query_start_loc, (int64_t)num_seqs + 1, st) ||
+        !fetch(lens, context_lens, num_seqs, st) ||
+        !fetch(tables, block_tables, (int64_t)num_seqs * max_blocks_per_seq, st))
+        return PA_ERR_LAUNCH;
+    for (int s = 0; s < num_seqs; ++s) {
+        const int n = qsl[s + 1] - qsl[s];
+        for (int j = 0; j < n; ++j) {
+            const int64_t sl = slots[(size_t)qsl[s] + j];
+            if (sl < 0) continue;
+            const int t = lens[s] - n + j;
+            const int64_t want =
+                (int64_t)tables[(size_t)s * max_blocks_per_seq + t / block_size] * block_size +
+                t % block_size;
+            if (sl != want) return PA_ERR_INDEX;
+        }
+    }
+    return PA_OK;
+}
+
 }  // namespace
 
 namespace pa {
@@ -290,6 +318,25 @@ int pa_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale,
     return launch_status(pa::launch_copy_blocks(a, st));
 }
 
+}  // extern "C"
+
+namespace {
+
+// pa_prefill, optionally writing the new tokens first (key != NULL).
+int prefill(const void* key, const void* value, const int64_t* slot_mapping, void* out,
+            const void* q, const void* k_cache, const void* v_cache,
+            const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
+            const int32_t* query_start_loc, const float* k_scale, const float* v_scale,
+            float scale, int num_seqs, int num_query_tokens, int max_query_len, int num_heads,
+            int num_kv_heads, int head_dim, int block_size, int64_t num_blocks,
+            int max_context_len, int partition_size, float* tmp_out, float* tmp_max,
+            float* tmp_sum, int32_t* row_lens, pa_dtype q_dtype, pa_dtype cache_dtype,
+            void* stream);
+
+}  // namespace
+
+extern "C" {
+
 int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
                const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
                const int32_t* query_start_loc, const float* k_scale, const float* v_scale,
@@ -298,6 +345,48 @@ int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cach
                int max_context_len, int partition_size, float* tmp_out, float* tmp_max,
                float* tmp_sum, int32_t* row_lens, pa_dtype q_dtype, pa_dtype cache_dtype,
                void* stream) {
+    return prefill(nullptr, nullptr, nullptr, out, q, k_cache, v_cache, block_tables,
+                   max_blocks_per_seq, context_lens, query_start_loc, k_scale, v_scale, scale,
+                   num_seqs, num_query_tokens, max_query_len, num_heads, num_kv_heads, head_dim,
+                   block_size, num_blocks, max_context_len, partition_size, tmp_out, tmp_max,
+                   tmp_sum, row_lens, q_dtype, cache_dtype, stream);
+}
+
+int pa_write_prefill(const void* key, const void* value, const int64_t* slot_mapping, void* out,
+                     const void* q, void* k_cache, void* v_cache, const int32_t* block_tables,
+                     int max_blocks_per_seq, const int32_t* context_lens,
+                     const int32_t* query_start_loc, float scale, int num_seqs,
+                     int num_query_tokens, int max_query_len, int num_heads, int num_kv_heads,
+                     int head_dim, int block_size, int64_t num_blocks, int max_context_len,
+                     int partition_size, float* tmp_out, float* tmp_max, float* tmp_sum,
+                     int32_t* row_lens, pa_dtype q_dtype, pa_dtype cache_dtype, void* stream) {
+    if (num_query_tokens > 0) {
+        if (!key || !value || !slot_mapping) return PA_ERR_NULL;
+        if (!aligned16(key) || !aligned16(value)) return PA_ERR_ALIGN;
+    }
+    if (cache_dtype != PA_BF16 && valid_cache(cache_dtype) && valid_act(q_dtype))
+        return PA_ERR_UNSUPPORTED;
+    return prefill(num_query_tokens > 0 ? key : nullptr, value, slot_mapping, out, q, k_cache,
+                   v_cache, block_tables, max_blocks_per_seq, context_lens, query_start_loc,
+                   nullptr, nullptr, scale, num_seqs, num_query_tokens, max_query_len, num_heads,
+                   num_kv_heads, head_dim, block_size, num_blocks, max_context_len,
+                   partition_size, tmp_out, tmp_max, tmp_sum, row_lens, q_dtype, cache_dtype,
+                   stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+int prefill(const void* key, const void* value, const int64_t* slot_mapping, void* out,
+            const void* q, const void* k_cache, const void* v_cache,
+            const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
+            const int32_t* query_start_loc, const float* k_scale, const float* v_scale,
+            float scale, int num_seqs, int num_query_tokens, int max_query_len, int num_heads,
+            int num_kv_heads, int head_dim, int block_size, int64_t num_blocks,
+            int max_context_len, int partition_size, float* tmp_out, float* tmp_max,
+            float* tmp_sum, int32_t* row_lens, pa_dtype q_dtype, pa_dtype cache_dtype,
+            void* stream) {
     // with no query rows, q and out are never read and may be NULL
     const void* qc = num_query_tokens == 0 && !q ? k_cache : q;
     int rc = check_decode(qc, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
@@ -330,6 +419,13 @@ int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cach
         a.tmp_sum = tmp_sum;
         a.row_lens = row_lens;
     }
+    if (key) {
+        a.key = key;
+        a.value = value;
+        a.slot_mapping = slot_mapping;
+        a.k_cache_w = const_cast<void*>(k_cache);     // pa_write_prefill's pool is writable
+        a.v_cache_w = const_cast<void*>(v_cache);
+    }
     if (!pa::prefill_supports(a)) return PA_ERR_UNSUPPORTED;
     if (num_seqs == 0 || num_query_tokens == 0) return PA_OK;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
@@ -340,9 +436,19 @@ int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cach
         rc = check_query_starts(query_start_loc, context_lens, num_seqs, num_query_tokens,
                                 max_query_len, st);
         if (rc) return rc;
+        if (key) {
+            rc = check_prefill_slots(slot_mapping, query_start_loc, block_tables,
+                                     max_blocks_per_seq, context_lens, num_seqs,
+                                     num_query_tokens, block_size, st);
+            if (rc) return rc;
+        }
     }
     return launch_status(pa::launch_prefill(a, st));
 }
+
+}  // namespace
+
+extern "C" {
 
 int pa_balanced_slots(int max_context_len, int min_piece_tokens) {
     if (max_context_len <= 0 || min_piece_tokens < 16) return 0;

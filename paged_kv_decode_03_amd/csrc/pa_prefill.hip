@@ -37,6 +37,7 @@
 // each KV tile read from HBM feeds 128 rows.
 #include "pa_device.hpp"
 #include "pa_prefill.hpp"
+#include "pa_write_row.hpp"
 
 namespace pa {
 namespace {
@@ -85,8 +86,10 @@ __device__ __forceinline__ void i8_to_bf16(uint4 v, uint4& lo, uint4& hi) {
     hi = make_uint4(o[4], o[5], o[6], o[7]);
 }
 
-template <int NR, int MB, bool I8, int BS>
+// WR: the kernel also writes the new tokens (bf16 caches)
+template <int NR, int MB, bool I8, int BS, bool WR>
 __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
+    static_assert(!(WR && I8), "the fused write covers bf16 caches");
     constexpr int NT = 4 / NR;
     constexpr int RT = NR * MB * 16;                  // query rows per workgroup
     constexpr int TPT = NR * 64;                      // threads filling one token group's tile
@@ -133,6 +136,21 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     const int nit = (nkt - kt0 + NT - 1) / NT;
     const float sl2 = a.scale * kLog2e;
     const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+    const int new0 = L - n;                           // position of the sequence's first new token
+
+    if constexpr (WR) {
+        // the new tokens of this tile's rows whose positions fall in this
+        // partition go to their slots (every token exactly once over the grid)
+        const int ntok = min(TQ, n - tok0);
+        for (int idx = threadIdx.x; idx < ntok * (PD / 8); idx += 256) {
+            const int j = tok0 + idx / (PD / 8), v = idx % (PD / 8);
+            const int pos = new0 + j;
+            if (P > 0 && (pos < t_begin || pos >= t_begin + P)) continue;
+            write_vector<Dtype::BF16, Dtype::BF16>(a.key, a.value, a.k_cache_w, a.v_cache_w,
+                                                   a.slot_mapping, nullptr, nullptr, Hkv, PD, B,
+                                                   (int64_t)q0 + j, g, v);
+        }
+    }
 
     // query rows of this lane: Q^T operands and positions (-1: a padding row)
     int rpos[MB];
@@ -197,8 +215,23 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
             const int64_t bb = !in ? base[0]
                              : HALF_UNIFORM ? base[(k * TOK_PER_LD) / 16]
                                             : (t < 16 ? base[0] : base[1]);
-            kr[k] = ld16(at(reinterpret_cast<const char*>(a.k_cache) + bb, lo));
-            vr[k] = ld16(at(reinterpret_cast<const char*>(a.v_cache) + bb, lo));
+            if constexpr (WR) {
+                // a new token's row comes from key / value (its slot is being
+                // written by this launch)
+                const int jn = kt * TK + (in ? t : 0) - new0;
+                const char* kp = reinterpret_cast<const char*>(a.k_cache) + bb + lo;
+                const char* vp = reinterpret_cast<const char*>(a.v_cache) + bb + lo;
+                if (jn >= 0) {
+                    const int64_t src = (((int64_t)q0 + jn) * Hkv + g) * PD + e;
+                    kp = reinterpret_cast<const char*>(a.key) + src * 2;
+                    vp = reinterpret_cast<const char*>(a.value) + src * 2;
+                }
+                kr[k] = ld16(kp);
+                vr[k] = ld16(vp);
+            } else {
+                kr[k] = ld16(at(reinterpret_cast<const char*>(a.k_cache) + bb, lo));
+                vr[k] = ld16(at(reinterpret_cast<const char*>(a.v_cache) + bb, lo));
+            }
         }
     };
     char* kl = lds + tg * TGBYTES;
@@ -318,11 +351,13 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     // one iteration: tile `it` (held in kr/vr) to LDS, tile it + PF into
     // kr/vr, then tile `it` computed (the barrier counts are the same in every
     // wave)
+    // With one row group a token group is one wave, alone on its buffer: its
+    // LDS accesses are performed in issue order, so no barrier is needed.
     auto step = [&](int it, uint4 (&kr)[NLD], uint4 (&vr)[NLD]) {
         const int kt = kt0 + it * NT + tg;
-        __syncthreads();                              // the previous tile's reads are done
+        if constexpr (NR > 1) __syncthreads();        // the previous tile's reads are done
         store_tile(kr, vr);
-        __syncthreads();
+        if constexpr (NR > 1) __syncthreads();
         if (it + PF < nit) load_tile(kt + PF * NT, kr, vr);
         if (kt < nkt) {
             if (kt * TK + TK - 1 > p_first)
@@ -436,9 +471,11 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
 template <int NR, int MB, int BS>
 void launch_bs(const PrefillArgs& a, dim3 grid, hipStream_t st) {
     if (a.cache == Dtype::I8)
-        hipLaunchKernelGGL((prefill_kernel<NR, MB, true, BS>), grid, dim3(256), 0, st, a);
+        hipLaunchKernelGGL((prefill_kernel<NR, MB, true, BS, false>), grid, dim3(256), 0, st, a);
+    else if (a.key)
+        hipLaunchKernelGGL((prefill_kernel<NR, MB, false, BS, true>), grid, dim3(256), 0, st, a);
     else
-        hipLaunchKernelGGL((prefill_kernel<NR, MB, false, BS>), grid, dim3(256), 0, st, a);
+        hipLaunchKernelGGL((prefill_kernel<NR, MB, false, BS, false>), grid, dim3(256), 0, st, a);
 }
 
 template <int NR, int MB>

@@ -29,6 +29,16 @@ struct PrefillArgs {
     float* tmp_max = nullptr;
     float* tmp_sum = nullptr;
     int32_t* row_lens = nullptr;
+    // The new tokens' K/V written by the kernel itself (key == nullptr: they are
+    // already in the cache): rows [qsl[s], qsl[s+1]) of key / value [T][Hkv][D]
+    // (q dtype) are the n_s newest tokens of sequence s, going to slots
+    // slot_mapping[row]; their positions are read from key / value, never from
+    // the cache. bf16 caches only.
+    const void* key = nullptr;
+    const void* value = nullptr;
+    const int64_t* slot_mapping = nullptr;
+    void* k_cache_w = nullptr;       // k_cache / v_cache, writable
+    void* v_cache_w = nullptr;
     int row_tiles = 0;               // set by the launcher: row tiles per (sequence, kv head)
 };
 

@@ -190,3 +190,94 @@ def test_prefill_full_size_sampled(name):
     err = np.abs(got[rows] - ref).max()
     print(f"[prefill full] {name}: max err {err:.3e}", flush=True)
     assert err <= tol(case)
+
+
+# ---- pa_write_prefill: the new tokens written by the same launch ------------
+
+def new_token_rows(case, qs):
+    """key / value rows [T, Hkv, D] and slots [T] of every sequence's n_s newest
+    tokens (the query rows), taken from the batch's source draws."""
+    import pins
+    idx, kall, vall = pins.source_rows(case)
+    seq = np.repeat(np.arange(case.S), qs.q_lens)
+    pos = case.context_lens[seq] - qs.q_lens[seq] + (np.arange(qs.num_tokens)
+                                                      - qs.query_start_loc[seq])
+    slots = case.block_tables[seq, pos // case.B].astype(np.int64) * case.B + pos % case.B
+    rows = idx[slots]
+    assert (rows >= 0).all()
+    return kall[rows], vall[rows], slots
+
+
+# (the copy-on-write batch takes one new token per sequence: a new token is
+# never in a shared prefix block there, as in a real copy-on-write pool)
+@pytest.mark.parametrize("name,P", [("verify_g4", 0), ("verify_g8_b32", 0), ("mixed_g4", 0),
+                                    ("chunk_g4", 0), ("whole_mha", 0), ("cow_g8", 0),
+                                    ("verify_g4", 64), ("chunk_g4", 256), ("cow_g8", 512)])
+def test_write_prefill_parity(name, P):
+    """One launch writes the new tokens and attends: the pool afterwards is
+    byte-identical to the oracle's write, the output within tolerance of the
+    oracle. The new tokens' slots hold poison (NaN) before the call."""
+    spec, ql = CASES[name]
+    if name == "cow_g8":
+        ql = ("const", 1)
+    case = synth.make_case(spec, 11)
+    if ql == "whole":
+        ql = case.context_lens.astype(np.int64)
+    qs = synth.make_queries(case, ql, 12)
+    ok, ov = oracle.fill_cache(case)
+    kn, vn, slots = new_token_rows(case, qs)
+    kp, vp = ok.copy(), ov.copy()
+    flat_k = kp.reshape(case.num_blocks, case.Hkv, case.B, case.D)
+    flat_v = vp.reshape(case.num_blocks, case.Hkv, case.B, case.D)
+    flat_k[slots // case.B, :, slots % case.B, :] = synth.BF16_POISON
+    flat_v[slots // case.B, :, slots % case.B, :] = synth.BF16_POISON
+    k = host_to_dev(kp, "bf16", "cuda")
+    v = host_to_dev(vp, "bf16", "cuda")
+    dc = to_device(case)
+    q = host_to_dev(qs.q, "bf16", "cuda")
+    qsl = torch.from_numpy(qs.query_start_loc).cuda()
+    out = torch.full_like(q, float("nan"))
+    maxL = case.max_context_len
+    args = (host_to_dev(kn, "bf16", "cuda"), host_to_dev(vn, "bf16", "cuda"),
+            torch.from_numpy(slots).cuda())
+    if P:
+        ws = pa.prefill_workspace(qs.num_tokens, case.Hq, case.D, maxL, P, "cuda")
+        pa.write_prefill(*args, None, q, k, v, dc.block_tables, dc.context_lens, qsl,
+                         float(case.scale), int(qs.q_lens.max()), maxL, partition_size=P,
+                         tmp_out=ws[0], tmp_max=ws[1], tmp_sum=ws[2], row_lens=ws[3])
+        pa.decode_splitk_reduce(out, ws[0], ws[1], ws[2], ws[3], maxL, P)
+    else:
+        pa.write_prefill(*args, out, q, k, v, dc.block_tables, dc.context_lens, qsl,
+                         float(case.scale), int(qs.q_lens.max()), maxL)
+    torch.cuda.synchronize()
+    from gpu_helpers import dev_to_host
+    assert np.array_equal(dev_to_host(k).view(np.uint8), ok.view(np.uint8)), "K pool differs"
+    assert np.array_equal(dev_to_host(v).view(np.uint8), ov.view(np.uint8)), "V pool differs"
+    got = as_f64(out)
+    ref = oracle.prefill(qs.q, ok, ov, case.block_tables, case.context_lens, qs.query_start_loc,
+                         case.scale)
+    assert np.isfinite(got).all()
+    err = np.abs(got - ref).max()
+    print(f"[write_prefill] {name} P={P}: max |gpu - oracle| = {err:.3e}", flush=True)
+    assert err <= tol(case)
+
+
+def test_write_prefill_matches_two_calls():
+    """Bit-identical to pa_write_kv_cache followed by pa_prefill."""
+    case, qs, dc = prepare("verify_g4")
+    kn, vn, slots = new_token_rows(case, qs)
+    args = (host_to_dev(kn, "bf16", "cuda"), host_to_dev(vn, "bf16", "cuda"),
+            torch.from_numpy(slots).cuda())
+    q = host_to_dev(qs.q, "bf16", "cuda")
+    qsl = torch.from_numpy(qs.query_start_loc).cuda()
+    k2, v2 = dc.k_cache.clone(), dc.v_cache.clone()
+    a = torch.empty_like(q)
+    b = torch.empty_like(q)
+    mq, maxL = int(qs.q_lens.max()), case.max_context_len
+    pa.write_prefill(*args, a, q, dc.k_cache, dc.v_cache, dc.block_tables, dc.context_lens, qsl,
+                     float(case.scale), mq, maxL)
+    pa.write_kv_cache(args[0], args[1], k2, v2, args[2])
+    pa.prefill(b, q, k2, v2, dc.block_tables, dc.context_lens, qsl, float(case.scale), mq, maxL)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert torch.equal(dc.k_cache.view(torch.int16), k2.view(torch.int16))
