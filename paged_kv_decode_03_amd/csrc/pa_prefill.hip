@@ -135,6 +135,11 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     const int nkt = P > 0 ? (min(limit, t_begin + P) + TK - 1) / TK : (limit + TK - 1) / TK;
     const int nit = (nkt - kt0 + NT - 1) / NT;
     const float sl2 = a.scale * kLog2e;
+    // bf16 caches: the logit scale is applied inside the exponent's fma and the
+    // row max is taken over the unscaled products, which needs a factor >= 0; a
+    // negative scale negates Q instead
+    const bool negq = !I8 && sl2 < 0.0f;
+    const float fq = negq ? -sl2 : sl2;
     const int32_t* bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
     const int new0 = L - n;                           // position of the sequence's first new token
 
@@ -168,16 +173,27 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
             uint4 v = make_uint4(0, 0, 0, 0);
             if (valid)
                 v = ld16(reinterpret_cast<const uint16_t*>(a.q) + orow[mb] + 32 * ks + 8 * quad);
+            if (negq) {
+                v.x ^= 0x80008000u;
+                v.y ^= 0x80008000u;
+                v.z ^= 0x80008000u;
+                v.w ^= 0x80008000u;
+            }
             qop[mb][ks] = as_bf16x8(v);
         }
     }
 
     float m[MB], l[MB];
     f32x4 o[MB][8];
+    // bf16 caches: row sums of the bf16 weights by an MFMA against ones (the
+    // same weights the P V product uses); every element holds the row's sum
+    f32x4 lsum[MB];
+    const bf16x8 ones = as_bf16x8(make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
         m[mb] = -__builtin_huge_valf();
         l[mb] = 0.0f;
+        lsum[mb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) o[mb][dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     }
@@ -296,6 +312,42 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
         bf16x8 pop[MB];
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
+          if constexpr (!I8) {
+            // max over the unscaled products (fq >= 0), masked ones excluded
+            float mx = -__builtin_huge_valf();
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const bool msk = EDGE && kt * TK + tt * 16 + 4 * quad + i > rpos[mb];
+                    mx = fmaxf(mx, msk ? -__builtin_huge_valf() : acc[mb][tt][i]);
+                }
+            mx = fmaxf(mx, lane_xor16(mx));
+            mx = fmaxf(mx, lane_xor32(mx));
+            const float mxs = mx == -__builtin_huge_valf() ? mx : mx * fq;
+            const float mn = fmaxf(m[mb], mxs);
+            if (__builtin_amdgcn_ballot_w64(mn > m[mb] + kLazy) != 0) {   // wave-uniform
+                const float mu = mn == -__builtin_huge_valf() ? 0.0f : mn;
+                const float alpha = __builtin_amdgcn_exp2f(m[mb] - mu);
+                m[mb] = mn;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) lsum[mb][i] *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) o[mb][dt][i] *= alpha;
+            }
+            const float nmu = m[mb] == -__builtin_huge_valf() ? 0.0f : -m[mb];
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float pr = __builtin_amdgcn_exp2f(fmaf(acc[mb][tt][i], fq, nmu));
+                    if (EDGE && kt * TK + tt * 16 + 4 * quad + i > rpos[mb]) pr = 0.0f;
+                    pop[mb][4 * tt + i] = (__bf16)pr;
+                }
+            lsum[mb] = mfma16x16x32(ones, pop[mb], lsum[mb]);
+          } else {
             float x[2][4];
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) {
@@ -336,6 +388,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
                     pop[mb][4 * tt + i] = (__bf16)(I8 ? pr * vsc[tt] : pr);
                 }
             l[mb] += sum;
+          }
         }
         // O^T += V^T P^T, each V^T operand read right before its MFMAs
 #pragma unroll
@@ -378,8 +431,12 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-        l[mb] += lane_xor16(l[mb]);
-        l[mb] += lane_xor32(l[mb]);
+        if constexpr (I8) {
+            l[mb] += lane_xor16(l[mb]);
+            l[mb] += lane_xor32(l[mb]);
+        } else {
+            l[mb] = lsum[mb][0];                      // already the whole row's sum
+        }
     }
 
     if (NT > 1) {
