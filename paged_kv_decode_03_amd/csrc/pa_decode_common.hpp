@@ -35,6 +35,7 @@ constexpr int kFastShare = 144;   // see balanced_setup
 constexpr int kChunkCost = 16;    // cost units per chunk (see balanced_setup)
 constexpr int kSegCost = 32;      // cost units per segment (see balanced_setup)
 
+
 template <bool BASE2>
 __device__ __forceinline__ float rel_weight(float m, float M) {
     // e^{m-M} (natural) or 2^{m-M} (base 2); 0 for an empty state.
@@ -241,10 +242,10 @@ __device__ __forceinline__ void decode_partitions(const DecodeArgs& a) {
 // sequences, e.g. those sharing prefix blocks, then share that XCD's L2).
 template <int NWG>                   // waves per workgroup
 struct BalancedShared {
-    int wave_tot[NWG];
+    int wave_tot[NWG], wave_shared[NWG];
     long long wave_cost[NWG];
     long long total, total_cost;
-    int s0[NWG + 1], L0[NWG + 1];
+    int s0[NWG + 1], L0[NWG + 1], g0[NWG + 1];
     long long base0[NWG + 1], cbase0[NWG + 1];
 };
 
@@ -256,7 +257,8 @@ struct SegPos {
     long long Y;      // cost position where chunk 0 of segment (s, g) starts
 };
 
-__device__ __forceinline__ SegPos next_pos(const DecodeArgs& a, SegPos p) {
+// hm: the segment list is kv head major (see balanced_setup)
+__device__ __forceinline__ SegPos next_pos(const DecodeArgs& a, SegPos p, bool hm) {
     if (p.c + 1 < p.n) {
         ++p.c;
         return p;
@@ -264,9 +266,20 @@ __device__ __forceinline__ SegPos next_pos(const DecodeArgs& a, SegPos p) {
     p.c = 0;
     p.Y += (long long)p.n * kChunkCost + kSegCost;
     p.A += p.n;
+    if (hm) {
+        do {                               // sequences with an empty context have no segments
+            if (++p.s == a.num_seqs) {
+                p.s = 0;
+                ++p.g;
+            }
+            p.L = ld_uniform(a.context_lens, p.s);
+            p.n = (p.L + CHUNK - 1) / CHUNK;
+        } while (p.n == 0);
+        return p;
+    }
     if (++p.g < a.num_kv_heads) return p;
     p.g = 0;
-    do {                                   // sequences with an empty context have no segments
+    do {
         ++p.s;
         p.L = ld_uniform(a.context_lens, p.s);
         p.n = (p.L + CHUNK - 1) / CHUNK;
@@ -303,6 +316,7 @@ struct WaveRange {
     long long X0, X1, wv;
     Ranges rg;
     SegPos cur;       // chunk X0
+    bool hm;          // the segment list is kv head major
 };
 
 // Set-up shared by the balanced drivers: chunk counts, their scan over the
@@ -328,23 +342,40 @@ __device__ __forceinline__ bool balanced_setup(const DecodeArgs& a, BalancedShar
     // segment cost on every measured batch (1-3% on the mixed-length ones);
     // 24 and 48 units were 4-5% slower where all contexts have one length,
     // as the cuts then fall just off the segment boundaries.
-    // Chunk c of segment (s, g) spans the units from
-    // P = Y_s + g (n_s kChunkCost + kSegCost) + kSegCost + c kChunkCost, Y_s
-    // the cost of the sequences before s, and belongs to the range holding
-    // its last unit P + kChunkCost - 1.
+    // Segment order. Sequence major (the 8 kv heads of a sequence in a row):
+    // chunk c of segment (s, g) spans the units from
+    // P = Y_s Hkv + g (n_s kChunkCost + kSegCost) + kSegCost + c kChunkCost,
+    // Y_s the cost of one kv head's segments of the sequences before s; a
+    // block's kv-head tiles, contiguous in the pool, are then read by
+    // neighbouring waves. Kv head major, chosen when at least a quarter of
+    // the sequences start on the same physical block as the next one (copy-
+    // on-write prefixes): P = g Yh + Y_s + kSegCost + c kChunkCost, Yh the cost
+    // of one kv head's segments. Each XCD then takes about one kv head's share
+    // of the list, so the shared prefix blocks that many sequences reread stay
+    // in its L2 for one head (2 MB for the mixed batch's four 1024-token
+    // prefixes) rather than for all heads (its whole 4 MB L2): 6% faster on
+    // that batch, 1-2% slower on batches without sharing. (Every workgroup
+    // takes the same decision from the same data.) A chunk belongs to the
+    // range holding its last unit P + kChunkCost - 1.
     constexpr int CC = kChunkCost, SC = kSegCost;
 
     // 1. chunk counts and costs per sequence: thread t sums its slice
     const int K = (S + NWG * 64 - 1) / (NWG * 64);
     const int sb = min(S, tid * K), se = min(S, sb + K);
     int my = 0, L1 = 0;                              // L1: length of sequence sb, kept
+    int shared = 0;                                  // s whose first block is s + 1's
     long long myc = 0;
     for (int s = sb; s < se; ++s) {
-        const int L = ld_const(a.context_lens, s);
+        // all four loads at once (entry 0 of a block-table row always exists)
+        const int t = min(s + 1, S - 1);
+        const int L = ld_const(a.context_lens, s), Ln = ld_const(a.context_lens, t);
+        const int b = ld_const(a.block_tables, (int64_t)s * a.max_blocks_per_seq);
+        const int bn = ld_const(a.block_tables, (int64_t)t * a.max_blocks_per_seq);
         if (s == sb) L1 = L;
         const int n = (L + CHUNK - 1) / CHUNK;
         my += n;
         myc += n ? (long long)n * CC + SC : 0;
+        if (t > s && L > a.block_size && Ln > a.block_size && b == bn) ++shared;
     }
     int inc = my;                                    // inclusive scans over the workgroup
     long long incc = myc;
@@ -357,17 +388,24 @@ __device__ __forceinline__ bool balanced_setup(const DecodeArgs& a, BalancedShar
             incc += yc;
         }
     }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) shared += __shfl_xor(shared, off);
     if (lane == 63) {
         sh.wave_tot[wave] = inc;
         sh.wave_cost[wave] = incc;
+        sh.wave_shared[wave] = shared;
     }
     __syncthreads();
-    int wbase = 0;
+    int wbase = 0, nshared = 0;
     long long wbasec = 0;
-    for (int v = 0; v < wave; ++v) {
-        wbase += sh.wave_tot[v];
-        wbasec += sh.wave_cost[v];
+    for (int v = 0; v < NWG; ++v) {
+        if (v < wave) {
+            wbase += sh.wave_tot[v];
+            wbasec += sh.wave_cost[v];
+        }
+        nshared += sh.wave_shared[v];
     }
+    const bool hm = uniform(nshared) * 4 >= S;       // kv head major (see above)
     const int excl = wbase + inc - my;               // chunks of sequences before sb
     const long long exclc = wbasec + incc - myc;     // their cost, per kv head
     if (tid == NWG * 64 - 1) {
@@ -407,7 +445,32 @@ __device__ __forceinline__ bool balanced_setup(const DecodeArgs& a, BalancedShar
 
     // 2. locate the sequence holding the cost position where each wave's
     // range starts (v = NWG: the next workgroup's first, where the last ends)
+    const long long Th = T / Hkv, Tch = Tc / Hkv;    // one kv head's chunks and cost
     auto locate = [&](long long Y, int v) {
+        if (hm) {
+            if (Y >= Tc) return;
+            const int g = (int)(Y / Tch);
+            const long long Yr = Y - (long long)g * Tch;
+            if (exclc <= Yr && Yr < exclc + myc) {
+                long long base = excl, cbase = exclc;
+                for (int s = sb; s < se; ++s) {
+                    const int L = s == sb ? L1 : ld_const(a.context_lens, s);
+                    const int n = (L + CHUNK - 1) / CHUNK;
+                    const long long cost = n ? (long long)n * CC + SC : 0;
+                    if (Yr < cbase + cost) {
+                        sh.s0[v] = s;
+                        sh.L0[v] = L;
+                        sh.g0[v] = g;
+                        sh.base0[v] = (long long)g * Th + base;
+                        sh.cbase0[v] = (long long)g * Tch + cbase;
+                        break;
+                    }
+                    base += n;
+                    cbase += cost;
+                }
+            }
+            return;
+        }
         if ((long long)Hkv * exclc <= Y && Y < (long long)Hkv * (exclc + myc)) {
             long long base = (long long)Hkv * excl, cbase = (long long)Hkv * exclc;
             for (int s = sb; s < se; ++s) {
@@ -435,8 +498,10 @@ __device__ __forceinline__ bool balanced_setup(const DecodeArgs& a, BalancedShar
         const long long base = uniform64(sh.base0[v]), cbase = uniform64(sh.cbase0[v]);
         const int n = (L + CHUNK - 1) / CHUNK;
         const long long sc = (long long)n * CC + SC;
-        const int g = (int)((Y - cbase) / sc);
-        const long long off = (Y - cbase) - (long long)g * sc;    // < sc, so c < n
+        // head major: base / cbase already name segment (s, g0)
+        const int g = hm ? uniform(sh.g0[v]) : (int)((Y - cbase) / sc);
+        const long long gb = hm ? 0 : g;              // segments of s before (s, g)
+        const long long off = (Y - cbase) - gb * sc;   // < sc, so c < n
         const int c = off < SC ? 0 : (int)((off - SC) / CC);
         if (p) {
             p->s = s;
@@ -444,12 +509,13 @@ __device__ __forceinline__ bool balanced_setup(const DecodeArgs& a, BalancedShar
             p->n = n;
             p->g = g;
             p->c = c;
-            p->A = base + (long long)g * n;
-            p->Y = cbase + (long long)g * sc + SC;
+            p->A = base + gb * n;
+            p->Y = cbase + gb * sc + SC;
         }
-        return base + (long long)g * n + c;
+        return base + gb * n + c;
     };
     r.rg = rg;
+    r.hm = hm;
     r.wv = (long long)w * NWG + wave;                 // this wave's range index
     const long long Y0 = rg.start(r.wv);
     if (Y0 >= Tc) return false;                      // uniform across the wave
@@ -540,7 +606,7 @@ __device__ __forceinline__ void decode_balanced(const DecodeArgs& a) {
     // that ends here. Returns false after the range's last chunk.
     auto one = [&](typename Core::Chunk& cb, typename Core::Chunk& nb) -> bool {
         const bool more = left > 1;
-        const SegPos nxp = more ? next_pos(a, cur) : cur;
+        const SegPos nxp = more ? next_pos(a, cur, r.hm) : cur;
         nb = core.load(nxp.s, nxp.g, nxp.c);
         core.step(St, cb, cur.c, cur.L);
         if (more && nxp.c != 0) {                    // same segment
@@ -625,7 +691,7 @@ __device__ __forceinline__ void decode_balanced_ring(const DecodeArgs& a) {
     const bool writes = a.slot_mapping != nullptr;
     auto issue_next = [&](char* sp) {
         core.issue(sp, ahead.s, ahead.g, ahead.c, writes && ahead.c + 1 == ahead.n);
-        if (++issued < n) ahead = next_pos(a, ahead);
+        if (++issued < n) ahead = next_pos(a, ahead, r.hm);
     };
 #pragma unroll
     for (int k = 0; k < R; ++k)
@@ -651,7 +717,7 @@ __device__ __forceinline__ void decode_balanced_ring(const DecodeArgs& a) {
         }
         end(St, cur, last);
         if (last) break;
-        cur = next_pos(a, cur);
+        cur = next_pos(a, cur, r.hm);
         core.begin_segment(cur.s, cur.g);
         wait_vmcnt<0>();
         core.init(St);

@@ -454,15 +454,22 @@ def test_balanced_onehot_bit_exact(name, P):
 
 @pytest.mark.parametrize("name", ["cfg1", "cfg2s", "cfg5s", "g4_b32"])
 def test_balanced_placement_invariance(name):
-    case, dc, _, _, _ = prepared(name)
+    """Renaming physical blocks gives a bit-identical output. Un-sharing the
+    copy-on-write prefixes changes the schedule itself (the balanced decode
+    orders its work kv head major when sequences share first blocks), so the
+    contexts are cut elsewhere and the split-K combination rounds differently:
+    that output is checked against the oracle and the shared one to tolerance."""
+    case, dc, _, _, ref = prepared(name)
     base = dev_to_host(run_decode(dc, 32, balanced=True))
-    variants = [synth.permute_placement(case, 41)]
+    dv = to_device(synth.permute_placement(case, 41))
+    fill_pool(dv)
+    assert np.array_equal(dev_to_host(run_decode(dv, 32, balanced=True)), base)
     if case.spec.prefix_groups:
-        variants.append(synth.unshare_prefixes(case))
-    for var in variants:
-        dv = to_device(var)
+        dv = to_device(synth.unshare_prefixes(case))
         fill_pool(dv)
-        assert np.array_equal(dev_to_host(run_decode(dv, 32, balanced=True)), base)
+        got = as_f64(run_decode(dv, 32, balanced=True))
+        assert np.abs(got - ref).max() <= tol(case)
+        assert np.abs(got - as_f64(run_decode(dc, 32, balanced=True))).max() <= tol(case)
 
 
 @pytest.mark.parametrize("name", ["cfg1", "cfg2s", "cfg4s", "cfg5s"])
