@@ -281,3 +281,46 @@ def test_write_prefill_matches_two_calls():
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
     assert torch.equal(dc.k_cache.view(torch.int16), k2.view(torch.int16))
+
+
+def test_pa_check_rejects_bad_queries(monkeypatch):
+    """PA_CHECK=1 validates the query layout and the new tokens' slots on the
+    host (nothing is launched): starts that do not end at the row count, more
+    rows than context, more rows than max_query_len, a slot that is not its
+    token's position."""
+    case, qs, dc = prepare("verify_g4")
+    q = host_to_dev(qs.q, "bf16", "cuda")
+    out = torch.empty_like(q)
+    maxL = case.max_context_len
+    monkeypatch.setenv("PA_CHECK", "1")
+
+    def call(qsl_np, mq):
+        qsl = torch.from_numpy(qsl_np.astype(np.int32)).cuda()
+        pa.prefill(out, q, dc.k_cache, dc.v_cache, dc.block_tables, dc.context_lens, qsl,
+                   float(case.scale), mq, maxL)
+
+    good = qs.query_start_loc.copy()
+    call(good, 4)                                   # accepted
+    bad = good.copy()
+    bad[-1] -= 1                                    # does not end at num_query_tokens
+    with pytest.raises(pa.PAError) as e:
+        call(bad, 4)
+    assert e.value.status == -7
+    with pytest.raises(pa.PAError) as e:
+        call(good, 3)                               # a sequence has more rows than max_query_len
+    assert e.value.status == -7
+    lens = dc.context_lens.clone()
+    lens[0] = 2                                     # fewer tokens than its 4 rows
+    with pytest.raises(pa.PAError) as e:
+        pa.prefill(out, q, dc.k_cache, dc.v_cache, dc.block_tables, lens,
+                   torch.from_numpy(good).cuda(), float(case.scale), 4, maxL)
+    assert e.value.status == -7
+    kn, vn, slots = new_token_rows(case, qs)
+    bad_slots = slots.copy()
+    bad_slots[0] += 1                               # not the slot of its position
+    with pytest.raises(pa.PAError) as e:
+        pa.write_prefill(host_to_dev(kn, "bf16", "cuda"), host_to_dev(vn, "bf16", "cuda"),
+                         torch.from_numpy(bad_slots).cuda(), out, q, dc.k_cache.clone(),
+                         dc.v_cache.clone(), dc.block_tables, dc.context_lens,
+                         torch.from_numpy(good).cuda(), float(case.scale), 4, maxL)
+    assert e.value.status == -7
