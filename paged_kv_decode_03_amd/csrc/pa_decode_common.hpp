@@ -34,6 +34,7 @@ constexpr int CHUNK = 16;    // tokens per chunk
 constexpr int kFastShare = 144;   // see balanced_setup
 constexpr int kChunkCost = 16;    // cost units per chunk (see balanced_setup)
 constexpr int kSegCost = 32;      // cost units per segment (see balanced_setup)
+constexpr int kSegCostG8 = 96;    // the same, 8 or more query heads per kv head
 
 
 template <bool BASE2>
@@ -257,14 +258,15 @@ struct SegPos {
     long long Y;      // cost position where chunk 0 of segment (s, g) starts
 };
 
-// hm: the segment list is kv head major (see balanced_setup)
-__device__ __forceinline__ SegPos next_pos(const DecodeArgs& a, SegPos p, bool hm) {
+// hm: the segment list is kv head major; sc: a segment's fixed cost (see
+// balanced_setup)
+__device__ __forceinline__ SegPos next_pos(const DecodeArgs& a, SegPos p, bool hm, int sc) {
     if (p.c + 1 < p.n) {
         ++p.c;
         return p;
     }
     p.c = 0;
-    p.Y += (long long)p.n * kChunkCost + kSegCost;
+    p.Y += (long long)p.n * kChunkCost + sc;
     p.A += p.n;
     if (hm) {
         do {                               // sequences with an empty context have no segments
@@ -317,6 +319,7 @@ struct WaveRange {
     Ranges rg;
     SegPos cur;       // chunk X0
     bool hm;          // the segment list is kv head major
+    int sc;           // a segment's fixed cost, cost units
 };
 
 // Set-up shared by the balanced drivers: chunk counts, their scan over the
@@ -341,7 +344,11 @@ __device__ __forceinline__ bool balanced_setup(const DecodeArgs& a, BalancedShar
     // chunks' worth was level with or faster than whole-chunk cuts with no
     // segment cost on every measured batch (1-3% on the mixed-length ones);
     // 24 and 48 units were 4-5% slower where all contexts have one length,
-    // as the cuts then fall just off the segment boundaries.
+    // as the cuts then fall just off the segment boundaries. With eight query
+    // heads to a kv head the fixed work is larger (twice the query rows and
+    // partial states to merge): 96 units there were 1-2% faster on the mixed
+    // batch than 32, 128 and more slower again. (kSegCost below stands for
+    // whichever applies.)
     // Segment order. Sequence major (the 8 kv heads of a sequence in a row):
     // chunk c of segment (s, g) spans the units from
     // P = Y_s Hkv + g (n_s kChunkCost + kSegCost) + kSegCost + c kChunkCost,
@@ -357,7 +364,7 @@ __device__ __forceinline__ bool balanced_setup(const DecodeArgs& a, BalancedShar
     // that batch, 1-2% slower on batches without sharing. (Every workgroup
     // takes the same decision from the same data.) A chunk belongs to the
     // range holding its last unit P + kChunkCost - 1.
-    constexpr int CC = kChunkCost, SC = kSegCost;
+    constexpr int CC = kChunkCost, SC = G >= 8 ? kSegCostG8 : kSegCost;
 
     // 1. chunk counts and costs per sequence: thread t sums its slice
     const int K = (S + NWG * 64 - 1) / (NWG * 64);
@@ -516,6 +523,7 @@ __device__ __forceinline__ bool balanced_setup(const DecodeArgs& a, BalancedShar
     };
     r.rg = rg;
     r.hm = hm;
+    r.sc = SC;
     r.wv = (long long)w * NWG + wave;                 // this wave's range index
     const long long Y0 = rg.start(r.wv);
     if (Y0 >= Tc) return false;                      // uniform across the wave
@@ -606,7 +614,7 @@ __device__ __forceinline__ void decode_balanced(const DecodeArgs& a) {
     // that ends here. Returns false after the range's last chunk.
     auto one = [&](typename Core::Chunk& cb, typename Core::Chunk& nb) -> bool {
         const bool more = left > 1;
-        const SegPos nxp = more ? next_pos(a, cur, r.hm) : cur;
+        const SegPos nxp = more ? next_pos(a, cur, r.hm, r.sc) : cur;
         nb = core.load(nxp.s, nxp.g, nxp.c);
         core.step(St, cb, cur.c, cur.L);
         if (more && nxp.c != 0) {                    // same segment
@@ -691,7 +699,7 @@ __device__ __forceinline__ void decode_balanced_ring(const DecodeArgs& a) {
     const bool writes = a.slot_mapping != nullptr;
     auto issue_next = [&](char* sp) {
         core.issue(sp, ahead.s, ahead.g, ahead.c, writes && ahead.c + 1 == ahead.n);
-        if (++issued < n) ahead = next_pos(a, ahead, r.hm);
+        if (++issued < n) ahead = next_pos(a, ahead, r.hm, r.sc);
     };
 #pragma unroll
     for (int k = 0; k < R; ++k)
@@ -717,7 +725,7 @@ __device__ __forceinline__ void decode_balanced_ring(const DecodeArgs& a) {
         }
         end(St, cur, last);
         if (last) break;
-        cur = next_pos(a, cur, r.hm);
+        cur = next_pos(a, cur, r.hm, r.sc);
         core.begin_segment(cur.s, cur.g);
         wait_vmcnt<0>();
         core.init(St);
