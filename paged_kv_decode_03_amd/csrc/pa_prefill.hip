@@ -86,6 +86,38 @@ __device__ __forceinline__ void i8_to_bf16(uint4 v, uint4& lo, uint4& hi) {
     hi = make_uint4(o[4], o[5], o[6], o[7]);
 }
 
+// Batches of at most this many sequences are placed by length (snake_seq).
+constexpr int kSnakeMax = 256;
+
+// The sequence that takes place p of the XCD-contiguous sequence list when
+// the places are dealt by length: the sequences ranked by context length
+// (longest first, ties by index) go to the 8 XCDs' runs of the list in a
+// snake (ranks 0-7 to XCDs 0-7, ranks 8-15 to XCDs 7-0, ...), each run
+// longest first. Every XCD then gets about the same share of the KV, and the
+// longest contexts start first. S = 8 runs of S / 8 places, S <= blockDim.x;
+// all threads of the workgroup call it (it has barriers). sh: S + 1 ints of
+// LDS, free again on return.
+__device__ int snake_seq(const int32_t* lens, int S, int p, int* sh) {
+    const int t = threadIdx.x;
+    if (t < S) sh[t] = lens[t];
+    __syncthreads();
+    const int per = S / 8, x = p / per, j = p % per;
+    const int r = 8 * j + ((j & 1) ? 7 - x : x);
+    if (t < S) {
+        const int Lt = sh[t];
+        int rank = 0;
+        for (int u = 0; u < S; ++u) {
+            const int Lu = sh[u];
+            rank += (Lu > Lt) || (Lu == Lt && u < t);
+        }
+        if (rank == r) sh[S] = t;                     // ranks are a permutation of 0..S-1
+    }
+    __syncthreads();
+    const int seq = sh[S];
+    __syncthreads();
+    return seq;
+}
+
 // WR: the kernel also writes the new tokens (bf16 caches)
 template <int NR, int MB, bool I8, int BS, bool WR>
 __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
@@ -105,16 +137,28 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     const int col = lane & 15, quad = lane >> 4;
     const int Hq = a.num_heads, Hkv = a.num_kv_heads;
     constexpr int B = BS;                             // block size (16 or 32)
-    // workgroup -> (row tile, kv head, sequence), XCD-contiguous: consecutive
-    // workgroups go to the 8 XCDs in turn, so the logical index runs through
-    // each XCD's share first, and the row tiles of one (sequence, kv head) --
-    // which read the same KV -- share one XCD's L2
+    // workgroup -> (row tile, kv head, sequence). Consecutive workgroups go
+    // to the 8 XCDs in turn; the logical index runs through each XCD's share
+    // first, so the row tiles of one (sequence, kv head), which read the same
+    // KV, share one XCD's L2, and so do the kv heads of a sequence, whose
+    // tiles of a block are neighbours in the pool. (Spreading the kv heads
+    // over the XCDs, which evens out the XCDs' shares of the KV, was 4-5%
+    // slower on the 64-sequence batch, with or without rotating the heads.)
+    // Split-K with one row tile: the logical index itself, which spreads the
+    // partitions of a (sequence, kv head) over the XCDs: 1-3% faster on the
+    // long-context decode and verify passes.
     const int W = gridDim.x, w0 = blockIdx.x;
-    const int w = (W % 8) ? w0 : (w0 % 8) * (W / 8) + w0 / 8;
+    const bool spread = a.row_tiles == 1 && a.num_partitions > 1;
+    const int w = (W % 8 || spread) ? w0 : (w0 % 8) * (W / 8) + w0 / 8;
     const int NP = a.num_partitions;                  // 1 without split-K
     const int rt = w % a.row_tiles, rest = w / a.row_tiles;
     const int part = rest % NP, sg = rest / NP;
-    const int g = sg % Hkv, s = sg / Hkv;
+    const int g = sg % Hkv;
+    // one row tile, no split: the sequences are placed by length (snake_seq)
+    const int s = (a.row_tiles == 1 && NP == 1 && W % 8 == 0 && a.num_seqs % 8 == 0 &&
+                   a.num_seqs <= kSnakeMax)
+                      ? snake_seq(a.context_lens, a.num_seqs, sg / Hkv, reinterpret_cast<int*>(lds))
+                      : sg / Hkv;
     const int G = Hq / Hkv;
     const int q0 = ld_const(a.query_start_loc, s);
     const int n = ld_const(a.query_start_loc, s + 1) - q0;
@@ -201,10 +245,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     // this thread's pieces of a tile: piece p = ti + k TPT is token p / PPR,
     // elements (p % PPR) * EPP ..
     const int ti = rg * 64 + lane;
-    // tiles in flight in registers: PF of them (buffers 0 and 1 alternate).
-    // Few rows per wave: one, so that two waves fit on a SIMD.
-    constexpr int PF = 1;
-    uint4 kr0[NLD], vr0[NLD], kr1[PF == 2 ? NLD : 1], vr1[PF == 2 ? NLD : 1];
+    // one tile in flight in registers (two would leave one wave per SIMD)
+    uint4 kr[NLD], vr[NLD];
     // A piece's address: the (block, kv head) tile's base, a scalar, plus
     // the lane's offset inside the tile (a tile starts on a block boundary,
     // so token t of the tile is row t % B of its block).
@@ -213,14 +255,19 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     // tokens of one load instruction: all in the same 16-token half?
     constexpr int TOK_PER_LD = TPT / PPR;
     constexpr bool HALF_UNIFORM = TOK_PER_LD <= 16;
-    auto load_tile = [&](int kt, uint4 (&kr)[NLD], uint4 (&vr)[NLD]) {
-        // the tile's (at most two) block ids as scalar loads: a vector load of
-        // a block id would have to wait for every K/V load issued before it
-        int64_t base[2] = {0, 0};
+    // The tile's (at most two) block ids, as scalar loads (a vector load of
+    // a block id would have to wait for every K/V load issued before it),
+    // turned into the byte offsets of its (block, kv head) tiles. They are
+    // fetched one tile ahead: under a saturated memory system even a cached
+    // id takes long to come back, and waiting for it between a tile's arrival
+    // and the next tile's loads would leave the wave with nothing in flight.
+    auto tile_bases = [&](int kt, int64_t (&base)[2]) {
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf)
-            if (kt * TK + 16 * hf < limit)
-                base[hf] = (int64_t)ld_uniform(bt, (kt * TK + 16 * hf) / B) * blk_stride + head_off;
+            base[hf] = kt * TK + 16 * hf < limit
+                ? (int64_t)ld_uniform(bt, (kt * TK + 16 * hf) / B) * blk_stride + head_off : 0;
+    };
+    auto load_tile = [&](int kt, const int64_t (&base)[2]) {
 #pragma unroll
         for (int k = 0; k < NLD; ++k) {
             const int p = ti + k * TPT, t = p / PPR, e = (p % PPR) * EPP;
@@ -401,33 +448,32 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
         }
     };
 
-    // one iteration: tile `it` (held in kr/vr) to LDS, tile it + PF into
-    // kr/vr, then tile `it` computed (the barrier counts are the same in every
-    // wave)
+    // One iteration: tile `it` (held in kr/vr) to LDS, tile it + 1 into
+    // kr/vr, the block ids of tile it + 2 requested, then tile `it` computed
+    // (the barrier counts are the same in every wave).
     // With one row group a token group is one wave, alone on its buffer: its
     // LDS accesses are performed in issue order, so no barrier is needed.
-    auto step = [&](int it, uint4 (&kr)[NLD], uint4 (&vr)[NLD]) {
+    int64_t bnext[2] = {0, 0};
+    if (nit > 0) {
+        tile_bases(kt0 + tg, bnext);
+        load_tile(kt0 + tg, bnext);
+    }
+    if (nit > 1) tile_bases(kt0 + tg + NT, bnext);
+    for (int it = 0; it < nit; ++it) {
         const int kt = kt0 + it * NT + tg;
         if constexpr (NR > 1) __syncthreads();        // the previous tile's reads are done
         store_tile(kr, vr);
         if constexpr (NR > 1) __syncthreads();
-        if (it + PF < nit) load_tile(kt + PF * NT, kr, vr);
+        if (it + 1 < nit) {
+            load_tile(kt + NT, bnext);
+            if (it + 2 < nit) tile_bases(kt + 2 * NT, bnext);
+        }
         if (kt < nkt) {
             if (kt * TK + TK - 1 > p_first)
                 compute(kt, std::true_type{});
             else
                 compute(kt, std::false_type{});
         }
-    };
-    if (nit > 0) load_tile(kt0 + tg, kr0, vr0);
-    if constexpr (PF == 2) {
-        if (nit > 1) load_tile(kt0 + tg + NT, kr1, vr1);
-        for (int it = 0; it < nit; it += 2) {
-            step(it, kr0, vr0);
-            if (it + 1 < nit) step(it + 1, kr1, vr1);
-        }
-    } else {
-        for (int it = 0; it < nit; ++it) step(it, kr0, vr0);
     }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
