@@ -86,8 +86,14 @@ __device__ __forceinline__ void i8_to_bf16(uint4 v, uint4& lo, uint4& hi) {
     hi = make_uint4(o[4], o[5], o[6], o[7]);
 }
 
-// Batches of at most this many sequences are placed by length (snake_seq).
+// Batches of at most this many sequences are placed by length (snake_place).
 constexpr int kSnakeMax = 256;
+
+// A workgroup's sequence, its first query row, its number of query rows and
+// its context length.
+struct SeqPlace {
+    int s, q0, n, L;
+};
 
 // The sequence that takes place p of the XCD-contiguous sequence list when
 // the places are dealt by length: the sequences ranked by context length
@@ -95,11 +101,14 @@ constexpr int kSnakeMax = 256;
 // snake (ranks 0-7 to XCDs 0-7, ranks 8-15 to XCDs 7-0, ...), each run
 // longest first. Every XCD then gets about the same share of the KV, and the
 // longest contexts start first. S = 8 runs of S / 8 places, S <= blockDim.x;
-// all threads of the workgroup call it (it has barriers). sh: S + 1 ints of
-// LDS, free again on return.
-__device__ int snake_seq(const int32_t* lens, int S, int p, int* sh) {
+// all threads of the workgroup call it (it has barriers). The lengths and
+// query starts are read once, into LDS (sh: 2 S + 2 ints, free again on
+// return), and the sequence's own values are taken from there.
+__device__ SeqPlace snake_place(const int32_t* lens, const int32_t* qsl, int S, int p, int* sh) {
     const int t = threadIdx.x;
+    int* shq = sh + S;                                // S + 1 query starts
     if (t < S) sh[t] = lens[t];
+    for (int i = t; i <= S; i += blockDim.x) shq[i] = qsl[i];
     __syncthreads();
     const int per = S / 8, x = p / per, j = p % per;
     const int r = 8 * j + ((j & 1) ? 7 - x : x);
@@ -110,12 +119,16 @@ __device__ int snake_seq(const int32_t* lens, int S, int p, int* sh) {
             const int Lu = sh[u];
             rank += (Lu > Lt) || (Lu == Lt && u < t);
         }
-        if (rank == r) sh[S] = t;                     // ranks are a permutation of 0..S-1
+        if (rank == r) sh[2 * S + 1] = t;             // ranks are a permutation of 0..S-1
     }
     __syncthreads();
-    const int seq = sh[S];
+    SeqPlace sp;
+    sp.s = sh[2 * S + 1];
+    sp.q0 = shq[sp.s];
+    sp.n = shq[sp.s + 1] - sp.q0;
+    sp.L = sh[sp.s];
     __syncthreads();
-    return seq;
+    return sp;
 }
 
 // WR: the kernel also writes the new tokens (bf16 caches)
@@ -144,30 +157,40 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     // tiles of a block are neighbours in the pool. (Spreading the kv heads
     // over the XCDs, which evens out the XCDs' shares of the KV, was 4-5%
     // slower on the 64-sequence batch, with or without rotating the heads.)
-    // Split-K with one row tile: the logical index itself, which spreads the
-    // partitions of a (sequence, kv head) over the XCDs: 1-3% faster on the
-    // long-context decode and verify passes.
+    // Split-K with one row tile: the logical index itself, with the partition
+    // index rotated by the (sequence, kv head) index. The partitions of a
+    // (sequence, kv head) then spread over the XCDs, and so do the first
+    // partitions of the different sequences, which mixed lengths make the
+    // busiest (copy-on-write batch, 1024-token partitions: 390 us with the
+    // XCD-contiguous order, 280 us rotated, 878 us unrotated, where XCD j
+    // took every partition j, j + 8, ...).
     const int W = gridDim.x, w0 = blockIdx.x;
     const bool spread = a.row_tiles == 1 && a.num_partitions > 1;
     const int w = (W % 8 || spread) ? w0 : (w0 % 8) * (W / 8) + w0 / 8;
     const int NP = a.num_partitions;                  // 1 without split-K
     const int rt = w % a.row_tiles, rest = w / a.row_tiles;
-    const int part = rest % NP, sg = rest / NP;
+    const int sg = rest / NP, part = spread ? (rest + sg) % NP : rest % NP;
     const int g = sg % Hkv;
-    // one row tile, no split: the sequences are placed by length (snake_seq)
-    const int s = (a.row_tiles == 1 && NP == 1 && W % 8 == 0 && a.num_seqs % 8 == 0 &&
-                   a.num_seqs <= kSnakeMax)
-                      ? snake_seq(a.context_lens, a.num_seqs, sg / Hkv, reinterpret_cast<int*>(lds))
-                      : sg / Hkv;
+    // one row tile, no split: the sequences are placed by length (snake_place)
+    static_assert((2 * kSnakeMax + 2) * 4 <= NT * TGBYTES, "placement scratch fits the LDS");
+    SeqPlace sp;
+    if (a.row_tiles == 1 && NP == 1 && W % 8 == 0 && a.num_seqs % 8 == 0 &&
+        a.num_seqs <= kSnakeMax) {
+        sp = snake_place(a.context_lens, a.query_start_loc, a.num_seqs, sg / Hkv,
+                         reinterpret_cast<int*>(lds));
+    } else {
+        sp.s = sg / Hkv;
+        sp.q0 = ld_const(a.query_start_loc, sp.s);
+        sp.n = ld_const(a.query_start_loc, sp.s + 1) - sp.q0;
+        sp.L = ld_const(a.context_lens, sp.s);
+    }
+    const int s = sp.s, q0 = sp.q0, n = sp.n, L = sp.L;
     const int G = Hq / Hkv;
-    const int q0 = ld_const(a.query_start_loc, s);
-    const int n = ld_const(a.query_start_loc, s + 1) - q0;
     const int tiles = (n * G + RT - 1) / RT;
     if (rt >= tiles) return;
     const int tile = tiles - 1 - rt;                  // the tiles with the longest context first
     const int TQ = RT / G;                            // query tokens per tile (G divides 16)
     const int tok0 = tile * TQ;
-    const int L = ld_const(a.context_lens, s);
     const int p_first = L - n + tok0;                 // position of the tile's first new token
     const int limit = p_first + min(TQ, n - tok0);    // the tile reads tokens [0, limit)
     // split-K: this workgroup takes the tokens [t_begin, min(t_begin + P, limit));
@@ -280,11 +303,13 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
                                             : (t < 16 ? base[0] : base[1]);
             if constexpr (WR) {
                 // a new token's row comes from key / value (its slot is being
-                // written by this launch)
+                // written by this launch). A tile wholly past the context (the
+                // last iteration's spare waves) has jn >= n and reads block 0
+                // of the cache instead, like the other instances.
                 const int jn = kt * TK + (in ? t : 0) - new0;
                 const char* kp = reinterpret_cast<const char*>(a.k_cache) + bb + lo;
                 const char* vp = reinterpret_cast<const char*>(a.v_cache) + bb + lo;
-                if (jn >= 0) {
+                if (jn >= 0 && jn < n) {
                     const int64_t src = (((int64_t)q0 + jn) * Hkv + g) * PD + e;
                     kp = reinterpret_cast<const char*>(a.key) + src * 2;
                     vp = reinterpret_cast<const char*>(a.value) + src * 2;

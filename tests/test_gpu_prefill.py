@@ -43,6 +43,15 @@ CASES = {
     "cow_g8": (synth.CONFIGS[5].replace(num_seqs=16, lens=("lognormal", 200, 1.0, 1, 1500),
                                         max_len=1500, prefix_groups=2, prefix_tokens=256),
                ("uniform", 1, 5)),
+    # one row per sequence, no split: up to 256 sequences (a multiple of 8) are
+    # placed on the XCDs by context length; many equal lengths at 64, the
+    # largest batch placed so at 256, the plain order at 264
+    "decode_ties_s64": (synth.CONFIGS[2].replace(num_seqs=64, lens=("uniform", 1, 40),
+                                                 max_len=40), ("const", 1)),
+    "decode_s256": (synth.CONFIGS[2].replace(num_seqs=256, lens=("uniform", 1, 300),
+                                             max_len=300), ("const", 1)),
+    "decode_s264": (synth.CONFIGS[2].replace(num_seqs=264, lens=("uniform", 1, 300),
+                                             max_len=300), ("const", 1)),
 }
 
 
@@ -212,6 +221,7 @@ def new_token_rows(case, qs):
 # never in a shared prefix block there, as in a real copy-on-write pool)
 @pytest.mark.parametrize("name,P", [("verify_g4", 0), ("verify_g8_b32", 0), ("mixed_g4", 0),
                                     ("chunk_g4", 0), ("whole_mha", 0), ("cow_g8", 0),
+                                    ("decode_ties_s64", 0), ("decode_s256", 0),
                                     ("verify_g4", 64), ("chunk_g4", 256), ("cow_g8", 512)])
 def test_write_prefill_parity(name, P):
     """One launch writes the new tokens and attends: the pool afterwards is
