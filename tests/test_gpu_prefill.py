@@ -175,6 +175,56 @@ def test_prefill_no_rows():
 
 
 @pytest.mark.timeout(600)
+@pytest.mark.parametrize("cfg,P", [(2, 0), (3, 2048)])
+def test_default_step_full_size_sampled(cfg, P):
+    """The default decode step of the Llama-shaped batch (one pass) and of the
+    long contexts (2048-token partitions, then the reduce) at full size, in the
+    launch configuration the bench times: pa_write_prefill with one query row
+    per sequence writes the new tokens (their slots hold poison before) and
+    attends. The pool is byte-identical to the oracle's; sampled sequences
+    (every head and dim) are checked against the oracle's decode."""
+    from gpu_helpers import poison_pool
+    spec = synth.CONFIGS[cfg]
+    print(f"[default step] cfg{cfg} P={P}: generating", flush=True)
+    case = synth.make_case(spec, cfg)
+    dc = to_device(case)
+    k, v = poison_pool(case)
+    if dc.pre_slots.numel():
+        pa.write_kv_cache(dc.pre_key, dc.pre_value, k, v, dc.pre_slots, dc.k_scale, dc.v_scale)
+    qsl = torch.arange(case.S + 1, dtype=torch.int32, device="cuda")
+    out = torch.full_like(dc.q, float("nan"))
+    maxL = case.max_context_len
+    print(f"[default step] cfg{cfg} P={P}: gpu", flush=True)
+    if P:
+        ws = pa.prefill_workspace(case.S, case.Hq, case.D, maxL, P, "cuda")
+        pa.write_prefill(dc.key, dc.value, dc.slot_mapping, None, dc.q, k, v, dc.block_tables,
+                         dc.context_lens, qsl, float(case.scale), 1, maxL, partition_size=P,
+                         tmp_out=ws[0], tmp_max=ws[1], tmp_sum=ws[2], row_lens=ws[3])
+        pa.decode_splitk_reduce(out, ws[0], ws[1], ws[2], ws[3], maxL, P)
+    else:
+        pa.write_prefill(dc.key, dc.value, dc.slot_mapping, out, dc.q, k, v, dc.block_tables,
+                         dc.context_lens, qsl, float(case.scale), 1, maxL)
+    torch.cuda.synchronize()
+    got = as_f64(out)
+    assert np.isfinite(got).all()
+    from gpu_helpers import dev_to_host
+    ok, ov = oracle.fill_cache(case)
+    assert np.array_equal(dev_to_host(k).view(np.uint8), ok.view(np.uint8)), "K pool differs"
+    assert np.array_equal(dev_to_host(v).view(np.uint8), ov.view(np.uint8)), "V pool differs"
+    L = case.context_lens
+    rng = np.random.default_rng(cfg)
+    seqs = sorted({int(np.argmax(L)), int(np.argmin(L)), 0, case.S - 1,
+                   *[int(x) for x in rng.choice(case.S, size=2, replace=False)]})
+    if cfg == 3:
+        seqs = seqs[:2]
+    print(f"[default step] cfg{cfg} P={P}: oracle on sequences {seqs}", flush=True)
+    ref = oracle.decode_case(case, ok, ov, seqs=seqs)
+    err = np.abs(got[seqs] - ref).max()
+    print(f"[default step] cfg{cfg} P={P}: max err {err:.3e}", flush=True)
+    assert err <= tol(case)
+
+
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("name", ["verify", "prefill", "verify_long"])
 def test_prefill_full_size_sampled(name):
     spec, ql = synth.MULTI_QUERY[name]
