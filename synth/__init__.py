@@ -415,6 +415,27 @@ class Queries:
         return int(self.query_start_loc[-1])
 
 
+def query_counts(context_lens: np.ndarray, q_lens, rng: np.random.Generator) -> np.ndarray:
+    """Per-sequence query-row counts n_s (int64 [S]) for ``make_queries``:
+    ("const", n), ("uniform", lo, hi) (inclusive, drawn from ``rng``) or a
+    sequence of counts, each clipped to [0, L_s]."""
+    L = np.asarray(context_lens).astype(np.int64)
+    S = L.shape[0]
+    if isinstance(q_lens, tuple) and q_lens[0] == "const":
+        n = np.full(S, int(q_lens[1]), dtype=np.int64)
+    elif isinstance(q_lens, tuple) and q_lens[0] == "uniform":
+        n = rng.integers(q_lens[1], q_lens[2] + 1, size=S).astype(np.int64)
+    else:
+        n = np.asarray(q_lens, dtype=np.int64).reshape(S)
+    return np.clip(n, 0, L)
+
+
+def draw_lens(spec: Spec, seed: int) -> np.ndarray:
+    """The context lengths ``make_case(spec, seed)`` draws (its first draw),
+    without building the batch."""
+    return _draw_lens(spec, np.random.default_rng(seed))
+
+
 def make_queries(case: Case, q_lens, seed: int) -> Queries:
     """Queries for a multi-token step over ``case``'s cache.
 
@@ -422,14 +443,8 @@ def make_queries(case: Case, q_lens, seed: int) -> Queries:
     of per-sequence counts; each count is clipped to [0, L_s]. Q ~ N(0, 1)
     times the spec's q_std, cast to the activation dtype."""
     rng = np.random.default_rng(seed)
-    S, L = case.S, case.context_lens.astype(np.int64)
-    if isinstance(q_lens, tuple) and q_lens[0] == "const":
-        n = np.full(S, int(q_lens[1]), dtype=np.int64)
-    elif isinstance(q_lens, tuple) and q_lens[0] == "uniform":
-        n = rng.integers(q_lens[1], q_lens[2] + 1, size=S).astype(np.int64)
-    else:
-        n = np.asarray(q_lens, dtype=np.int64).reshape(S)
-    n = np.clip(n, 0, L)
+    S = case.S
+    n = query_counts(case.context_lens, q_lens, rng)
     qsl = np.zeros(S + 1, dtype=np.int32)
     qsl[1:] = np.cumsum(n)
     q32 = rng.standard_normal((int(qsl[-1]), case.Hq, case.D), dtype=np.float32)
