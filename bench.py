@@ -13,9 +13,12 @@ every context. Schedules (--schedule):
   partitions: pa_write_kv_cache, pa_decode over fixed partitions, then
     pa_decode_splitk_reduce;
   auto (default): the fastest measured one for the workload (AUTO_SCHEDULE).
-Default workload: the Llama-3-8B-shaped bf16 GQA batch (64 sequences,
-context lengths U[128, 2048], 32 query / 8 kv heads, head_dim 128, block 16,
-shuffled pool sized 1.25x the need), on the multi-query schedule.
+Default workload: the largest of the five, the mixed batch with copy-on-write
+shared prefixes (256 sequences, lognormal context lengths with median 1024
+clipped to [16, 16384], 64 query / 8 kv heads, head_dim 128, block 32, bf16, four
+groups of 64 sequences sharing a 1024-token prefix), on its default schedule;
+--config 2/3/4 select the Llama-3-8B-shaped batch, the long contexts and the
+int8 cache.
 
 The KV pool is replicated R times (R x pool >= 2 GB, far above the 256 MB
 last-level cache) and step i uses copy i mod R, so every step streams its KV
@@ -104,9 +107,48 @@ def measured_traffic(cfg: int, partition: int, schedule: str):
     return ent.get("bytes_per_launch")
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def sample_bytes(case, seqs, np):
+    """Algorithmic bytes of decoding sequences ``seqs`` alone: their unique
+    physical in-context tokens' K/V, Q, output, block-table entries, lengths and
+    int8 scales (the whole-batch count of synth.traffic, restricted)."""
+    import synth
+    B, Hkv, D = case.B, case.Hkv, case.D
+    ce, ae = synth.elt_bytes(case.spec.cache), synth.elt_bytes(case.spec.act)
+    slots, blocks = [], []
+    for s in seqs:
+        L = int(case.context_lens[s])
+        p = np.arange(L)
+        slots.append(case.block_tables[s, p // B].astype(np.int64) * B + p % B)
+        blocks.append(case.block_tables[s, :(L + B - 1) // B])
+    uniq = int(np.unique(np.concatenate(slots)).size)
+    nblk = sum(len(b) for b in blocks)
+    scales = (int(np.unique(np.concatenate(blocks)).size) * Hkv * 2 * 4
+              if case.spec.cache == "i8" else 0)
+    return uniq * 2 * Hkv * D * ce + 2 * len(seqs) * case.Hq * D * ae + 4 * nblk \
+        + 4 * len(seqs) + scales
+
+
 def cpu_baseline(case, budget_s: float):
-    """The fp64 oracle (write + decode) on this host's cores, repeated until
-    about `budget_s` seconds of work; bytes/s on the same algorithmic count."""
+    """The fp64 oracle on this host's cores, in the bench line's unit (GB/s on
+    the same algorithmic byte count).
+
+    All cores: write + decode of the whole batch, repeated until about
+    ``budget_s`` seconds of work. One thread: decode of the first sequences
+    (index order, about 1/8 of the batch's tokens, at least one sequence)
+    repeated for about ``budget_s / 2`` seconds."""
+    import numpy as np
+
     import oracle
     import synth
     k, v = oracle.fill_cache(case)
@@ -121,10 +163,31 @@ def cpu_baseline(case, budget_s: float):
         el = time.perf_counter() - t0
         if el >= budget_s or reps >= 1000:
             break
-    return {"value": round(nbytes * reps / el / 1e9, 4), "unit": "GB/s",
-            "cores": oracle.num_threads(), "kind": "oracle",
+    cores = oracle.num_threads()
+    L = case.context_lens.astype(np.int64)
+    n1 = max(1, int(np.searchsorted(np.cumsum(L), L.sum() / 8)))
+    seqs = list(range(min(case.S, n1)))
+    b1 = sample_bytes(case, seqs, np)
+    oracle.set_num_threads(1)
+    try:
+        r1, t1 = 0, time.perf_counter()
+        while True:
+            oracle.decode_case(case, k, v, seqs=seqs)
+            r1 += 1
+            e1 = time.perf_counter() - t1
+            if e1 >= budget_s / 2 or r1 >= 1000:
+                break
+    finally:
+        oracle.set_num_threads(cores)
+    return {"value": round(nbytes * reps / el / 1e9, 4), "unit": "GB/s", "cores": cores,
+            "kind": "oracle",
             "sample": f"the whole batch (all {case.S} sequences), write + decode, "
-                      f"{reps} repetitions in {el:.1f} s, fp64"}
+                      f"{reps} repetitions in {el:.1f} s, fp64",
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
+            "one_thread": {"value": round(b1 * r1 / e1 / 1e9, 4), "unit": "GB/s", "cores": 1,
+                           "sample": f"decode of sequences 0..{len(seqs) - 1} "
+                                     f"({int(L[seqs].sum())} context tokens), {r1} repetitions "
+                                     f"in {e1:.1f} s, fp64"}}
 
 
 def bench_copy_blocks(args, spec, torch, np, pa, synth):
@@ -345,7 +408,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--config", type=int, default=5, choices=[1, 2, 3, 4, 5],
+                    help="workload (default 5: the largest, the mixed batch with copy-on-write prefixes)")
     ap.add_argument("--partition", type=int, default=None,
                     help="split-K partition (default: the workload's), or the smallest "
                          f"balanced piece in tokens (default {BALANCED_MIN_PIECE})")

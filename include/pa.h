@@ -18,7 +18,9 @@
  *      Connections; "Llama forward -> Paged decode attention", "How
  *      brave30/mini-inference-engine works", Connections);
  *   3. for long contexts, splits each sequence's context into partitions and
- *      combines the per-partition results with a log-sum-exp reduce.
+ *      combines the per-partition results with a log-sum-exp reduce (not on
+ *      the pages: the flash-decoding split-K of the decode step's
+ *      specification; see pa_decode_splitk_reduce).
  *
  * Math of step 2, for sequence s, query head h, kv head g = h / (Hq / Hkv):
  *   x_t   = scale * sum_d q[s,h,d] * k_t[d]          t = 0 .. L_s - 1
@@ -293,8 +295,10 @@ int pa_copy_blocks(void *k_cache, void *v_cache, float *k_scale, float *v_scale,
  *                   partition_size): caller-owned workspace, required iff
  *                   partition_size > 0 (and num_query_tokens > 0).
  * Precision: Q K^T and P V run on bf16 MFMAs with fp32 accumulation; the
- * softmax weights are rounded to bf16 for the P V product (the row sums use
- * the fp32 weights).
+ * softmax weights are rounded to bf16 for the P V product, and each row's sum
+ * is the sum of those same bf16 weights. int8 caches: codes convert exactly to
+ * bf16; the K scale multiplies the logits and the V scale multiplies, in fp32,
+ * the P V product of the 16 tokens of its block.
  * Supported instances (others return PA_ERR_UNSUPPORTED): q BF16; cache BF16 or
  * I8; head_dim 128; block_size 16 or 32; group size Hq / Hkv in {1, 2, 4, 8, 16}.
  * num_seqs and num_kv_heads <= 65535. num_query_tokens = 0 does nothing (q and out
@@ -315,11 +319,13 @@ int pa_prefill(void *out, const void *q, const void *k_cache, const void *v_cach
  * pa_prefill, in one launch. Row r = qsl[s] + j of key and value (the layout of
  * q: [num_query_tokens][num_kv_heads][head_dim], q_dtype) is new token j of
  * sequence s, at position L_s - n_s + j, and goes to slot slot_mapping[r]
- * (int64; negative: not written). The kernel reads those positions from key
+ * (int64). The kernel reads the positions of tokens with a slot >= 0 from key
  * and value, never from the cache, and stores them to their slots, so the
- * cache holds them afterwards exactly as after pa_write_kv_cache, and the
- * result equals pa_write_kv_cache then pa_prefill. context_lens counts the
- * new tokens. Other arguments and the split-K option as in pa_prefill.
+ * cache holds them afterwards exactly as after pa_write_kv_cache. A token with
+ * a negative slot is not written, and its position is read from the cache as
+ * it stands. Result and pool are therefore bit-identical to pa_write_kv_cache
+ * followed by pa_prefill. context_lens counts the new tokens. Other arguments
+ * and the split-K option as in pa_prefill.
  * Supported: bf16 q and cache (an int8 cache returns PA_ERR_UNSUPPORTED; use
  * pa_write_kv_cache then pa_prefill). key and value 16-byte aligned; PA_CHECK=1
  * also verifies each slot against its position.
@@ -340,6 +346,11 @@ int pa_balanced_slots(int max_context_len, int min_piece_tokens);
 
 /*
  * pa_decode_splitk_reduce -- log-sum-exp combination of split-K partials.
+ * The pages define no long-context split: the partition of each context into
+ * fixed-size pieces and this exact combination of their (normalised output,
+ * max, sum) triples are the flash-decoding split-K that the decode step's
+ * specification adds for long contexts; the formula is the merge of two
+ * softmax states over disjoint token sets, applied to all of them at once.
  * For each (s, h), over j < n = ceil(L_s / partition_size):
  *   M = max_j tmp_max[j], W_j = tmp_sum[j] * exp(tmp_max[j] - M),
  *   out[s][h][:] = sum_j W_j tmp_out[j][:] / sum_j W_j      (0 when n = 0),

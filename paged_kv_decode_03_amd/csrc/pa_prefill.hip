@@ -252,8 +252,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
 
     float m[MB], l[MB];
     f32x4 o[MB][8];
-    // bf16 caches: row sums of the bf16 weights by an MFMA against ones (the
-    // same weights the P V product uses); every element holds the row's sum
+    // row sums of the bf16 weights by an MFMA against ones (the same weights
+    // the P V product uses); every element holds the row's sum
     f32x4 lsum[MB];
     const bf16x8 ones = as_bf16x8(make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
 #pragma unroll
@@ -291,6 +291,18 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
                 ? (int64_t)ld_uniform(bt, (kt * TK + 16 * hf) / B) * blk_stride + head_off : 0;
     };
     auto load_tile = [&](int kt, const int64_t (&base)[2]) {
+        // WR: bit t set when token kt TK + t is a new token with a negative
+        // slot: it is not written, so its position is read from the cache
+        // like any other (scalar loads, only for tiles that hold new tokens)
+        uint32_t negm = 0;
+        if constexpr (WR) {
+            const int j0 = kt * TK - new0;            // new-token index of the tile's token 0
+            if (j0 + TK > 0 && j0 < n) {
+                const int tb = max(0, -j0), te = min(TK, n - j0);
+                for (int t = tb; t < te; ++t)
+                    if (ld_uniform(a.slot_mapping, (int64_t)q0 + j0 + t) < 0) negm |= 1u << t;
+            }
+        }
 #pragma unroll
         for (int k = 0; k < NLD; ++k) {
             const int p = ti + k * TPT, t = p / PPR, e = (p % PPR) * EPP;
@@ -306,10 +318,11 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
                 // written by this launch). A tile wholly past the context (the
                 // last iteration's spare waves) has jn >= n and reads block 0
                 // of the cache instead, like the other instances.
-                const int jn = kt * TK + (in ? t : 0) - new0;
+                const int tt = in ? t : 0;
+                const int jn = kt * TK + tt - new0;
                 const char* kp = reinterpret_cast<const char*>(a.k_cache) + bb + lo;
                 const char* vp = reinterpret_cast<const char*>(a.v_cache) + bb + lo;
-                if (jn >= 0 && jn < n) {
+                if (jn >= 0 && jn < n && !((negm >> tt) & 1u)) {
                     const int64_t src = (((int64_t)q0 + jn) * Hkv + g) * PD + e;
                     kp = reinterpret_cast<const char*>(a.key) + src * 2;
                     vp = reinterpret_cast<const char*>(a.value) + src * 2;
@@ -443,33 +456,52 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
                 const float mu = mn == -__builtin_huge_valf() ? 0.0f : mn;
                 const float alpha = __builtin_amdgcn_exp2f(m[mb] - mu);
                 m[mb] = mn;
-                l[mb] *= alpha;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) lsum[mb][i] *= alpha;
 #pragma unroll
                 for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) o[mb][dt][i] *= alpha;
             }
             const float mu = m[mb] == -__builtin_huge_valf() ? 0.0f : m[mb];
-            float sum = 0.0f;
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float pr = __builtin_amdgcn_exp2f(x[tt][i] - mu);
-                    sum += pr;
-                    pop[mb][4 * tt + i] = (__bf16)(I8 ? pr * vsc[tt] : pr);
-                }
-            l[mb] += sum;
+                for (int i = 0; i < 4; ++i)
+                    pop[mb][4 * tt + i] = (__bf16)__builtin_amdgcn_exp2f(x[tt][i] - mu);
+            lsum[mb] = mfma16x16x32(ones, pop[mb], lsum[mb]);
           }
         }
-        // O^T += V^T P^T, each V^T operand read right before its MFMAs
+        // O^T += V^T P^T, each V^T operand read right before its MFMAs. The k
+        // slots 0-3 of a lane are tokens of the tile's first 16-token half and
+        // slots 4-7 of its second, so on an int8 cache the product splits into
+        // two 16x16x16 MFMAs, one per half (one block each), whose results are
+        // scaled by that block's V scale in fp32.
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
             const uint2 x0 = ds_read_tr16(vl + vtr + 32 * dt);
             const uint2 x1 = ds_read_tr16(vl + vtr + 16 * KSTR + 32 * dt);
-            const bf16x8 vop = as_bf16x8(make_uint4(x0.x, x0.y, x1.x, x1.y));
+            if constexpr (!I8) {
+                const bf16x8 vop = as_bf16x8(make_uint4(x0.x, x0.y, x1.x, x1.y));
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb) o[mb][dt] = mfma16x16x32(vop, pop[mb], o[mb][dt]);
+                for (int mb = 0; mb < MB; ++mb) o[mb][dt] = mfma16x16x32(vop, pop[mb], o[mb][dt]);
+            } else {
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) {
+                    const i16x4v p0 = __builtin_bit_cast(i16x4v, __builtin_shufflevector(
+                        pop[mb], pop[mb], 0, 1, 2, 3));
+                    const i16x4v p1 = __builtin_bit_cast(i16x4v, __builtin_shufflevector(
+                        pop[mb], pop[mb], 4, 5, 6, 7));
+                    const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+                    const f32x4 t0 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+                        __builtin_bit_cast(i16x4v, x0), p0, zero, 0, 0, 0);
+                    const f32x4 t1 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+                        __builtin_bit_cast(i16x4v, x1), p1, zero, 0, 0, 0);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        o[mb][dt][i] = fmaf(vsc[1], t1[i], fmaf(vsc[0], t0[i], o[mb][dt][i]));
+                }
+            }
         }
     };
 
@@ -501,14 +533,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
         }
     }
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-        if constexpr (I8) {
-            l[mb] += lane_xor16(l[mb]);
-            l[mb] += lane_xor32(l[mb]);
-        } else {
-            l[mb] = lsum[mb][0];                      // already the whole row's sum
-        }
-    }
+    for (int mb = 0; mb < MB; ++mb) l[mb] = lsum[mb][0];   // already the whole row's sum
 
     if (NT > 1) {
         // token groups 1 .. NT-1 hand their states to token group 0 of their row group

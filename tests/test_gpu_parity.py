@@ -8,7 +8,6 @@ Small cases span several 16-token chunks, several partitions and a ragged
 tail; the full-size workloads run in the bench's launch configuration and are
 checked on sampled sequences (every head and dim of those sequences).
 """
-import dataclasses
 import os
 
 import numpy as np
@@ -18,6 +17,7 @@ import torch
 import oracle
 import pins
 import synth
+from probe_cases import onehot_case
 from gpu_helpers import (TORCH_DT, as_f64, dev_to_host, fill_pool, host_to_dev, poison_pool,
                          run_decode, to_device, tol)
 
@@ -262,35 +262,7 @@ def test_reduce_from_oracle_partials():
 
 def _onehot_case(spec, seed, tstar_of):
     """q = 128 e_0, k_{t*} = 128 e_0, other k_0 = 0: the output is v_{t*} exactly."""
-    case = synth.make_case(spec, seed)
-    act = spec.act
-    idx, _, _ = pins.source_rows(case)
-    npre = len(case.pre_slots)
-    one = np.float32(128.0)
-    val = synth.bf16_bits(np.array([one]))[0] if act == "bf16" else one
-    zero = np.uint16(0) if act == "bf16" else np.float32(0)
-    pk, nk, q = case.pre_key.copy(), case.key.copy(), np.zeros_like(case.q)
-    pk[:, :, 0] = zero
-    nk[:, :, 0] = zero
-    q[:, :, 0] = val
-    ts = []
-    for s in range(case.S):
-        # probe only tokens in blocks this sequence owns alone: a probe in a
-        # shared copy-on-write block would be seen by the whole group
-        L = int(case.context_lens[s])
-        own = [t for t in range(L) if case.refcount[case.block_tables[s, t // case.B]] == 1]
-        t = own[tstar_of(s, len(own))]
-        ts.append(t)
-        slot = int(case.block_tables[s, t // case.B]) * case.B + t % case.B
-        r = idx[slot]
-        if r < npre:
-            pk[r, :, 0] = val
-        else:
-            nk[r - npre, :, 0] = val
-    new = dataclasses.replace(case, pre_key=pk, key=nk, q=q)
-    if spec.cache == "i8":
-        new.k_scale, new.v_scale = synth.absmax_scales(new)
-    return new, ts
+    return onehot_case(spec, seed, tstar_of)
 
 
 @pytest.mark.parametrize("name", ["cfg1", "cfg2s", "cfg4s", "cfg5s", "g2_bf16", "mha_i8_f32q"])
@@ -615,4 +587,82 @@ def test_write_decode_matches_two_calls(name):
         assert np.array_equal(dev_to_host(o), want)
     err = np.abs(as_f64(outs[0]) - ref).max()
     print(f"[fused] {name} max err {err:.3e}", flush=True)
+    assert err <= tol(case)
+
+
+@pytest.mark.parametrize("name", ["cfg2s", "cfg4s", "cfg5s", "g8_i8", "mid_g8_cow"])
+def test_write_decode_negative_slots_match_two_calls(name):
+    """New tokens with a negative slot are not written: the fused call stays
+    bit-identical (output and pool) to pa_write_kv_cache followed by
+    pa_decode_balanced, which reads whatever the cache holds at position L - 1."""
+    case, dc, ok, ov, ref = prepared(name)
+    P = 64
+    slots = dc.slot_mapping.clone()
+    slots[::3] = -1
+    k1, v1 = dc.k_cache.clone(), dc.v_cache.clone()
+    k2, v2 = dc.k_cache.clone(), dc.v_cache.clone()
+    for kk, vv in ((k1, v1), (k2, v2)):              # the cache differs from key / value
+        kk.view(torch.uint8 if case.spec.cache == "i8" else torch.int16).bitwise_xor_(1)
+        vv.view(torch.uint8 if case.spec.cache == "i8" else torch.int16).bitwise_xor_(1)
+    ws1 = pa.balanced_workspace(case.S, case.Hq, case.Hkv, case.D, case.max_context_len, P, "cuda")
+    ws2 = pa.balanced_workspace(case.S, case.Hq, case.Hkv, case.D, case.max_context_len, P, "cuda")
+    a = torch.empty_like(dc.q)
+    b = torch.empty_like(dc.q)
+    pa.write_decode_balanced(dc.key, dc.value, slots, a, dc.q, k1, v1, dc.block_tables,
+                             dc.context_lens, float(case.scale), case.max_context_len, P, *ws1,
+                             k_scale=dc.k_scale, v_scale=dc.v_scale)
+    pa.write_kv_cache(dc.key, dc.value, k2, v2, slots, dc.k_scale, dc.v_scale)
+    pa.decode_balanced(b, dc.q, k2, v2, dc.block_tables, dc.context_lens, float(case.scale),
+                       case.max_context_len, P, *ws2, k_scale=dc.k_scale, v_scale=dc.v_scale)
+    sync()
+    assert np.array_equal(dev_to_host(k1).view(np.uint8), dev_to_host(k2).view(np.uint8))
+    assert np.array_equal(dev_to_host(v1).view(np.uint8), dev_to_host(v2).view(np.uint8))
+    assert np.array_equal(dev_to_host(a), dev_to_host(b))
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("cfg", [4, 5])
+def test_default_balanced_step_full_size_sampled(cfg):
+    """The default decode step of the int8 batch and of the mixed copy-on-write
+    batch at full size, in the exact launch configuration the bench times:
+    pa_write_decode_balanced with pieces of >= 128 tokens writes every new token
+    (its slot holds poison before) and decodes in one launch. The pool is
+    byte-identical to the oracle's write; sampled sequences (every head and
+    dim) are within tolerance of the oracle's decode; a second step on the
+    same inputs is bit-identical and leaves the counters at zero."""
+    spec = C[cfg]
+    print(f"[default balanced] cfg{cfg}: generating", flush=True)
+    case = synth.make_case(spec, cfg)
+    dc = to_device(case)
+    k, v = poison_pool(case)
+    if dc.pre_slots.numel():
+        pa.write_kv_cache(dc.pre_key, dc.pre_value, k, v, dc.pre_slots, dc.k_scale, dc.v_scale)
+    P = 128
+    ws = pa.balanced_workspace(case.S, case.Hq, case.Hkv, case.D, case.max_context_len, P,
+                               "cuda")
+    outs = []
+    print(f"[default balanced] cfg{cfg}: gpu", flush=True)
+    for _ in range(2):
+        out = torch.full_like(dc.q, float("nan"))
+        pa.write_decode_balanced(dc.key, dc.value, dc.slot_mapping, out, dc.q, k, v,
+                                 dc.block_tables, dc.context_lens, float(case.scale),
+                                 case.max_context_len, P, *ws, k_scale=dc.k_scale,
+                                 v_scale=dc.v_scale)
+        outs.append(out)
+    sync()
+    assert int(ws[3].abs().sum()) == 0, "counters not reset"
+    assert np.array_equal(dev_to_host(outs[0]), dev_to_host(outs[1]))
+    got = as_f64(outs[0])
+    assert np.isfinite(got).all()
+    print(f"[default balanced] cfg{cfg}: oracle", flush=True)
+    ok, ov = oracle.fill_cache(case)
+    assert np.array_equal(dev_to_host(k).view(np.uint8), ok.view(np.uint8)), "K pool differs"
+    assert np.array_equal(dev_to_host(v).view(np.uint8), ov.view(np.uint8)), "V pool differs"
+    L = case.context_lens
+    rng = np.random.default_rng(cfg)
+    seqs = sorted({int(np.argmax(L)), int(np.argmin(L)), 0, case.S - 1,
+                   *[int(x) for x in rng.choice(case.S, size=4, replace=False)]})
+    ref = oracle.decode_case(case, ok, ov, seqs=seqs)
+    err = np.abs(got[seqs] - ref).max()
+    print(f"[default balanced] cfg{cfg}: seqs {seqs} max err {err:.3e}", flush=True)
     assert err <= tol(case)

@@ -384,3 +384,229 @@ def test_pa_check_rejects_bad_queries(monkeypatch):
                          dc.v_cache.clone(), dc.block_tables, dc.context_lens,
                          torch.from_numpy(good).cuda(), float(case.scale), 4, maxL)
     assert e.value.status == -7
+
+
+# ---- exactness: one-hot probes, L = 1, placement, negative slots ------------
+
+EXACT = {
+    # name: (spec, query rows per sequence); rows <= 16 per (seq, kv head): one
+    # row block (the decode and verify shape); more: two row blocks, 64-row
+    # and 128-row tiles
+    "g4_b16": (synth.CONFIGS[2].replace(num_seqs=12, lens=("uniform", 1, 900), max_len=900), 1),
+    "g4_b16_rows4": (synth.CONFIGS[2].replace(num_seqs=12, lens=("uniform", 1, 900),
+                                              max_len=900), 4),
+    "g8_b32_cow": (synth.CONFIGS[5].replace(num_seqs=16, lens=("lognormal", 200, 1.0, 1, 1500),
+                                            max_len=1500, prefix_groups=2, prefix_tokens=256), 1),
+    "g8_b32_cow_rows3": (synth.CONFIGS[5].replace(num_seqs=16,
+                                                  lens=("lognormal", 200, 1.0, 1, 1500),
+                                                  max_len=1500, prefix_groups=2,
+                                                  prefix_tokens=256), 3),
+    "g4_i8_b16": (synth.CONFIGS[4].replace(num_seqs=10, lens=("uniform", 1, 1300),
+                                           max_len=1300), 1),
+    "g4_i8_b16_rows4": (synth.CONFIGS[4].replace(num_seqs=10, lens=("uniform", 1, 1300),
+                                                 max_len=1300), 4),
+    "g2_i8_b32_rows6": (S_("G=2 int8 B=32", 6, ("uniform", 1, 700), 8, 4, 128, 32, act="bf16",
+                           cache="i8", max_len=700), 6),
+    "g1_rows20": (S_("MHA 20 rows", 4, ("uniform", 1, 500), 4, 4, 128, 16, act="bf16",
+                     cache="bf16", max_len=500), 20),
+    "g4_rows40": (S_("G=4 40 rows", 3, ("uniform", 40, 700), 8, 2, 128, 16, act="bf16",
+                     cache="bf16", max_len=700), 40),
+    "g8_i8_rows100": (S_("G=8 int8 100 rows", 2, ("uniform", 100, 600), 16, 2, 128, 32,
+                         act="bf16", cache="i8", max_len=600), 100),
+}
+
+
+def _onehot_prefill(name, seed, rng):
+    """One-hot batch with query rows: every row of sequence s (positions L - n ..
+    L - 1) sees its probe t* <= L - n, which lies in a block s owns alone. A
+    sequence whose private blocks start after L - rows takes fewer rows."""
+    from probe_cases import onehot_case, onehot_queries
+    spec, rows = EXACT[name]
+    base = synth.make_case(spec, seed)
+    L0 = base.context_lens.astype(np.int64)
+    n = np.minimum(rows, L0)
+    for s in range(base.S):
+        first_own = next(t for t in range(int(L0[s]))
+                         if base.refcount[base.block_tables[s, t // base.B]] == 1)
+        n[s] = max(1, min(n[s], L0[s] - first_own))
+    case, ts = onehot_case(spec, seed, lambda s, c: int(rng.integers(0, c)),
+                           max_pos=lambda s: int(L0[s] - n[s]))
+    return case, onehot_queries(case, n), ts
+
+
+def _onehot_want(case, qs, ts):
+    """Row-by-row expected output: v_{t*} of the row's sequence (int8: code x
+    scale as the oracle's write leaves it), repeated over the group's heads,
+    in fp32 then rounded to the q dtype."""
+    import pins
+    from gpu_helpers import TORCH_DT
+    if case.spec.cache == "i8":
+        ok, ov = oracle.fill_cache(case)
+        dense = pins.dense_kv(case, ok, ov)
+    else:
+        dense = pins.dense_kv(case)
+    G = case.Hq // case.Hkv
+    want = np.empty((qs.num_tokens, case.Hq, case.D), dtype=np.float64)
+    for s, t in enumerate(ts):
+        v = np.repeat(dense[s][1][t].astype(np.float32), G, axis=0)
+        vq = torch.from_numpy(v).to(TORCH_DT[case.spec.act]).double().numpy()
+        want[qs.query_start_loc[s]:qs.query_start_loc[s + 1]] = vq
+    return want
+
+
+@pytest.mark.parametrize("P", [0, 64])
+@pytest.mark.parametrize("name", list(EXACT))
+def test_prefill_onehot_bit_exact(name, P):
+    """Through shuffled block tables, every query row of every sequence sees its
+    sequence's probe token t* (placed at or before the first new token) and
+    returns v_{t*} bit for bit: the block-table lookup and the K/V gather are
+    exact, and the int8 path dequantises V exactly as the oracle does."""
+    rng = np.random.default_rng(17)
+    for rep in range(2):
+        case, qs, ts = _onehot_prefill(name, 60 + rep, rng)
+        print(f"[onehot prefill] {name} P={P} rep {rep}: {qs.num_tokens} rows", flush=True)
+        dc = to_device(case)
+        fill_pool(dc)
+        got = run_prefill(case, qs, dc, partition_size=P)
+        want = _onehot_want(case, qs, ts)
+        bad = np.argwhere(got != want)
+        assert bad.size == 0, f"{name} P={P}: first mismatch at row/head/dim {bad[0]}"
+
+
+@pytest.mark.parametrize("name", ["g4_b16", "g4_b16_rows4", "g8_b32_cow", "g8_b32_cow_rows3",
+                                  "g1_rows20", "g4_rows40"])
+def test_write_prefill_onehot_bit_exact(name):
+    """The fused write: the new tokens' slots hold poison before the call, t* may
+    be a new token (read from key / value), and the output is v_{t*} bit for
+    bit; the pool afterwards is byte-identical to the oracle's write."""
+    rng = np.random.default_rng(19)
+    case, qs, ts = _onehot_prefill(name, 70, rng)
+    ok, ov = oracle.fill_cache(case)
+    kn, vn, slots = new_token_rows(case, qs)
+    kp, vp = ok.copy(), ov.copy()
+    for arr in (kp, vp):
+        arr.reshape(case.num_blocks, case.Hkv, case.B, case.D)[
+            slots // case.B, :, slots % case.B, :] = synth.BF16_POISON
+    k = host_to_dev(kp, "bf16", "cuda")
+    v = host_to_dev(vp, "bf16", "cuda")
+    dc = to_device(case)
+    q = host_to_dev(qs.q, "bf16", "cuda")
+    qsl = torch.from_numpy(qs.query_start_loc).cuda()
+    out = torch.full_like(q, float("nan"))
+    pa.write_prefill(host_to_dev(kn, "bf16", "cuda"), host_to_dev(vn, "bf16", "cuda"),
+                     torch.from_numpy(slots).cuda(), out, q, k, v, dc.block_tables,
+                     dc.context_lens, qsl, float(case.scale), int(qs.q_lens.max()),
+                     case.max_context_len)
+    torch.cuda.synchronize()
+    from gpu_helpers import dev_to_host
+    assert np.array_equal(dev_to_host(k).view(np.uint8), ok.view(np.uint8)), "K pool differs"
+    assert np.array_equal(dev_to_host(v).view(np.uint8), ov.view(np.uint8)), "V pool differs"
+    assert np.array_equal(as_f64(out), _onehot_want(case, qs, ts))
+
+
+@pytest.mark.parametrize("cache", ["bf16", "i8"])
+@pytest.mark.parametrize("P", [0, 32])
+def test_prefill_context_len_one_returns_v(cache, P):
+    """Every context is the new token alone: the output is its V row exactly
+    (int8: its codes times the block's V scale, in fp32, then rounded)."""
+    spec = synth.CONFIGS[2 if cache == "bf16" else 4].replace(
+        num_seqs=24, lens=("const", 1), max_len=16)
+    case = synth.make_case(spec, 9)
+    qs = synth.Queries(query_start_loc=np.arange(case.S + 1, dtype=np.int32), q=case.q,
+                       q_lens=np.ones(case.S, dtype=np.int64))
+    dc = to_device(case)
+    fill_pool(dc)
+    got = run_prefill(case, qs, dc, partition_size=P)
+    assert np.array_equal(got, _onehot_want(case, qs, [0] * case.S))
+
+
+def test_write_prefill_context_len_one_returns_v():
+    spec = synth.CONFIGS[5].replace(num_seqs=32, lens=("const", 1), max_len=32,
+                                    prefix_groups=0, prefix_tokens=0)
+    case = synth.make_case(spec, 10)
+    from gpu_helpers import poison_pool, dev_to_host
+    dc = to_device(case)
+    k, v = poison_pool(case)
+    qsl = torch.arange(case.S + 1, dtype=torch.int32, device="cuda")
+    out = torch.full_like(dc.q, float("nan"))
+    pa.write_prefill(dc.key, dc.value, dc.slot_mapping, out, dc.q, k, v, dc.block_tables,
+                     dc.context_lens, qsl, float(case.scale), 1, case.max_context_len)
+    torch.cuda.synchronize()
+    G = case.Hq // case.Hkv
+    assert np.array_equal(dev_to_host(out), np.repeat(case.value, G, axis=1))
+    ok, ov = oracle.fill_cache(case)
+    assert np.array_equal(dev_to_host(k).view(np.uint8), ok.view(np.uint8))
+
+
+@pytest.mark.parametrize("name", ["g4_b16", "g4_b16_rows4", "g8_b32_cow_rows3", "g4_i8_b16_rows4",
+                                  "g4_rows40"])
+def test_prefill_placement_bit_identical(name):
+    """Renaming the physical blocks, and un-sharing copy-on-write prefixes, leave
+    the output bit-identical, in one pass and split over 64-token partitions
+    (the arithmetic order depends only on logical positions)."""
+    spec, rows = EXACT[name]
+    case = synth.make_case(spec, 80)
+    qs = synth.make_queries(case, ("const", rows), 81)
+    variants = [synth.permute_placement(case, 82), synth.permute_placement(case, 83)]
+    if spec.prefix_groups:
+        variants.append(synth.unshare_prefixes(case))
+    base = []
+    dc = to_device(case)
+    fill_pool(dc)
+    for P in (0, 64):
+        base.append(run_prefill(case, qs, dc, partition_size=P))
+    for var in variants:
+        dv = to_device(var)
+        fill_pool(dv)
+        for P, b in zip((0, 64), base):
+            assert np.array_equal(run_prefill(var, qs, dv, partition_size=P), b), f"P={P}"
+
+
+@pytest.mark.parametrize("name", ["verify_g4", "mixed_g4", "cow_g8", "decode_ties_s64"])
+def test_write_prefill_negative_slots_match_two_calls(name):
+    """New tokens with a negative slot are neither written nor read from key /
+    value: the fused launch stays bit-identical (output and pool) to
+    pa_write_kv_cache followed by pa_prefill, whose decode then reads whatever
+    the cache holds at those positions."""
+    case, qs, dc = prepare(name)
+    if name == "cow_g8":
+        qs = synth.make_queries(case, ("const", 1), 12)
+    kn, vn, slots = new_token_rows(case, qs)
+    slots = slots.copy()
+    slots[::3] = -1
+    args = (host_to_dev(kn, "bf16", "cuda"), host_to_dev(vn, "bf16", "cuda"),
+            torch.from_numpy(slots).cuda())
+    q = host_to_dev(qs.q, "bf16", "cuda")
+    qsl = torch.from_numpy(qs.query_start_loc).cuda()
+    mq, maxL = int(qs.q_lens.max()), case.max_context_len
+    for P in (0, 64):
+        k1, v1 = dc.k_cache.clone(), dc.v_cache.clone()
+        k2, v2 = dc.k_cache.clone(), dc.v_cache.clone()
+        # the skipped positions hold other values in the cache than in key / value
+        for kk, vv in ((k1, v1), (k2, v2)):
+            kk.view(torch.int16).bitwise_xor_(1)      # one mantissa ulp
+            vv.view(torch.int16).bitwise_xor_(1)
+        a = torch.empty_like(q)
+        b = torch.empty_like(q)
+        if P:
+            w1 = pa.prefill_workspace(qs.num_tokens, case.Hq, case.D, maxL, P, "cuda")
+            w2 = pa.prefill_workspace(qs.num_tokens, case.Hq, case.D, maxL, P, "cuda")
+            pa.write_prefill(*args, None, q, k1, v1, dc.block_tables, dc.context_lens, qsl,
+                             float(case.scale), mq, maxL, partition_size=P, tmp_out=w1[0],
+                             tmp_max=w1[1], tmp_sum=w1[2], row_lens=w1[3])
+            pa.decode_splitk_reduce(a, w1[0], w1[1], w1[2], w1[3], maxL, P)
+            pa.write_kv_cache(args[0], args[1], k2, v2, args[2])
+            pa.prefill(None, q, k2, v2, dc.block_tables, dc.context_lens, qsl,
+                       float(case.scale), mq, maxL, partition_size=P, tmp_out=w2[0],
+                       tmp_max=w2[1], tmp_sum=w2[2], row_lens=w2[3])
+            pa.decode_splitk_reduce(b, w2[0], w2[1], w2[2], w2[3], maxL, P)
+        else:
+            pa.write_prefill(*args, a, q, k1, v1, dc.block_tables, dc.context_lens, qsl,
+                             float(case.scale), mq, maxL)
+            pa.write_kv_cache(args[0], args[1], k2, v2, args[2])
+            pa.prefill(b, q, k2, v2, dc.block_tables, dc.context_lens, qsl, float(case.scale),
+                       mq, maxL)
+        torch.cuda.synchronize()
+        assert torch.equal(k1.view(torch.int16), k2.view(torch.int16)), f"P={P}: K pool"
+        assert torch.equal(v1.view(torch.int16), v2.view(torch.int16)), f"P={P}: V pool"
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"P={P}: output"

@@ -172,6 +172,12 @@ def model_launch(lens, qlens, Hq, Hkv, B, i8=False, wr=False, P=0, max_query_len
             f = T0 < limit
             check(T0[f] // B < nvalid, "block-table entry past the context")
             fetched.append(f)
+        if wr:                                         # load_tile: the tile's new-token slots
+            j0 = kts * TK - new0
+            has = (j0 + TK > 0) & (j0 < n)
+            for jj in j0[has]:
+                tb, te = max(0, -int(jj)), min(TK, n - int(jj))
+                check(q0 + jj + tb >= 0 and q0 + jj + te - 1 < T, "slot_mapping entry")
         for k in range(NLD):                           # load_tile
             t, e = PIECE_T[(NR, i8)][k], PIECE_E[(NR, i8)][k]
             inn = kts[:, None] * TK + t[None, :] < limit
