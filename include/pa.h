@@ -166,22 +166,23 @@ int pa_decode(void *out, const void *q, const void *k_cache, const void *v_cache
  *
  * Schedule: all (sequence, kv head) contexts are laid end to end as one list
  * of 16-token chunks; a persistent grid (resident workgroups per CU times the
- * CU count) splits it into equal contiguous ranges of at least
- * min_piece_tokens / 16 chunks. A context inside one range is finished in
- * place. A context cut by range ends leaves one partial per piece in the
- * workspace; the workgroup that completes its last piece (an atomic counter
+ * CU count) splits it into one contiguous range of about equal cost per wave,
+ * each at least min_piece_tokens / 16 chunks. A context inside one range is
+ * finished in place. A context cut by range ends leaves one partial per piece
+ * in the workspace; the wave that completes its last piece (an atomic counter
  * per (sequence, kv head)) combines the pieces exactly as
  * pa_decode_splitk_reduce would, writes `out`, and resets the counter.
  *
  *   out, q, k_cache, v_cache, block_tables, context_lens, k_scale, v_scale,
  *   scale, num_seqs .. max_context_len, q_dtype, cache_dtype: as pa_decode.
  *   min_piece_tokens  smallest piece a range may be cut to, a multiple of 16.
- *   tmp_out       [num_seqs][num_heads][NS][head_dim] fp32, tmp_max and tmp_sum
- *                 [num_seqs][num_heads][NS] fp32, NS = pa_balanced_slots(
- *                 max_context_len, min_piece_tokens). Contents on return are
+ *   tmp_out       [slots][G][head_dim] fp32, tmp_max and tmp_sum [slots][G] fp32,
+ *                 G = num_heads / num_kv_heads, slots as pa_balanced_workspace
+ *                 reports for the stream's device. Contents on return are
  *                 unspecified.
- *   counters      [num_seqs][num_kv_heads] int32, all zero before the call; the
- *                 call leaves them all zero again (zero them once, reuse).
+ *   counters      int32 [counters as pa_balanced_workspace reports], all zero
+ *                 before the call; the call leaves them all zero again (zero
+ *                 them once, reuse).
  * Calls that share `counters` or the workspace must not overlap in time
  * (e.g. run them on one stream). Supported instances: as pa_decode.
  * Alignment: out, q, k_cache, v_cache, tmp_out 16-byte aligned.
@@ -339,10 +340,20 @@ int pa_write_prefill(const void *key, const void *value, const int64_t *slot_map
                      int partition_size, float *tmp_out, float *tmp_max, float *tmp_sum,
                      int32_t *row_lens, pa_dtype q_dtype, pa_dtype cache_dtype, void *stream);
 
-/* Workspace slots per (sequence, query head) that pa_decode_balanced needs:
- * ceil(ceil(max_context_len / 16) / (min_piece_tokens / 16)) + 1, or 0 when
- * max_context_len <= 0 or min_piece_tokens < 16. */
-int pa_balanced_slots(int max_context_len, int min_piece_tokens);
+/*
+ * pa_balanced_workspace -- sizes of the workspace that pa_decode_balanced and
+ * pa_write_decode_balanced need for these shapes on the device of `stream`
+ * (any dtypes): *slots partial-state slots, i.e. tmp_out [*slots][G][head_dim]
+ * and tmp_max, tmp_sum [*slots][G] fp32 with G = num_heads / num_kv_heads,
+ * and *counters int32 counters (num_seqs * num_kv_heads). The slots grow
+ * with the device (4 per wave of the persistent grid), not with the context
+ * lengths. Returns PA_OK, PA_ERR_NULL,
+ * PA_ERR_SHAPE, PA_ERR_UNSUPPORTED (no balanced instance for head_dim and G)
+ * or PA_ERR_LAUNCH (the runtime could not report the device's occupancy).
+ * Allocates nothing; the caller allocates and zeroes the counters once.
+ */
+int pa_balanced_workspace(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                          void *stream, int64_t *slots, int64_t *counters);
 
 /*
  * pa_decode_splitk_reduce -- log-sum-exp combination of split-K partials.

@@ -47,8 +47,9 @@ _lib.pa_decode_balanced.argtypes = [_p, _p, _p, _p, _p, _i, _p, _p, _p, _f, _i, 
                                     _i64, _i, _i, _p, _p, _p, _p, _i, _i, _p]
 _lib.pa_write_decode_balanced.restype = _i
 _lib.pa_write_decode_balanced.argtypes = [_p, _p, _p] + _lib.pa_decode_balanced.argtypes
-_lib.pa_balanced_slots.restype = _i
-_lib.pa_balanced_slots.argtypes = [_i, _i]
+_lib.pa_balanced_workspace.restype = _i
+_lib.pa_balanced_workspace.argtypes = [_i, _i, _i, _i, _p, ctypes.POINTER(_i64),
+                                       ctypes.POINTER(_i64)]
 _lib.pa_copy_blocks.restype = _i
 _lib.pa_copy_blocks.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i64, _i, _p]
 _lib.pa_decode_splitk_reduce.restype = _i
@@ -270,8 +271,28 @@ def copy_blocks(k_cache, v_cache, block_mapping, k_scale=None, v_scale=None, str
     _check("pa_copy_blocks", rc)
 
 
-def balanced_slots(max_context_len: int, min_piece_tokens: int) -> int:
-    return _lib.pa_balanced_slots(int(max_context_len), int(min_piece_tokens))
+def balanced_sizes(num_seqs, num_heads, num_kv_heads, head_dim, device=None):
+    """(slots, counters) of the balanced schedule's workspace on ``device``
+    (pa_balanced_workspace): tmp_out [slots, G, D], tmp_max / tmp_sum
+    [slots, G] fp32, counters int32 [counters]."""
+    dev = torch.device("cuda" if device is None else device)
+    if dev.index is None:
+        dev = torch.device("cuda", torch.cuda.current_device())
+    slots, counters = _i64(0), _i64(0)
+    rc = _lib.pa_balanced_workspace(int(num_seqs), int(num_heads), int(num_kv_heads),
+                                    int(head_dim), _stream(None, dev), ctypes.byref(slots),
+                                    ctypes.byref(counters))
+    _check("pa_balanced_workspace", rc)
+    return slots.value, counters.value
+
+
+def _check_balanced_ws(q, num_kv_heads, tmp_out, tmp_max, tmp_sum, counters):
+    S, Hq, D = q.shape
+    ns, nc = balanced_sizes(S, Hq, num_kv_heads, D, q.device)
+    G = Hq // num_kv_heads
+    if tmp_out.numel() < ns * G * D or tmp_max.numel() < ns * G or tmp_sum.numel() < ns * G \
+            or counters.numel() < nc:
+        raise ValueError("workspace too small (see balanced_sizes)")
 
 
 def decode_balanced(out, q, k_cache, v_cache, block_tables, context_lens, scale,
@@ -287,13 +308,9 @@ def decode_balanced(out, q, k_cache, v_cache, block_tables, context_lens, scale,
     S, Hq, D = q.shape
     NB, Hkv, B, D2 = k_cache.shape
     if D2 != D or v_cache.shape != k_cache.shape or block_tables.shape[0] != S \
-            or context_lens.shape != (S,) or out.shape != q.shape \
-            or counters.numel() < S * Hkv:
+            or context_lens.shape != (S,) or out.shape != q.shape:
         raise ValueError("shape mismatch")
-    ns = balanced_slots(max_context_len, min_piece_tokens)
-    if tmp_out.numel() < S * Hq * ns * D or tmp_max.numel() < S * Hq * ns \
-            or tmp_sum.numel() < S * Hq * ns:
-        raise ValueError("workspace too small")
+    _check_balanced_ws(q, Hkv, tmp_out, tmp_max, tmp_sum, counters)
     if out.dtype != q.dtype:
         raise TypeError("out must have the dtype of q")
     rc = _lib.pa_decode_balanced(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
@@ -325,13 +342,9 @@ def write_decode_balanced(key, value, slot_mapping, out, q, k_cache, v_cache, bl
             or key.dtype != q.dtype or value.dtype != q.dtype:
         raise ValueError("key/value must be [S, Hkv, D] of q's dtype, slot_mapping [S]")
     if D2 != D or v_cache.shape != k_cache.shape or block_tables.shape[0] != S \
-            or context_lens.shape != (S,) or out.shape != q.shape \
-            or counters.numel() < S * Hkv:
+            or context_lens.shape != (S,) or out.shape != q.shape:
         raise ValueError("shape mismatch")
-    ns = balanced_slots(max_context_len, min_piece_tokens)
-    if tmp_out.numel() < S * Hq * ns * D or tmp_max.numel() < S * Hq * ns \
-            or tmp_sum.numel() < S * Hq * ns:
-        raise ValueError("workspace too small")
+    _check_balanced_ws(q, Hkv, tmp_out, tmp_max, tmp_sum, counters)
     if out.dtype != q.dtype:
         raise TypeError("out must have the dtype of q")
     rc = _lib.pa_write_decode_balanced(_ptr(key), _ptr(value), _ptr(slot_mapping), _ptr(out),
@@ -347,12 +360,16 @@ def write_decode_balanced(key, value, slot_mapping, out, q, k_cache, v_cache, bl
 
 def balanced_workspace(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len,
                        min_piece_tokens, device):
-    """(tmp_out, tmp_max, tmp_sum, counters) for decode_balanced; counters zeroed."""
-    ns = max(1, balanced_slots(max_context_len, min_piece_tokens))
-    return (torch.empty((num_seqs, num_heads, ns, head_dim), dtype=torch.float32, device=device),
-            torch.empty((num_seqs, num_heads, ns), dtype=torch.float32, device=device),
-            torch.empty((num_seqs, num_heads, ns), dtype=torch.float32, device=device),
-            torch.zeros((num_seqs, num_kv_heads), dtype=torch.int32, device=device))
+    """(tmp_out, tmp_max, tmp_sum, counters) for decode_balanced; counters zeroed.
+    The sizes depend on the device and the head shape only (balanced_sizes);
+    max_context_len and min_piece_tokens are accepted for symmetry with
+    ``workspace`` and do not change them."""
+    ns, nc = balanced_sizes(num_seqs, num_heads, num_kv_heads, head_dim, device)
+    G = num_heads // num_kv_heads
+    return (torch.empty((ns, G, head_dim), dtype=torch.float32, device=device),
+            torch.empty((ns, G), dtype=torch.float32, device=device),
+            torch.empty((ns, G), dtype=torch.float32, device=device),
+            torch.zeros((nc,), dtype=torch.int32, device=device))
 
 
 def workspace(num_seqs, num_heads, head_dim, max_context_len, partition_size, device):

@@ -450,11 +450,22 @@ int prefill(const void* key, const void* value, const int64_t* slot_mapping, voi
 
 extern "C" {
 
-int pa_balanced_slots(int max_context_len, int min_piece_tokens) {
-    if (max_context_len <= 0 || min_piece_tokens < 16) return 0;
-    const int64_t chunks = ((int64_t)max_context_len + 15) / 16;
-    const int64_t minc = min_piece_tokens / 16;
-    return (int)((chunks + minc - 1) / minc + 1);
+int pa_balanced_workspace(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                          void* stream, int64_t* slots, int64_t* counters) {
+    if (!slots || !counters) return PA_ERR_NULL;
+    if (num_seqs < 0 || num_heads < 1 || num_kv_heads < 1 || num_heads % num_kv_heads ||
+        head_dim < 1)
+        return PA_ERR_SHAPE;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    const int G = num_heads / num_kv_heads;
+    const int wv = pa::balanced_waves_valu(head_dim, G, st);
+    const int wm = pa::balanced_waves_mfma(head_dim, G, st);
+    if (wv < 0 || wm < 0) return PA_ERR_LAUNCH;
+    const int waves = wv > wm ? wv : wm;
+    if (waves == 0) return PA_ERR_UNSUPPORTED;
+    *slots = 4 * (int64_t)waves;
+    *counters = (int64_t)num_seqs * num_kv_heads;
+    return PA_OK;
 }
 
 }  // extern "C"
@@ -484,12 +495,10 @@ int balanced(const void* key, const void* value, const int64_t* slot_mapping, vo
         if (!key || !value) return PA_ERR_NULL;
         if (!aligned16(key) || !aligned16(value)) return PA_ERR_ALIGN;
     }
-    const int ns = pa_balanced_slots(max_context_len, min_piece_tokens);
     pa::DecodeArgs a{out, q, k_cache, v_cache, block_tables, context_lens, k_scale, v_scale,
                      tmp_out, tmp_max, tmp_sum, counters, scale, num_seqs, num_heads,
                      num_kv_heads, head_dim, block_size, max_blocks_per_seq, max_context_len,
-                     min_piece_tokens, ns > 0 ? ns : 1, (pa::Dtype)q_dtype,
-                     (pa::Dtype)cache_dtype};
+                     min_piece_tokens, 1, (pa::Dtype)q_dtype, (pa::Dtype)cache_dtype};
     const bool mfma = pa::mfma_supports(a);
     if (!mfma && !pa::valu_supports(a)) return PA_ERR_UNSUPPORTED;
     if ((int64_t)num_kv_heads * (((int64_t)max_context_len + 15) / 16) * num_seqs > 0x7fffffff)

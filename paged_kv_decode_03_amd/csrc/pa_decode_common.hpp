@@ -232,11 +232,15 @@ __device__ __forceinline__ void decode_partitions(const DecodeArgs& a) {
 // the set-up, and the loads of the next chunk -- in the same segment or the
 // next one -- are in flight while the current chunk is computed.
 // A segment wholly inside one range is finished in place. A segment cut by
-// range ends leaves one partial per piece in the workspace; after its stores
-// have completed, each piece's wave increments an agent-scope counter for the
-// segment, and the wave that brings it to the number of pieces combines them
-// all (coherent loads), writes out and resets the counter to 0. No wave ever
-// waits for another.
+// range ends leaves one partial per range that holds part of it, in the
+// workspace slot 2j of range j when the segment started in an earlier range,
+// 2j + 1 when it goes on past range j (a range cuts at most its first and its
+// last segment, so the slots are distinct and number 4 per wave of the grid,
+// whatever the context lengths). After its stores have completed, each
+// piece's wave increments an agent-scope counter for the segment, and the wave
+// that brings it to the number of pieces combines them in range order
+// (coherent loads), writes out and resets the counter to 0. No wave ever waits
+// for another.
 //
 // Workgroups are dealt round-robin to the 8 XCDs, so the workgroup index is
 // remapped to give each XCD a contiguous run of ranges (neighbouring
@@ -543,9 +547,10 @@ struct PieceEnd {
     const Core& core;
     const WaveRange& r;
     int64_t held_seg = -1;                           // a stored, unpublished piece
+    long long held_first = 0;
     int held_pieces = 0;
 
-    __device__ void publish(int64_t seg, int pieces) const {
+    __device__ void publish(int64_t seg, long long first, int pieces) const {
         const int lane = threadIdx.x & 63;
         int prev = 0;
         if (lane == 0) prev = atomicAdd(&a.counters[seg], 1);
@@ -553,7 +558,7 @@ struct PieceEnd {
         if (prev == pieces - 1) {                    // every other piece is published
             const int Hkv = a.num_kv_heads;
             const int s = (int)(seg / Hkv), g = (int)(seg - (int64_t)s * Hkv);
-            core.combine(seg * a.num_partitions, pieces, s, g);
+            core.combine(first, pieces, s, g);
             if (lane == 0)
                 __hip_atomic_store(&a.counters[seg], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
@@ -570,21 +575,22 @@ struct PieceEnd {
             const int pieces =
                 (int)(r.rg.of(p.Y + (long long)p.n * kChunkCost - 1) - first) + 1;
             const int64_t seg = (int64_t)p.s * a.num_kv_heads + p.g;
-            core.store_slot(St, seg * a.num_partitions + (r.wv - first));
+            core.store_slot(St, 2 * r.wv + (p.A >= r.X0 ? 1 : 0));   // (see above)
             if (!last) {
                 held_seg = seg;
+                held_first = first;
                 held_pieces = pieces;
                 return;
             }
             __builtin_amdgcn_s_waitcnt(0);           // every store of this wave is complete
-            if (held_seg >= 0) publish(held_seg, held_pieces);
-            publish(seg, pieces);
+            if (held_seg >= 0) publish(held_seg, held_first, held_pieces);
+            publish(seg, first, pieces);
             held_seg = -1;
             return;
         }
         if (last && held_seg >= 0) {
             __builtin_amdgcn_s_waitcnt(0);
-            publish(held_seg, held_pieces);
+            publish(held_seg, held_first, held_pieces);
             held_seg = -1;
         }
     }

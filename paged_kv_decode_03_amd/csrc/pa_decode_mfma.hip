@@ -508,14 +508,16 @@ struct MfmaCore {
         }
     }
 
-    // Log-sum-exp of slots slot0 .. slot0+n-1 of (s, g) into out: the pieces
-    // are read kBatch at a time with a running maximum (earlier sums are
-    // rescaled when it moves), so their loads overlap.
+    // Log-sum-exp of the partials of pieces first .. first+n-1 of (s, g) into
+    // out (piece first + k left its partial in slot 2 (first + k) + (k == 0)):
+    // the partials are read kBatch at a time with a running maximum (earlier
+    // sums are rescaled when it moves), so their loads overlap.
     static constexpr int kBatch = 8;
-    __device__ void combine(int64_t slot0, int n, int s, int g) const {
-        const __amdgpu_buffer_rsrc_t rs = ws_rsrc(a.tmp_out + slot0 * (G * D), (uint32_t)n * (G * D * 4));
-        const __amdgpu_buffer_rsrc_t rm = ws_rsrc(a.tmp_max + slot0 * G, (uint32_t)n * (G * 4));
-        const __amdgpu_buffer_rsrc_t rl = ws_rsrc(a.tmp_sum + slot0 * G, (uint32_t)n * (G * 4));
+    __device__ void combine(long long first, int n, int s, int g) const {
+        const int64_t slot0 = 2 * first;
+        const __amdgpu_buffer_rsrc_t rs = ws_rsrc(a.tmp_out + slot0 * (G * D), (uint32_t)(2 * n) * (G * D * 4));
+        const __amdgpu_buffer_rsrc_t rm = ws_rsrc(a.tmp_max + slot0 * G, (uint32_t)(2 * n) * (G * 4));
+        const __amdgpu_buffer_rsrc_t rl = ws_rsrc(a.tmp_sum + slot0 * G, (uint32_t)(2 * n) * (G * 4));
 #pragma unroll
         for (int hb = 0; hb < NHB; ++hb) {
             const uint32_t hoff = 4 * (hb * 4 + j4);
@@ -529,10 +531,11 @@ struct MfmaCore {
 #pragma unroll
                 for (int j = 0; j < kBatch; ++j) {
                     const uint32_t k = (uint32_t)min(k0 + j, n - 1);
-                    mk[j] = ws_load4(rm, k * (G * 4) + hoff);
-                    lk[j] = ws_load4(rl, k * (G * 4) + hoff);
-                    a0[j] = ws_load16(rs, k * (G * D * 4) + aoff);
-                    a1[j] = ws_load16(rs, k * (G * D * 4) + aoff + 16);
+                    const uint32_t sl = 2 * k + (k == 0 ? 1u : 0u);
+                    mk[j] = ws_load4(rm, sl * (G * 4) + hoff);
+                    lk[j] = ws_load4(rl, sl * (G * 4) + hoff);
+                    a0[j] = ws_load16(rs, sl * (G * D * 4) + aoff);
+                    a1[j] = ws_load16(rs, sl * (G * D * 4) + aoff + 16);
                 }
                 float Mb = M;
 #pragma unroll
@@ -600,6 +603,21 @@ hipError_t launch(const DecodeArgs& a, Schedule sch, hipStream_t st) {
 }
 
 }  // namespace
+
+int balanced_waves_mfma(int head_dim, int G, hipStream_t st) {
+    if (head_dim != 128 || (G != 4 && G != 8)) return 0;
+    const void* fns[2] = {G == 4 ? reinterpret_cast<const void*>(&mfma_balanced<4, BF16>)
+                                 : reinterpret_cast<const void*>(&mfma_balanced<8, BF16>),
+                          G == 4 ? reinterpret_cast<const void*>(&mfma_balanced<4, I8>)
+                                 : reinterpret_cast<const void*>(&mfma_balanced<8, I8>)};
+    int m = 0;
+    for (const void* fn : fns) {
+        const int grid = balanced_grid(fn, NWR * 64, st);
+        if (grid <= 0) return -1;
+        m = grid * NWR > m ? grid * NWR : m;
+    }
+    return m;
+}
 
 bool mfma_supports(const DecodeArgs& a) {
     const int G = a.num_heads / a.num_kv_heads;

@@ -231,18 +231,20 @@ struct ValuCore {
         }
     }
 
-    // Log-sum-exp of slots slot0 .. slot0+n-1 of (s, g) into out.
-    __device__ void combine(int64_t slot0, int n, int s, int g) const {
+    // Log-sum-exp of the partials of pieces first .. first+n-1 of (s, g) into
+    // out; piece first + k left its partial in slot 2 (first + k) + (k == 0).
+    __device__ void combine(long long first, int n, int s, int g) const {
         const int64_t base = ((int64_t)s * a.num_heads + g * G) * D;
+        auto slot = [&](int k) -> int64_t { return 2 * (first + k) + (k == 0 ? 1 : 0); };
         for (int i = lane; i < G * D; i += 64) {
             const int h = i / D;
             float M = kNegInf;
-            for (int k = 0; k < n; ++k) M = fmaxf(M, ws_load_coherent(a.tmp_max + (slot0 + k) * G + h));
+            for (int k = 0; k < n; ++k) M = fmaxf(M, ws_load_coherent(a.tmp_max + slot(k) * G + h));
             float lsum = 0.0f, o = 0.0f;
             for (int k = 0; k < n; ++k) {
-                const float W = rel_weight<false>(ws_load_coherent(a.tmp_max + (slot0 + k) * G + h), M);
-                lsum += W * ws_load_coherent(a.tmp_sum + (slot0 + k) * G + h);
-                o += W * ws_load_coherent(a.tmp_out + (slot0 + k) * (G * D) + i);
+                const float W = rel_weight<false>(ws_load_coherent(a.tmp_max + slot(k) * G + h), M);
+                lsum += W * ws_load_coherent(a.tmp_sum + slot(k) * G + h);
+                o += W * ws_load_coherent(a.tmp_out + slot(k) * (G * D) + i);
             }
             store_out(a.out, base + i, o / lsum, a.q_dtype);
         }
@@ -274,6 +276,22 @@ hipError_t launch(const DecodeArgs& a, Schedule sch, hipStream_t st) {
     return hipGetLastError();
 }
 
+// Waves of the balanced grid of each instance with head_dim D and group G.
+template <int D, int G>
+int waves_of(hipStream_t st) {
+    const void* fns[4] = {reinterpret_cast<const void*>(&valu_balanced<D, G, F32, F32>),
+                          reinterpret_cast<const void*>(&valu_balanced<D, G, BF16, BF16>),
+                          reinterpret_cast<const void*>(&valu_balanced<D, G, F32, I8>),
+                          reinterpret_cast<const void*>(&valu_balanced<D, G, BF16, I8>)};
+    int m = 0;
+    for (const void* fn : fns) {
+        const int grid = balanced_grid(fn, NW * 64, st);
+        if (grid <= 0) return -1;
+        m = grid * NW > m ? grid * NW : m;
+    }
+    return m;
+}
+
 template <int D, int G>
 hipError_t by_dtype(const DecodeArgs& a, Schedule sch, hipStream_t st) {
     if (a.q_dtype == F32 && a.cache == F32) return launch<D, G, F32, F32>(a, sch, st);
@@ -291,6 +309,12 @@ bool valu_supports(const DecodeArgs& a) {
                     (a.cache == I8 && (a.q_dtype == F32 || a.q_dtype == BF16));
     return dt && (G == 1 || G == 2) && (a.head_dim == 64 || a.head_dim == 128) &&
            (a.block_size == 16 || a.block_size == 32);
+}
+
+int balanced_waves_valu(int head_dim, int G, hipStream_t st) {
+    if (head_dim == 64) return G == 1 ? waves_of<64, 1>(st) : G == 2 ? waves_of<64, 2>(st) : 0;
+    if (head_dim == 128) return G == 1 ? waves_of<128, 1>(st) : G == 2 ? waves_of<128, 2>(st) : 0;
+    return 0;
 }
 
 hipError_t launch_decode_valu(const DecodeArgs& a, Schedule sch, hipStream_t st) {

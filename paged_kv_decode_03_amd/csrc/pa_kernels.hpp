@@ -33,7 +33,8 @@ struct DecodeArgs {
     float* tmp_out;
     float* tmp_max;
     float* tmp_sum;
-    int32_t* counters;    // [S][Hkv], balanced mode only; zero on entry and exit
+    int32_t* counters;    // balanced mode only: [S][Hkv] segment counters, then the
+                          // schedule's claims; all zero on entry and exit
     float scale;
     int num_seqs, num_heads, num_kv_heads, head_dim, block_size;
     int max_blocks_per_seq;
@@ -76,6 +77,10 @@ hipError_t launch_decode_valu(const DecodeArgs& a, Schedule sch, hipStream_t st)
 hipError_t launch_decode_mfma(const DecodeArgs& a, Schedule sch, hipStream_t st);
 // Workgroups of a balanced launch: resident workgroups per CU times CUs.
 int balanced_grid(const void* kernel, int threads, hipStream_t st);
+// Most waves any balanced instance for (head_dim, G) runs on the stream's
+// device (0: no instance; < 0: the runtime failed).
+int balanced_waves_valu(int head_dim, int G, hipStream_t st);
+int balanced_waves_mfma(int head_dim, int G, hipStream_t st);
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t st);
 hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t st);
 
