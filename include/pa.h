@@ -226,6 +226,34 @@ int pa_write_decode_balanced(const void *key, const void *value, const int64_t *
                              pa_dtype cache_dtype, void *stream);
 
 /*
+ * pa_write_decode_balanced_noalloc -- pa_write_decode_balanced for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): the same step, with the workspace
+ * (partials, maxima, sums, counters) in a static array of the library instead
+ * of caller buffers. It calls no hipMalloc or hipFree and allocates nothing.
+ *
+ * The array is 40 MiB per GPU (held by every device that loads the library
+ * until the process ends): a 1 MiB region of int32 counters, cleared by a
+ * kernel on `stream` at the first call on each device and left zero by every
+ * call, then the partial states. Shapes whose workspace (pa_balanced_workspace)
+ * does not fit -- more than 262144 (sequence, kv head) counters, or partial
+ * slots beyond the rest of the array -- return PA_ERR_SHAPE before anything is
+ * enqueued (on a 256-CU device every kernel instance's slots fit). Every call on
+ * one GPU uses that GPU's array: calls that overlap in time on one GPU (two
+ * streams, two host threads) race and must not be made. Arguments, results and
+ * errors otherwise as pa_write_decode_balanced.
+ */
+int pa_write_decode_balanced_noalloc(const void *key, const void *value,
+                                     const int64_t *slot_mapping, void *out, const void *q,
+                                     void *k_cache, void *v_cache, const int32_t *block_tables,
+                                     int max_blocks_per_seq, const int32_t *context_lens,
+                                     const float *k_scale, const float *v_scale, float scale,
+                                     int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                                     int block_size, int64_t num_blocks, int max_context_len,
+                                     int min_piece_tokens, pa_dtype q_dtype, pa_dtype cache_dtype,
+                                     void *stream);
+
+/*
  * pa_copy_blocks -- the copy step of copy-on-write block sharing
  * ("Continuous-Batching-LLM-Inference-Engine" README, feature list: the paged
  * KV cache's block pool with copy-on-write reference counts): before a

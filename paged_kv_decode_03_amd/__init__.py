@@ -13,6 +13,10 @@ Entry points (same names as the C ABI without the ``pa_`` prefix):
   decode_splitk_reduce     log-sum-exp reduce of split-K partials
   decode_balanced          work-balanced split-K decode with the reduce fused in
   write_decode_balanced    the new-token write and decode_balanced in one call
+  write_decode_balanced_noalloc
+                           the same, with the workspace in the library's static
+                           per-GPU array (no allocation; calls on one GPU must
+                           not overlap)
   copy_blocks              copy-on-write copy of whole blocks (K, V, int8 scales)
 plus ``workspace`` / ``balanced_workspace`` (allocate with torch) and
 ``paged_attention`` (decode into a new output tensor, any schedule).
@@ -47,6 +51,9 @@ _lib.pa_decode_balanced.argtypes = [_p, _p, _p, _p, _p, _i, _p, _p, _p, _f, _i, 
                                     _i64, _i, _i, _p, _p, _p, _p, _i, _i, _p]
 _lib.pa_write_decode_balanced.restype = _i
 _lib.pa_write_decode_balanced.argtypes = [_p, _p, _p] + _lib.pa_decode_balanced.argtypes
+_lib.pa_write_decode_balanced_noalloc.restype = _i
+_lib.pa_write_decode_balanced_noalloc.argtypes = (_lib.pa_write_decode_balanced.argtypes[:-7]
+                                                  + [_i, _i, _p])
 _lib.pa_balanced_workspace.restype = _i
 _lib.pa_balanced_workspace.argtypes = [_i, _i, _i, _i, _p, ctypes.POINTER(_i64),
                                        ctypes.POINTER(_i64)]
@@ -356,6 +363,36 @@ def write_decode_balanced(key, value, slot_mapping, out, q, k_cache, v_cache, bl
                                        _ptr(counters), _dt(q), _dt(k_cache),
                                        _stream(stream, dev))
     _check("pa_write_decode_balanced", rc)
+
+
+def write_decode_balanced_noalloc(key, value, slot_mapping, out, q, k_cache, v_cache,
+                                  block_tables, context_lens, scale, max_context_len,
+                                  min_piece_tokens, k_scale=None, v_scale=None, stream=None):
+    """write_decode_balanced with the workspace in the library's static array:
+    nothing is allocated. Shapes whose workspace does not fit that array raise
+    PAError (shape); calls that overlap in time on one GPU race."""
+    dev = _dev(key, value, slot_mapping, out, q, k_cache, v_cache, block_tables, context_lens,
+               k_scale, v_scale)
+    if slot_mapping.dtype != torch.int64:
+        raise TypeError("slot_mapping must be int64")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise TypeError("block_tables and context_lens must be int32")
+    S, Hq, D = q.shape
+    NB, Hkv, B, D2 = k_cache.shape
+    if key.shape != (S, Hkv, D) or value.shape != key.shape or slot_mapping.shape != (S,) \
+            or key.dtype != q.dtype or value.dtype != q.dtype:
+        raise ValueError("key/value must be [S, Hkv, D] of q's dtype, slot_mapping [S]")
+    if D2 != D or v_cache.shape != k_cache.shape or block_tables.shape[0] != S \
+            or context_lens.shape != (S,) or out.shape != q.shape:
+        raise ValueError("shape mismatch")
+    if out.dtype != q.dtype:
+        raise TypeError("out must have the dtype of q")
+    rc = _lib.pa_write_decode_balanced_noalloc(
+        _ptr(key), _ptr(value), _ptr(slot_mapping), _ptr(out), _ptr(q), _ptr(k_cache),
+        _ptr(v_cache), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
+        _ptr(k_scale), _ptr(v_scale), float(scale), S, Hq, Hkv, D, B, NB, int(max_context_len),
+        int(min_piece_tokens), _dt(q), _dt(k_cache), _stream(stream, dev))
+    _check("pa_write_decode_balanced_noalloc", rc)
 
 
 def balanced_workspace(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len,

@@ -594,3 +594,92 @@ int pa_decode_splitk_reduce(void* out, const float* tmp_out, const float* tmp_ma
 }
 
 }  // extern "C"
+
+// ---- the decode step without a caller workspace ------------------------------
+// The balanced step's workspace in a file-scope device array, one copy per GPU
+// (each device that loads the library holds it until the process ends): the
+// counters first (zeroed once per device, left zero by every call), then the
+// partial states. In host code the array's name is only a stand-in: its device
+// address, per device, comes from hipGetSymbolAddress and is used everywhere
+// host code needs the memory.
+namespace {
+
+constexpr size_t kScratchBytes = size_t(40) << 20;           // 40 MiB per GPU
+constexpr size_t kScratchCounters = size_t(1) << 18;         // int32 counters (1 MiB)
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+__global__ void zero_ints(int32_t* p, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = 0;
+}
+
+// The scratch's device address on the stream's device, taken once per device
+// (with that device current), its counters cleared by a kernel on the stream
+// at that first call. nullptr: the runtime failed.
+char* scratch_on(hipStream_t st) {
+    static std::mutex mu;
+    static std::map<int, char*> addr;
+    int dev = 0;
+    if (st ? hipStreamGetDevice(st, &dev) != hipSuccess : hipGetDevice(&dev) != hipSuccess)
+        return nullptr;
+    std::lock_guard<std::mutex> lk(mu);
+    auto it = addr.find(dev);
+    if (it != addr.end()) return it->second;
+    int cur = 0;
+    if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return nullptr;
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (cur != dev) (void)hipSetDevice(cur);
+    if (e != hipSuccess || !ptr) return nullptr;
+    hipLaunchKernelGGL(zero_ints, dim3(256), dim3(256), 0, st, reinterpret_cast<int32_t*>(ptr),
+                       (int64_t)kScratchCounters);
+    if (hipGetLastError() != hipSuccess) return nullptr;
+    addr[dev] = reinterpret_cast<char*>(ptr);
+    return addr[dev];
+}
+
+size_t round256(size_t n) { return (n + 255) & ~size_t(255); }
+
+}  // namespace
+
+extern "C" {
+
+int pa_write_decode_balanced_noalloc(const void* key, const void* value,
+                                     const int64_t* slot_mapping, void* out, const void* q,
+                                     void* k_cache, void* v_cache, const int32_t* block_tables,
+                                     int max_blocks_per_seq, const int32_t* context_lens,
+                                     const float* k_scale, const float* v_scale, float scale,
+                                     int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                                     int block_size, int64_t num_blocks, int max_context_len,
+                                     int min_piece_tokens, pa_dtype q_dtype, pa_dtype cache_dtype,
+                                     void* stream) {
+    if (num_seqs > 0 && !slot_mapping) return PA_ERR_NULL;
+    if (num_seqs < 0 || num_heads < 1 || num_kv_heads < 1 || num_heads % num_kv_heads ||
+        head_dim < 1)
+        return PA_ERR_SHAPE;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    int64_t slots = 0, counters = 0;
+    int rc = pa_balanced_workspace(num_seqs, num_heads, num_kv_heads, head_dim, stream, &slots,
+                                   &counters);
+    if (rc) return rc;
+    const size_t G = (size_t)(num_heads / num_kv_heads);
+    const size_t out_bytes = round256((size_t)slots * G * (size_t)head_dim * 4);
+    const size_t ml_bytes = round256((size_t)slots * G * 4);
+    if ((size_t)counters > kScratchCounters ||
+        kScratchCounters * 4 + out_bytes + 2 * ml_bytes > kScratchBytes)
+        return PA_ERR_SHAPE;                         // beyond the static scratch
+    char* base = scratch_on(st);
+    if (!base) return PA_ERR_LAUNCH;
+    int32_t* cnt = reinterpret_cast<int32_t*>(base);
+    float* tmp_out = reinterpret_cast<float*>(base + kScratchCounters * 4);
+    float* tmp_max = reinterpret_cast<float*>(base + kScratchCounters * 4 + out_bytes);
+    float* tmp_sum = reinterpret_cast<float*>(base + kScratchCounters * 4 + out_bytes + ml_bytes);
+    return balanced(key, value, slot_mapping, out, q, k_cache, v_cache, block_tables,
+                    max_blocks_per_seq, context_lens, k_scale, v_scale, scale, num_seqs, num_heads,
+                    num_kv_heads, head_dim, block_size, num_blocks, max_context_len,
+                    min_piece_tokens, tmp_out, tmp_max, tmp_sum, cnt, q_dtype, cache_dtype, stream);
+}
+
+}  // extern "C"
