@@ -20,18 +20,26 @@
 //    log2(e) folded into the scale) over its tokens, so the running max needs
 //    no cross-lane reduction inside the loop; the reference max only moves
 //    when it is exceeded by more than 8, so rescales are rare.
-//  PV: v_mfma_f32_4x4x1_16b_f32, 32 per chunk and head group. The A operand
-//    is V row 4*step + tg, dims 8*(l%16) + e, straight from a fully coalesced
-//    16-byte load; the B operand is the lane's own probability register
-//    `step`, already in place. V and P stay in fp32.
+//  PV, bf16 cache: v_mfma_f32_4x4x4_16b_bf16, 8 per chunk and head group.
+//    Block (tg, qd) sums over the 4 tokens 4*k + tg of row group tg: the A
+//    operand of lane l is one dim (8*(l%16) + e) of those 4 V rows, taken
+//    from the lane's own 16-byte row loads by byte permutes; the B operand is
+//    the lane's 4 probabilities, rounded to bf16 (the row sum l adds the
+//    rounded values, so the output is an exact convex combination of the
+//    weights used).
+//  PV, int8 cache: v_mfma_f32_4x4x1_16b_f32, 32 per chunk and head group, on
+//    the codes and p * v_scale in fp32. The A operand is V row 4*step + tg,
+//    dims 8*(l%16) + e; the B operand is the lane's own probability register
+//    `step`, already in place.
 //  The 4 row states are merged with lane shuffles. Afterwards lane
 //  (tg, qd, j4) owns dims 8*(4*qd + tg) + e, e = 0..7, of head j4: the final
 //  output, a workspace partial and the combine of partials all use that
 //  assignment, so each is one coalesced 16-byte (or 8 x 4-byte) access per lane.
 //
-// No LDS is used in the main loop: K and V go from HBM straight to registers
-// with 16-byte loads, and the next chunk's loads are issued before the current
-// chunk is computed.
+// The partition driver loads K and V from HBM straight to registers with
+// 16-byte loads (load), the next chunk's issued before the current one is
+// computed; the balanced driver streams them through a per-wave LDS ring
+// filled by direct loads (issue / fetch).
 #include "pa_decode_common.hpp"
 #include "pa_write_row.hpp"
 
@@ -338,6 +346,7 @@ struct MfmaCore {
         }
         const float xs = sl2 * cur.ks;
         float p[NHB][4];
+        uint32_t pk[NHB][2];                     // bf16 cache: p rounded, packed
         float alpha[NHB];
         bool rescale = false;
 #pragma unroll
@@ -364,9 +373,15 @@ struct MfmaCore {
             alpha[hb] = __builtin_amdgcn_exp2f(S.m[hb] - muse);
             float psum = 0.0f;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                p[hb][i] = __builtin_amdgcn_exp2f(x[i] - muse);
-                psum += p[hb][i];
+            for (int i = 0; i < 4; ++i) p[hb][i] = __builtin_amdgcn_exp2f(x[i] - muse);
+            if constexpr (Q8) {
+                psum = (p[hb][0] + p[hb][1]) + (p[hb][2] + p[hb][3]);
+            } else {
+                // the weights PV uses, and their sum, are the bf16-rounded ones
+                pk[hb][0] = pack_bf16_rne(p[hb][0], p[hb][1]);
+                pk[hb][1] = pack_bf16_rne(p[hb][2], p[hb][3]);
+                psum = (bf16lo(pk[hb][0]) + bf16hi(pk[hb][0])) +
+                       (bf16lo(pk[hb][1]) + bf16hi(pk[hb][1]));
             }
             S.l[hb] = S.l[hb] * alpha[hb] + psum;
             S.m[hb] = mnew;
@@ -380,23 +395,43 @@ struct MfmaCore {
         }
 
         // ---- PV ----------------------------------------------------------------
+        if constexpr (!Q8) {
+            // bf16 cache: one 4x4x4 bf16 product per dim e covers the row
+            // group's 4 tokens. A operand of lane (tg, qd, j4): dim
+            // 8*(4*qd + j4) + e of V rows 4k + tg, k = 0..3 (the lane's own
+            // loads, transposed by byte permutes); B: its 4 weights, k = 0..3.
+            // Rows past the context may hold NaN: their words are zeroed.
+            uint32_t w[4][4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const bool z = tail && c * CHUNK + 4 * k + tg >= t1;
+                w[k][0] = z ? 0u : cur.v[k].x;
+                w[k][1] = z ? 0u : cur.v[k].y;
+                w[k][2] = z ? 0u : cur.v[k].z;
+                w[k][3] = z ? 0u : cur.v[k].w;
+            }
+            i16x4 va[8];
+#pragma unroll
+            for (int n = 0; n < 4; ++n) {
+                va[2 * n] = as_i16x4(lo_halves(w[0][n], w[1][n]), lo_halves(w[2][n], w[3][n]));
+                va[2 * n + 1] = as_i16x4(hi_halves(w[0][n], w[1][n]), hi_halves(w[2][n], w[3][n]));
+            }
+#pragma unroll
+            for (int hb = 0; hb < NHB; ++hb) {
+                const i16x4 pb = as_i16x4(pk[hb][0], pk[hb][1]);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) S.acc[hb][e] = mfma4x4x4bf16(va[e], pb, S.acc[hb][e]);
+            }
+            return;
+        }
+        // int8 cache: fp32 4x4x1 products, the codes and p * v_scale in fp32
 #pragma unroll
         for (int step = 0; step < 4; ++step) {
             float vf[8];
-            if constexpr (Q8) {
 #pragma unroll
-                for (int n = 0; n < 4; ++n) {
-                    vf[n] = i8_at(cur.v[step].x, n);
-                    vf[4 + n] = i8_at(cur.v[step].y, n);
-                }
-            } else {
-                const uint32_t w4[4] = {cur.v[step].x, cur.v[step].y, cur.v[step].z,
-                                        cur.v[step].w};
-#pragma unroll
-                for (int n = 0; n < 4; ++n) {
-                    vf[2 * n] = bf16lo(w4[n]);
-                    vf[2 * n + 1] = bf16hi(w4[n]);
-                }
+            for (int n = 0; n < 4; ++n) {
+                vf[n] = i8_at(cur.v[step].x, n);
+                vf[4 + n] = i8_at(cur.v[step].y, n);
             }
             if (tail && c * CHUNK + 4 * step + tg >= t1) {
 #pragma unroll

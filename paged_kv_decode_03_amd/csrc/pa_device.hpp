@@ -28,6 +28,22 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return (uint16_t)(b >> 16);
 }
 
+// Two fp32 -> packed bf16 pair, each rounded to nearest even.
+__device__ __forceinline__ uint32_t pack_bf16_rne(float lo, float hi) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// Low halves (resp. high halves) of two packed bf16 pairs: x's in the low
+// half of the result, y's in the high half.
+__device__ __forceinline__ uint32_t lo_halves(uint32_t x, uint32_t y) {
+    return __builtin_amdgcn_perm(y, x, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t hi_halves(uint32_t x, uint32_t y) {
+    return __builtin_amdgcn_perm(y, x, 0x07060302u);
+}
+
 // Two small exact integers held as fp32 -> packed bf16 pair (upper halves).
 __device__ __forceinline__ uint32_t pack_bf16_trunc(float lo, float hi) {
     return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);

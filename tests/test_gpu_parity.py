@@ -215,7 +215,11 @@ def test_decode_parity(name, P):
 
 @pytest.mark.parametrize("name", ["cfg1", "cfg2s", "cfg5s", "g8_i8"])
 def test_splitk_partials(name):
-    """Each partition's (o_j, m_j, l_j) against the oracle's partials."""
+    """Each partition's (o_j, m_j, l_j) against the oracle's partials. With a
+    bf16 cache the MFMA kernel rounds each weight to bf16 before PV and sums the
+    rounded weights into l_j, so l_j is within the bf16 unit roundoff (2^-9,
+    bound here by 2^-8 with the fp32 sums) of the exact sum; fp32 weights are
+    within 1e-4."""
     case, dc, ok, ov, _ = prepared(name)
     P = 64
     S, Hq, D = case.S, case.Hq, case.D
@@ -230,12 +234,13 @@ def test_splitk_partials(name):
     sync()
     go, gm, gl = (t.cpu().numpy().astype(np.float64) for t in ws)
     n = -(-case.context_lens.astype(np.int64) // P)
+    l_tol = 2.0 ** -8 if case.spec.cache == "bf16" else 1e-4
     for s in range(S):
         assert np.isnan(go[s, :, n[s]:]).all(), "partition past the length was written"
         sl = slice(0, n[s])
         assert np.abs(go[s, :, sl] - o[s, :, sl]).max() <= tol(case)
         assert np.abs(gm[s, :, sl] - m[s, :, sl]).max() <= 1e-4 * max(1.0, np.abs(m[s, :, sl]).max())
-        assert np.abs(gl[s, :, sl] / l[s, :, sl] - 1).max() <= 1e-4
+        assert np.abs(gl[s, :, sl] / l[s, :, sl] - 1).max() <= l_tol
 
 
 def test_reduce_from_oracle_partials():
