@@ -2,7 +2,10 @@
 
 Every entry point enqueues only kernels (no allocation, no memset: the
 balanced schedule's counters are reset by the kernel itself), so a step can be
-captured once and replayed. Each test replays the graph several times, with
+captured once and replayed: the fused balanced step (with a caller workspace,
+or without one), write + split-K decode + reduce, and the default step on bf16
+batches (the write fused with the multi-query kernel, one pass or split with
+the reduce). Each test replays the graph several times, with
 eager launches of the same entry points and synchronisations in between, and
 checks every replay bit for bit against the eager result of the same step
 (the schedules are static, so eager and replayed results are the same bits),
@@ -47,6 +50,30 @@ def make_step(case, dc, k, v, out, schedule):
                                      dc.block_tables, dc.context_lens, scale, maxL, 64, *ws,
                                      k_scale=dc.k_scale, v_scale=dc.v_scale)
         return step, ws
+    if schedule == "noalloc":
+        def step():
+            pa.write_decode_balanced_noalloc(dc.key, dc.value, dc.slot_mapping, out, dc.q, k, v,
+                                             dc.block_tables, dc.context_lens, scale, maxL, 64,
+                                             k_scale=dc.k_scale, v_scale=dc.v_scale)
+        return step, None
+    if schedule.startswith("multi-query"):
+        # the default step on bf16 batches: pa_write_prefill with one query row
+        # per sequence, in one pass or split over P-token partitions + the reduce
+        P = int(schedule.split(":")[1]) if ":" in schedule else 0
+        qsl = torch.arange(case.S + 1, dtype=torch.int32, device="cuda")
+        ws = pa.prefill_workspace(case.S, case.Hq, case.D, maxL, P, "cuda") if P else None
+
+        def step():
+            if P:
+                pa.write_prefill(dc.key, dc.value, dc.slot_mapping, None, dc.q, k, v,
+                                 dc.block_tables, dc.context_lens, qsl, scale, 1, maxL,
+                                 partition_size=P, tmp_out=ws[0], tmp_max=ws[1], tmp_sum=ws[2],
+                                 row_lens=ws[3])
+                pa.decode_splitk_reduce(out, *ws[:3], ws[3], maxL, P)
+            else:
+                pa.write_prefill(dc.key, dc.value, dc.slot_mapping, out, dc.q, k, v,
+                                 dc.block_tables, dc.context_lens, qsl, scale, 1, maxL)
+        return step, ws
     P = case.spec.partition_size or 512
     ws = pa.workspace(case.S, case.Hq, case.D, maxL, P, "cuda")
 
@@ -60,7 +87,9 @@ def make_step(case, dc, k, v, out, schedule):
 
 @pytest.mark.parametrize("name,schedule", [("cfg2s", "fused"), ("cfg4s", "fused"),
                                            ("cfg5s", "fused"), ("cfg3s", "partitions"),
-                                           ("cfg2s", "partitions")])
+                                           ("cfg2s", "partitions"), ("cfg2s", "multi-query"),
+                                           ("cfg3s", "multi-query:2048"), ("cfg5s", "noalloc"),
+                                           ("cfg4s", "noalloc")])
 def test_graph_replays_match_eager(name, schedule):
     print(f"[graph] {name} {schedule}", flush=True)
     case = synth.make_case(SPECS[name], 21)

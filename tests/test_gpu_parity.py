@@ -132,9 +132,9 @@ def test_write_int8_near_ties():
         assert np.array_equal(dev_to_host(k), ok), act
 
 
-# Scales for the quantiser's two paths: ordinary ones (the reciprocal with its
-# boundary test), and ones whose reciprocal leaves the normal range or is not
-# finite (the division).
+# Scales across the quantiser's range: ordinary ones, and ones whose quotients
+# reach the subnormal, overflow, zero, negative, infinite and NaN cases of the
+# correctly rounded division.
 INT8_SCALES = [1 / 127, 0.0123, 3.7e-3, 1.0, 0.125, 5.3e-5, 2.0 ** -125, 2.0 ** -126, 1e-39,
                2.0 ** 125, 2.0 ** 126, 3e38, 0.0, -0.37, float("inf"), float("nan")]
 
