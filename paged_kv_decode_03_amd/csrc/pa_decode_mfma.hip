@@ -599,6 +599,313 @@ struct MfmaCore {
     }
 };
 
+// ---- 16x16 core: bf16 cache, balanced ring driver -----------------------------
+// The G query heads of a kv head as the columns of 16x16 MFMA tiles (G <= 16;
+// columns G..15 carry zero queries and their results are dropped). Lane
+// l = 16*qg + n:
+//  QK^T: S^T = K Q^T on v_mfma_f32_16x16x32_bf16, 4 per chunk: A = K row n,
+//    dims 32*kk + 8*qg .. +7 (one 16-byte LDS read), B = query head n, the same
+//    dims. The lane receives the logits of head n for tokens 4*qg + i.
+//  softmax: one running max per head, common to the 4 lanes holding its
+//    tokens (a max over lanes n, n^16, n^32, n^48 per chunk), lazy as in
+//    MfmaCore; each lane sums its own tokens' weights into l.
+//  PV: O^T += V^T P^T on v_mfma_f32_16x16x16_bf16, 8 per chunk (16 dims each):
+//    A = dims 16*j + n of V rows 4*qg .. +3 (one transposing LDS read), B = the
+//    lane's own 4 weights rounded to bf16, already in place. The lane then
+//    holds dims 16*j + 4*qg + i of head n, summed over all 16 tokens.
+// Per chunk and wave this is 12 MFMAs and about 40 other VALU instructions,
+// whatever G (MfmaCore at G = 8: 32 MFMAs and about 180).
+//
+// LDS layout of a ring slot (K tile, V tile, then a new token's rows): row r of
+// the K tile holds its 16-byte piece p at position p ^ r, row r of the V tile
+// at position p ^ 2*(r % 8), so the K operand reads (16 rows, one piece each)
+// and the transposing V reads (rows 4*qg .. +3, 32 bytes each) spread over the
+// banks. The direct loads write 16 bytes per lane at consecutive addresses, so
+// the permutation is applied to the global addresses the lanes read.
+template <int G_>
+struct Mfma16Core {
+    static constexpr int G = G_;
+    static constexpr int D = 128;
+    static constexpr bool BASE2 = true;
+    static constexpr float kSlack = 8.0f;
+    static_assert(G <= 16, "one 16-column tile of query heads");
+
+    struct State {
+        float m, l;
+        f32x4 acc[8];                            // acc[j][i]: dim 16*j + 4*qg + i, head n
+    };
+    struct Chunk {
+        uint4 k[4];                              // K operands, kk = 0..3
+        u32x2 v[8];                              // V^T operands, j = 0..7
+    };
+
+    static constexpr int KT = 16 * D * 2;        // bytes of one 16-token K (or V) tile
+    static constexpr int NDK = KT / 1024;        // 1 KB load instructions per tile
+    static constexpr int NEW = 2 * KT;           // then a new token's K and V rows, and its slot
+    static constexpr int SLOT = NEW + 4 * D + 16;
+    static constexpr int DPC = 2 * NDK;          // vector memory instructions per chunk
+    static constexpr int R = 2;                  // ring slots per wave
+
+    const DecodeArgs& a;
+    int lane, n, qg;
+    float sl2;
+    int shift;
+    int64_t head_stride, block_stride;
+    uint4 qr[4];                                 // query operands of the segment
+    uint32_t kdma[NDK], vdma[NDK];               // source byte offsets in a tile, per load
+    uint32_t krd[4];                             // LDS byte offsets of the K operands
+    uint32_t vrd[8];                             // LDS byte offsets of the V^T operands
+
+    __device__ explicit Mfma16Core(const DecodeArgs& args) : a(args) {
+        lane = threadIdx.x & 63;
+        n = lane & 15;
+        qg = lane >> 4;
+        sl2 = a.scale * kLog2e;
+        shift = (a.block_size == 32) ? 1 : 0;
+        head_stride = (int64_t)a.block_size * D;
+        block_stride = head_stride * a.num_kv_heads;
+#pragma unroll
+        for (int i = 0; i < NDK; ++i) {
+            // load i, lane 16*q + t lands at row 4i + q, position t
+            const int r = 4 * i + qg;
+            kdma[i] = r * 256 + 16 * (n ^ r);
+            vdma[i] = r * 256 + 16 * (n ^ (2 * (r & 7)));
+        }
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) krd[kk] = 256 * n + 16 * ((4 * kk + qg) ^ n);
+        // transposing read j: lane 4*k4 + q of the 16-lane group qg addresses
+        // V row 4*qg + k4, dims 16*j + 4*q .. +3 (8 bytes)
+        const int r = 4 * qg + (n >> 2), q = n & 3;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) vrd[j] = KT + 256 * r + 32 * (j ^ (r & 7)) + 8 * q;
+    }
+
+    __device__ void issue(char* slot, int s, int g, int c, bool fresh) const {
+        if (fresh) {
+            if (lane < 32) {                     // lanes 0..15: K, 16..31: V, 16 bytes each
+                const char* src = (const char*)(lane < 16 ? a.key : a.value);
+                dma16(src + (((int64_t)s * a.num_kv_heads + g) * D + 8 * (lane & 15)) * 2,
+                      slot + NEW);
+            }
+            if (lane < 2) dma4((const char*)(a.slot_mapping + s) + 4 * lane, slot + NEW + 4 * D);
+        }
+        const int phys = ld_uniform(a.block_tables, (int64_t)s * a.max_blocks_per_seq + (c >> shift));
+        const int64_t off = phys * block_stride + g * head_stride + (int64_t)(c & shift) * CHUNK * D;
+        const char* kt = (const char*)a.k_cache + off * 2;
+        const char* vt = (const char*)a.v_cache + off * 2;
+#pragma unroll
+        for (int i = 0; i < NDK; ++i) dma16(at(kt, kdma[i]), slot + 1024 * i);
+#pragma unroll
+        for (int i = 0; i < NDK; ++i) dma16(at(vt, vdma[i]), slot + KT + 1024 * i);
+    }
+
+    static __device__ void write_vector_at(const DecodeArgs& a, int s, int g, int v) {
+        write_vector<BF16, BF16>(a.key, a.value, const_cast<void*>(a.k_cache),
+                                 const_cast<void*>(a.v_cache), a.slot_mapping, a.k_scale,
+                                 a.v_scale, a.num_kv_heads, D, a.block_size, s, g, v);
+    }
+
+    // As MfmaCore::patch_new_token, for this layout: the new token's row o of
+    // the chunk was brought in by lanes 16*(o%4) + t of load o/4 (position t),
+    // which overwrite it with the new row's pieces t ^ o (K) and t ^ 2*(o%8) (V).
+    __device__ void patch_new_token(char* slot, int g, int L) const {
+        const uint32_t b = lds_addr(slot), nb = b + NEW;
+        u32x2 sv = ds_read8<4 * D>(nb);
+        lds_wait(sv);
+        const int64_t sl = uniform64((long long)(((uint64_t)sv.y << 32) | sv.x));
+        if (sl < 0) return;
+        const int o = (L - 1) & (CHUNK - 1);
+        const int64_t blk = sl >> (4 + shift), off = sl & (a.block_size - 1);
+        const int64_t row = ((blk * a.num_kv_heads + g) * a.block_size + off) * D;
+        if (lane < 32) {
+            u32x4 w = ds_read16(nb + 16 * lane);
+            lds_wait(w);
+            char* dst = (char*)(lane < 16 ? a.k_cache : a.v_cache) + (row + 8 * (lane & 15)) * 2;
+            *reinterpret_cast<uint4*>(dst) = make_uint4(w.x, w.y, w.z, w.w);
+        }
+        if (qg == (o & 3)) {
+            u32x4 kw = ds_read16(nb + 16 * (n ^ o));
+            u32x4 vw = ds_read16(nb + 2 * D + 16 * (n ^ (2 * (o & 7))));
+            lds_wait(kw, vw);
+            ds_write16(b + 1024 * (o >> 2) + 16 * lane, kw);
+            ds_write16(b + KT + 1024 * (o >> 2) + 16 * lane, vw);
+        }
+    }
+
+    __device__ Chunk fetch(const char* slot) const {
+        Chunk ch;
+        const uint32_t b = lds_addr(slot);
+        u32x4 k0 = ds_read16(b + krd[0]), k1 = ds_read16(b + krd[1]), k2 = ds_read16(b + krd[2]),
+              k3 = ds_read16(b + krd[3]);
+        u32x2 v0 = ds_read8_tr(b + vrd[0]), v1 = ds_read8_tr(b + vrd[1]),
+              v2 = ds_read8_tr(b + vrd[2]), v3 = ds_read8_tr(b + vrd[3]),
+              v4 = ds_read8_tr(b + vrd[4]), v5 = ds_read8_tr(b + vrd[5]),
+              v6 = ds_read8_tr(b + vrd[6]), v7 = ds_read8_tr(b + vrd[7]);
+        lds_wait(k0, k1, k2, k3, v0, v1, v2, v3, v4, v5, v6, v7);
+        ch.k[0] = make_uint4(k0.x, k0.y, k0.z, k0.w);
+        ch.k[1] = make_uint4(k1.x, k1.y, k1.z, k1.w);
+        ch.k[2] = make_uint4(k2.x, k2.y, k2.z, k2.w);
+        ch.k[3] = make_uint4(k3.x, k3.y, k3.z, k3.w);
+        ch.v[0] = v0; ch.v[1] = v1; ch.v[2] = v2; ch.v[3] = v3;
+        ch.v[4] = v4; ch.v[5] = v5; ch.v[6] = v6; ch.v[7] = v7;
+        return ch;
+    }
+
+    // Query head n of the segment (zero for n >= G; the load is clamped to a
+    // head of the segment), dims 32*kk + 8*qg .. +7.
+    __device__ void begin_segment(int s, int g) {
+        const uint16_t* q0 = (const uint16_t*)a.q + ((int64_t)s * a.num_heads + g * G) * D;
+        const int h = n < G ? n : 0;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const uint4 w = ld16(at(q0, 2 * (h * D + 32 * kk + 8 * qg)));
+            qr[kk] = n < G ? w : make_uint4(0, 0, 0, 0);
+        }
+    }
+
+    __device__ void init(State& S) const {
+        S.m = kNegInf;
+        S.l = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) S.acc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+
+    __device__ void step(State& S, const Chunk& cur, int c, int t1) const {
+        const bool tail = ((c + 1) * CHUNK) > t1;
+        f32x4 sacc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+            sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8_t, cur.k[kk]), __builtin_bit_cast(bf16x8_t, qr[kk]), sacc,
+                0, 0, 0);
+        float x[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            // x is rounded once; the max and exp2(x - max) see the same x
+            x[i] = sacc[i] * sl2;
+            if (tail && c * CHUNK + 4 * qg + i >= t1) x[i] = kNegInf;
+        }
+        float mloc = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+        mloc = fmaxf(mloc, lane_xor16(mloc));
+        mloc = fmaxf(mloc, lane_xor32(mloc));
+        const float mnew = (mloc > S.m + kSlack) ? mloc : S.m;
+        const float muse = (mnew == kNegInf) ? 0.0f : mnew;
+        const float alpha = __builtin_amdgcn_exp2f(S.m - muse);
+        float p[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(x[i] - muse);
+        // the weights PV uses, and their sum, are the bf16-rounded ones
+        const uint32_t pk0 = pack_bf16_rne(p[0], p[1]), pk1 = pack_bf16_rne(p[2], p[3]);
+        const float psum = (bf16lo(pk0) + bf16hi(pk0)) + (bf16lo(pk1) + bf16hi(pk1));
+        S.l = S.l * alpha + psum;
+        S.m = mnew;
+        if (__any(alpha != 1.0f)) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) S.acc[j] *= alpha;
+        }
+        // rows past the context may hold NaN: their bf16 halves are zeroed
+        uint32_t m01 = 0xffffffffu, m23 = 0xffffffffu;
+        if (tail) {
+            const int t0 = c * CHUNK + 4 * qg;
+            m01 = (t0 < t1 ? 0x0000ffffu : 0u) | (t0 + 1 < t1 ? 0xffff0000u : 0u);
+            m23 = (t0 + 2 < t1 ? 0x0000ffffu : 0u) | (t0 + 3 < t1 ? 0xffff0000u : 0u);
+        }
+        const i16x4 pb = as_i16x4(pk0, pk1);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            S.acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+                as_i16x4(cur.v[j].x & m01, cur.v[j].y & m23), pb, S.acc[j], 0, 0, 0);
+    }
+
+    // The 4 lanes of head n share m; their token sums add up.
+    __device__ void merge_rows(State& S) const {
+        S.l += lane_xor16(S.l);
+        S.l += lane_xor32(S.l);
+    }
+
+    // The lane's 4 values of dims 16*j + 4*qg .. +3 of head n as bf16.
+    __device__ void store4(int s, int g, int j, float v0, float v1, float v2, float v3) const {
+        uint16_t* o0 = (uint16_t*)a.out + ((int64_t)s * a.num_heads + g * G + n) * D;
+        const uint2 w = make_uint2(f32_to_bf16(v0) | ((uint32_t)f32_to_bf16(v1) << 16),
+                                   f32_to_bf16(v2) | ((uint32_t)f32_to_bf16(v3) << 16));
+        *reinterpret_cast<uint2*>(at(o0, 2 * (16 * j + 4 * qg))) = w;
+    }
+
+    __device__ void store_final(const State& S, int s, int g) const {
+        if (n >= G) return;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            store4(s, g, j, S.acc[j][0] / S.l, S.acc[j][1] / S.l, S.acc[j][2] / S.l,
+                   S.acc[j][3] / S.l);
+    }
+
+    // Workspace slot: tmp_out [G][D] (unnormalised), tmp_max / tmp_sum [G]
+    // (m base 2, l), all with coherent stores.
+    __device__ void store_slot(const State& S, int64_t slot) const {
+        if (n >= G) return;
+        const __amdgpu_buffer_rsrc_t rs = ws_rsrc(a.tmp_out + slot * (G * D), G * D * 4);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            ws_store16(rs, 4 * (n * D + 16 * j + 4 * qg), S.acc[j][0], S.acc[j][1], S.acc[j][2],
+                       S.acc[j][3]);
+        if (qg == 0) {
+            ws_store<true>(at(a.tmp_max + slot * G, 4 * n), S.m);
+            ws_store<true>(at(a.tmp_sum + slot * G, 4 * n), S.l);
+        }
+    }
+
+    // Log-sum-exp of the partials of pieces first .. first+np-1 of (s, g) into
+    // out (piece first + k left its partial in slot 2 (first + k) + (k == 0)),
+    // kBatch pieces at a time with a running maximum.
+    static constexpr int kBatch = 2;
+    __device__ void combine(long long first, int np, int s, int g) const {
+        if (n >= G) return;
+        const int64_t slot0 = 2 * first;
+        const __amdgpu_buffer_rsrc_t rs = ws_rsrc(a.tmp_out + slot0 * (G * D), (uint32_t)(2 * np) * (G * D * 4));
+        const __amdgpu_buffer_rsrc_t rm = ws_rsrc(a.tmp_max + slot0 * G, (uint32_t)(2 * np) * (G * 4));
+        const __amdgpu_buffer_rsrc_t rl = ws_rsrc(a.tmp_sum + slot0 * G, (uint32_t)(2 * np) * (G * 4));
+        float M = kNegInf, lsum = 0.0f;
+        f32x4 o[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int k0 = 0; k0 < np; k0 += kBatch) {
+            float mk[kBatch], lk[kBatch];
+            u32x4_t x[kBatch][8];
+#pragma unroll
+            for (int jj = 0; jj < kBatch; ++jj) {
+                const uint32_t k = (uint32_t)min(k0 + jj, np - 1);
+                const uint32_t sl = 2 * k + (k == 0 ? 1u : 0u);
+                mk[jj] = ws_load4(rm, 4 * (sl * G + n));
+                lk[jj] = ws_load4(rl, 4 * (sl * G + n));
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    x[jj][j] = ws_load16(rs, 4 * (sl * (G * D) + n * D + 16 * j + 4 * qg));
+            }
+            float Mb = M;
+#pragma unroll
+            for (int jj = 0; jj < kBatch; ++jj)
+                if (k0 + jj < np) Mb = fmaxf(Mb, mk[jj]);
+            const float sc = rel_weight<true>(M, Mb);
+            lsum *= sc;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) o[j] *= sc;
+#pragma unroll
+            for (int jj = 0; jj < kBatch; ++jj) {
+                const float W = (k0 + jj < np) ? rel_weight<true>(mk[jj], Mb) : 0.0f;
+                lsum += W * lk[jj];
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) o[j][i] += W * __uint_as_float(x[jj][j][i]);
+            }
+            M = Mb;
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            store4(s, g, j, o[j][0] / lsum, o[j][1] / lsum, o[j][2] / lsum, o[j][3] / lsum);
+    }
+};
+
 // Register budget per lane of the register-path kernel: 168 (3 waves per SIMD)
 // for G = 4, 256 (2 waves) for G = 8; enough resident waves to keep HBM busy
 // with one chunk in flight. The ring kernel is held to 2 waves per SIMD by its
@@ -617,10 +924,19 @@ void mfma_partitions(DecodeArgs a) {
 // measured to stream unevenly, the second one slower.
 constexpr int NWR = 8;
 
+// G = 8 with a bf16 cache runs the 16x16 core, the other instances MfmaCore.
+// Measured in one process (balanced fused step, pieces >= 128 tokens): the
+// mixed copy-on-write batch (G 8) 202.5 -> 197.3 us; at G = 4 the 16x16 core,
+// three quarters of whose MFMA columns are then idle, was slower (8 x 32768
+// batch 186.2 -> 195.1 us, Llama-shaped batch 67.3 -> 72.9 us).
+template <int G, Dtype CT>
+using RingCore =
+    typename std::conditional<CT == BF16 && G == 8, Mfma16Core<G>, MfmaCore<G, CT>>::type;
+
 template <int G, Dtype CT>
 __global__ __launch_bounds__(NWR * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void mfma_balanced(DecodeArgs a) {
-    decode_balanced_ring<MfmaCore<G, CT>, NWR>(a);
+    decode_balanced_ring<RingCore<G, CT>, NWR>(a);
 }
 
 template <int G, Dtype CT>

@@ -13,6 +13,7 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
 // ---- bf16 <-> fp32 -------------------------------------------------------
 
@@ -220,6 +221,15 @@ __device__ __forceinline__ void ds_write16(uint32_t addr, u32x4 v) {
 __device__ __forceinline__ void ds_write4(uint32_t addr, uint32_t v) {
     asm volatile("ds_write_b32 %0, %1" : : "v"(addr), "v"(v) : "memory");
 }
+// ds_read_b64_tr_b16: within each 16-lane group, lane i receives as its
+// element k (of four 16-bit elements) element i % 4 of the 8 bytes addressed
+// by lane 4k + i/4.
+template <int OFF = 0>
+__device__ __forceinline__ u32x2 ds_read8_tr(uint32_t addr) {
+    u32x2 v;
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF) : "memory");
+    return v;
+}
 // Wait for the LDS reads above; the operands tie their results to this point so
 // that no use is scheduled before it.
 __device__ __forceinline__ void lds_wait(u32x4& a) {
@@ -233,6 +243,15 @@ __device__ __forceinline__ void lds_wait(u32x2& a) {
 }
 __device__ __forceinline__ void lds_wait(u32x2& a, u32x2& b) {
     asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b) : : "memory");
+}
+__device__ __forceinline__ void lds_wait(u32x4& a, u32x4& b, u32x4& c, u32x4& d, u32x2& e, u32x2& f,
+                                         u32x2& g, u32x2& h, u32x2& i, u32x2& j, u32x2& k,
+                                         u32x2& l) {
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(a), "+v"(b), "+v"(c), "+v"(d), "+v"(e), "+v"(f), "+v"(g), "+v"(h),
+                   "+v"(i), "+v"(j), "+v"(k), "+v"(l)
+                 :
+                 : "memory");
 }
 __device__ __forceinline__ void lds_wait(u32x4& a, u32x4& b, u32x4& c, u32x4& d, u32x4& e, u32x4& f,
                                          u32x4& g, u32x4& h) {
