@@ -31,7 +31,7 @@ namespace pa {
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr int NW = 4;        // waves per workgroup
 constexpr int CHUNK = 16;    // tokens per chunk
-constexpr int kFastShare = 144;   // see balanced_setup
+constexpr int kFastShare = 160;   // see balanced_setup
 constexpr int kChunkCost = 16;    // cost units per chunk (see balanced_setup)
 constexpr int kSegCost = 32;      // cost units per segment (see balanced_setup)
 constexpr int kSegCostG8 = 96;    // the same, 8 or more query heads per kv head
@@ -442,7 +442,9 @@ __device__ __forceinline__ bool balanced_setup(const DecodeArgs& a, BalancedShar
     // instruction issue: with equal ranges it finished 1.2-1.35x sooner, then
     // sat idle while the younger one ran alone. It gets a share kFastShare/256
     // of the pair's cost. (The CU's waves share one bandwidth, so this mostly
-    // shortens the idle time rather than the launch: 0-4% faster measured.)
+    // shortens the idle time rather than the launch: 0-4% faster measured.
+    // Shares of 128, 144, 160, 176 and 192 measured in one process: 160 was
+    // best or level on all four batches, 1.7% faster than 144 on the int8 one.)
     // Every range keeps at least the cost of a minimum piece, cmin.
     Ranges rg;
     if (NWG == 8) {
