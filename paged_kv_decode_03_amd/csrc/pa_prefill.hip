@@ -143,7 +143,13 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     constexpr int NLD = TK * PPR / TPT;               // pieces per thread per tile (K, and V)
     static_assert(TK * PPR % TPT == 0, "tile split");
     constexpr int ELT = I8 ? 1 : 2;
-    __shared__ __attribute__((aligned(16))) char lds[NT * TGBYTES];
+    // Tiles in flight in registers: two where a tile takes at most 2 pieces
+    // per thread and pool (16 VGPRs: the 128-row instances, whose 4 waves
+    // fill one tile together), one otherwise (a second would leave one wave
+    // per SIMD). With two, each token group also has two LDS buffers used in
+    // turn, and one barrier per tile suffices.
+    constexpr int DEPTH = NLD <= 2 ? 2 : 1;
+    __shared__ __attribute__((aligned(16))) char lds[DEPTH * NT * TGBYTES];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int rg = wave % NR, tg = wave / NR;
@@ -268,8 +274,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     // this thread's pieces of a tile: piece p = ti + k TPT is token p / PPR,
     // elements (p % PPR) * EPP ..
     const int ti = rg * 64 + lane;
-    // one tile in flight in registers (two would leave one wave per SIMD)
-    uint4 kr[NLD], vr[NLD];
+    uint4 kr[NLD], vr[NLD], kr2[NLD], vr2[NLD];
     // A piece's address: the (block, kv head) tile's base, a scalar, plus
     // the lane's offset inside the tile (a tile starts on a block boundary,
     // so token t of the tile is row t % B of its block).
@@ -290,7 +295,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
             base[hf] = kt * TK + 16 * hf < limit
                 ? (int64_t)ld_uniform(bt, (kt * TK + 16 * hf) / B) * blk_stride + head_off : 0;
     };
-    auto load_tile = [&](int kt, const int64_t (&base)[2]) {
+    auto load_tile = [&](int kt, const int64_t (&base)[2], uint4 (&kr)[NLD], uint4 (&vr)[NLD]) {
         // WR: bit t set when token kt TK + t is a new token with a negative
         // slot: it is not written, so its position is read from the cache
         // like any other (scalar loads, only for tiles that hold new tokens)
@@ -335,7 +340,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
             }
         }
     };
-    char* kl = lds + tg * TGBYTES;
+    char* kl = lds + tg * TGBYTES;                    // the token group's buffer in use
     char* vl = kl + KBYTES;
     // this lane's address in the transposed V reads (see the file comment)
     const int vtr = (4 * quad + col / 4) * KSTR + 8 * (col % 4);
@@ -395,44 +400,62 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
                     acc[mb][tt] = mfma16x16x32(kop, qop[mb][ks], acc[mb][tt]);
             }
         bf16x8 pop[MB];
+        if constexpr (!I8) {
+            // every row block's max first, then one wave-uniform test for the
+            // (rare) rescale of any of them, then the weights: no branch
+            // separates the row blocks' exponentials and sums
+            float mn[MB];
+            bool grow = false;
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                // max over the unscaled products (fq >= 0), masked ones excluded
+                float mx = -__builtin_huge_valf();
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const bool msk = EDGE && kt * TK + tt * 16 + 4 * quad + i > rpos[mb];
+                        mx = fmaxf(mx, msk ? -__builtin_huge_valf() : acc[mb][tt][i]);
+                    }
+                mx = fmaxf(mx, lane_xor16(mx));
+                mx = fmaxf(mx, lane_xor32(mx));
+                const float mxs = mx == -__builtin_huge_valf() ? mx : mx * fq;
+                mn[mb] = fmaxf(m[mb], mxs);
+                grow = grow || mn[mb] > m[mb] + kLazy;
+            }
+            if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) {
+                    if (__builtin_amdgcn_ballot_w64(mn[mb] > m[mb] + kLazy) != 0) {   // wave-uniform
+                        const float mu = mn[mb] == -__builtin_huge_valf() ? 0.0f : mn[mb];
+                        const float alpha = __builtin_amdgcn_exp2f(m[mb] - mu);
+                        m[mb] = mn[mb];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) lsum[mb][i] *= alpha;
+#pragma unroll
+                        for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) o[mb][dt][i] *= alpha;
+                    }
+                }
+            }
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                const float nmu = m[mb] == -__builtin_huge_valf() ? 0.0f : -m[mb];
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        float pr = __builtin_amdgcn_exp2f(fmaf(acc[mb][tt][i], fq, nmu));
+                        if (EDGE && kt * TK + tt * 16 + 4 * quad + i > rpos[mb]) pr = 0.0f;
+                        pop[mb][4 * tt + i] = (__bf16)pr;
+                    }
+                lsum[mb] = mfma16x16x32(ones, pop[mb], lsum[mb]);
+            }
+        } else {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-          if constexpr (!I8) {
-            // max over the unscaled products (fq >= 0), masked ones excluded
-            float mx = -__builtin_huge_valf();
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const bool msk = EDGE && kt * TK + tt * 16 + 4 * quad + i > rpos[mb];
-                    mx = fmaxf(mx, msk ? -__builtin_huge_valf() : acc[mb][tt][i]);
-                }
-            mx = fmaxf(mx, lane_xor16(mx));
-            mx = fmaxf(mx, lane_xor32(mx));
-            const float mxs = mx == -__builtin_huge_valf() ? mx : mx * fq;
-            const float mn = fmaxf(m[mb], mxs);
-            if (__builtin_amdgcn_ballot_w64(mn > m[mb] + kLazy) != 0) {   // wave-uniform
-                const float mu = mn == -__builtin_huge_valf() ? 0.0f : mn;
-                const float alpha = __builtin_amdgcn_exp2f(m[mb] - mu);
-                m[mb] = mn;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) lsum[mb][i] *= alpha;
-#pragma unroll
-                for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) o[mb][dt][i] *= alpha;
-            }
-            const float nmu = m[mb] == -__builtin_huge_valf() ? 0.0f : -m[mb];
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    float pr = __builtin_amdgcn_exp2f(fmaf(acc[mb][tt][i], fq, nmu));
-                    if (EDGE && kt * TK + tt * 16 + 4 * quad + i > rpos[mb]) pr = 0.0f;
-                    pop[mb][4 * tt + i] = (__bf16)pr;
-                }
-            lsum[mb] = mfma16x16x32(ones, pop[mb], lsum[mb]);
-          } else {
+          {
             float x[2][4];
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) {
@@ -472,6 +495,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
             lsum[mb] = mfma16x16x32(ones, pop[mb], lsum[mb]);
           }
         }
+        }
         // O^T += V^T P^T, each V^T operand read right before its MFMAs. The k
         // slots 0-3 of a lane are tokens of the tile's first 16-token half and
         // slots 4-7 of its second, so on an int8 cache the product splits into
@@ -510,20 +534,39 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     // (the barrier counts are the same in every wave).
     // With one row group a token group is one wave, alone on its buffer: its
     // LDS accesses are performed in issue order, so no barrier is needed.
+    // With two tiles in flight every iteration issues the loads of tile
+    // it + 2, also past the last tile (such a tile reads in-bounds cache
+    // memory, as spare tiles do, and is never computed): with the loads
+    // unconditional the compiler's wait before storing a tile counts exactly
+    // the other tile's loads as still in flight (conditional loads made it
+    // wait for both).
     int64_t bnext[2] = {0, 0};
-    if (nit > 0) {
+    if (DEPTH == 2 || nit > 0) {
         tile_bases(kt0 + tg, bnext);
-        load_tile(kt0 + tg, bnext);
+        load_tile(kt0 + tg, bnext, kr, vr);
     }
-    if (nit > 1) tile_bases(kt0 + tg + NT, bnext);
-    for (int it = 0; it < nit; ++it) {
+    if (DEPTH == 2) {
+        tile_bases(kt0 + tg + NT, bnext);
+        load_tile(kt0 + tg + NT, bnext, kr2, vr2);
+    }
+    if (DEPTH == 2 || nit > DEPTH) tile_bases(kt0 + tg + DEPTH * NT, bnext);
+    // Iteration it: its tile (in kr/vr) to LDS, tile it + DEPTH into the same
+    // registers, the block ids of tile it + DEPTH + 1 requested, then tile it
+    // computed.
+    // With one LDS buffer the barrier before the store waits for the previous
+    // tile's reads. With two, buffer b is written again two tiles later, after
+    // the next tile's barrier, which every wave reaches only once it has
+    // computed from b.
+    auto iteration = [&](int it, uint4 (&kr)[NLD], uint4 (&vr)[NLD], int buf) {
         const int kt = kt0 + it * NT + tg;
-        if constexpr (NR > 1) __syncthreads();        // the previous tile's reads are done
+        kl = lds + (buf * NT + tg) * TGBYTES;
+        vl = kl + KBYTES;
+        if constexpr (NR > 1 && DEPTH == 1) __syncthreads();
         store_tile(kr, vr);
         if constexpr (NR > 1) __syncthreads();
-        if (it + 1 < nit) {
-            load_tile(kt + NT, bnext);
-            if (it + 2 < nit) tile_bases(kt + 2 * NT, bnext);
+        if (DEPTH == 2 || it + DEPTH < nit) {
+            load_tile(kt + DEPTH * NT, bnext, kr, vr);
+            if (DEPTH == 2 || it + DEPTH + 1 < nit) tile_bases(kt + (DEPTH + 1) * NT, bnext);
         }
         if (kt < nkt) {
             if (kt * TK + TK - 1 > p_first)
@@ -531,6 +574,18 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
             else
                 compute(kt, std::false_type{});
         }
+    };
+    if constexpr (DEPTH == 2) {
+        // both halves unconditional inside the loop (see above), the odd
+        // last tile after it
+        int it = 0;
+        for (; it + 1 < nit; it += 2) {
+            iteration(it, kr, vr, 0);
+            iteration(it + 1, kr2, vr2, 1);
+        }
+        if (it < nit) iteration(it, kr, vr, 0);
+    } else {
+        for (int it = 0; it < nit; ++it) iteration(it, kr, vr, 0);
     }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) l[mb] = lsum[mb][0];   // already the whole row's sum

@@ -164,13 +164,22 @@ def model_launch(lens, qlens, Hq, Hkv, B, i8=False, wr=False, P=0, max_query_len
         # kt0 + it NT + tg for it < nit (the spares of the last iteration
         # included), each with the block ids tile_bases fetched for that same
         # tile (fetched one tile ahead into bnext, which is overwritten only
-        # after the load that uses it has been issued)
-        kts = (kt0 + np.arange(nit)[:, None] * NT + np.arange(NT)[None, :]).reshape(-1)
+        # after the load that uses it has been issued). With two register
+        # tiles in flight (a tile of at most 2 pieces per thread and pool) the
+        # loads are unconditional: tiles it < nit + 2 are loaded and the block
+        # ids of it < nit + 3 fetched.
+        depth = 2 if NLD <= 2 else 1
+        n_load = nit + 2 if depth == 2 else nit
+        n_bases = nit + 3 if depth == 2 else nit
+        kts = (kt0 + np.arange(n_load)[:, None] * NT + np.arange(NT)[None, :]).reshape(-1)
+        kbs = (kt0 + np.arange(n_bases)[:, None] * NT + np.arange(NT)[None, :]).reshape(-1)
+        for hf in range(2):                            # tile_bases, every tile asked for
+            T0 = kbs * TK + 16 * hf
+            check(T0[T0 < limit] // B < nvalid, "block-table entry past the context")
         fetched = []
-        for hf in range(2):                            # tile_bases
+        for hf in range(2):                            # the bases each loaded tile uses
             T0 = kts * TK + 16 * hf
             f = T0 < limit
-            check(T0[f] // B < nvalid, "block-table entry past the context")
             fetched.append(f)
         if wr:                                         # load_tile: the tile's new-token slots
             j0 = kts * TK - new0
