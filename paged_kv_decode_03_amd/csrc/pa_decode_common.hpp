@@ -34,7 +34,7 @@ constexpr int CHUNK = 16;    // tokens per chunk
 constexpr int kFastShare = 160;   // see balanced_setup
 constexpr int kChunkCost = 16;    // cost units per chunk (see balanced_setup)
 constexpr int kSegCost = 32;      // cost units per segment (see balanced_setup)
-constexpr int kSegCostG8 = 96;    // the same, 8 or more query heads per kv head
+constexpr int kSegCostG8 = 64;    // the same, 8 or more query heads per kv head
 
 
 template <bool BASE2>
@@ -350,9 +350,10 @@ __device__ __forceinline__ bool balanced_setup(const DecodeArgs& a, BalancedShar
     // 24 and 48 units were 4-5% slower where all contexts have one length,
     // as the cuts then fall just off the segment boundaries. With eight query
     // heads to a kv head the fixed work is larger (twice the query rows and
-    // partial states to merge): 96 units there were 1-2% faster on the mixed
-    // batch than 32, 128 and more slower again. (kSegCost below stands for
-    // whichever applies.)
+    // partial states to merge): with the 4x4 core 96 units were 1-2% faster
+    // on the mixed batch than 32, 128 and more slower again; with the 16x16
+    // core (G = 8, bf16) 32 and 64 units were both 1.2% faster than 96, 0 level
+    // with it. (kSegCost below stands for whichever applies.)
     // Segment order. Sequence major (the 8 kv heads of a sequence in a row):
     // chunk c of segment (s, g) spans the units from
     // P = Y_s Hkv + g (n_s kChunkCost + kSegCost) + kSegCost + c kChunkCost,

@@ -33,7 +33,7 @@ import pytest
 
 import synth
 
-CHUNK, CC, SC4, SC8, FAST, TAIL = 16, 16, 32, 96, 144, 48
+CHUNK, CC, SC4, SC8, FAST, TAIL = 16, 16, 32, 64, 160, 48
 
 
 class Plan:
