@@ -30,8 +30,16 @@
  *
  * Conventions used by every entry point
  *  - All data pointers are DEVICE pointers owned by the caller. The library
- *    allocates nothing, keeps no state between calls, and may be called from
- *    several host threads at once.
+ *    allocates nothing, keeps no state between calls (beyond a cache of grid
+ *    sizes per kernel and device), and may be called from several host
+ *    threads at once -- except pa_write_decode_balanced_noalloc, whose
+ *    workspace is one static array per GPU, so its calls must not overlap.
+ *  - Precision: dot products and sums accumulate in fp32. The MFMA kernels
+ *    (4 or 8 query heads per kv head with a bf16 cache, and pa_prefill) round
+ *    the softmax weights to bf16 for the P V product and sum those same
+ *    rounded weights; the VALU kernels (1 or 2 query heads per kv head) and
+ *    the decode kernels on an int8 cache keep the weights, and the V scale,
+ *    in fp32.
  *  - All tensors are dense, row-major, with the layouts given per argument.
  *    The KV pool is [num_blocks][num_kv_heads][block_size][head_dim]: the
  *    block_size x head_dim tile of one (block, kv head) is contiguous.
