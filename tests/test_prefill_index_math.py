@@ -45,7 +45,9 @@ def snake_seq(lens, p):
     """Sequence taking place p of the XCD-contiguous list (snake_place)."""
     S = len(lens)
     per = S // 8
-    x, j = p // per, p % per
+    x, j0 = p // per, p % per
+    half = per // 2
+    j = j0 if j0 < half else per - 1 - (j0 - half)   # the run's second half reversed
     r = 8 * j + (7 - x if j & 1 else x)
     order = sorted(range(S), key=lambda t: (-int(lens[t]), t))   # rank r -> sequence
     return order[r]
@@ -315,7 +317,7 @@ def test_planted_jn_bound_is_caught():
 def test_snake_place_is_a_permutation():
     """Every sequence gets exactly one place (ties in length broken by index)."""
     rng = np.random.default_rng(0)
-    for S in (8, 64, 256):
+    for S in (8, 40, 64, 72, 256):
         lens = rng.integers(1, 40, size=S)
         got = sorted(snake_seq(lens, p) for p in range(S))
         assert got == list(range(S))
