@@ -99,26 +99,31 @@ struct SeqPlace {
 // the places are dealt by length: the sequences ranked by context length
 // (longest first, ties by index) go to the 8 XCDs' runs of the list in a
 // snake (ranks 0-7 to XCDs 0-7, ranks 8-15 to XCDs 7-0, ...); within a run
-// the first half is longest first and the second half shortest first. Every
-// XCD then gets about the same share of the KV, each CU a long and a short
-// context, and the longest contexts start first. S = 8 runs of S / 8 places,
+// longest first, or (pair) the first half longest first and the second half
+// shortest first. Every XCD then gets about the same share of the KV, with
+// pair each CU a long and a short context, and the longest contexts start
+// first. S = 8 runs of S / 8 places,
 // S <= blockDim.x;
 // all threads of the workgroup call it (it has barriers). The lengths and
 // query starts are read once, into LDS (sh: 2 S + 2 ints, free again on
 // return), and the sequence's own values are taken from there.
-__device__ SeqPlace snake_place(const int32_t* lens, const int32_t* qsl, int S, int p, int* sh) {
+__device__ SeqPlace snake_place(const int32_t* lens, const int32_t* qsl, int S, int p, int* sh,
+                                bool pair) {
     const int t = threadIdx.x;
     int* shq = sh + S;                                // S + 1 query starts
     if (t < S) sh[t] = lens[t];
     for (int i = t; i <= S; i += blockDim.x) shq[i] = qsl[i];
     __syncthreads();
-    // the run's second half in reverse (longest of it last): the XCD's
-    // workgroups fill its CUs' first slots in run order, then their second
-    // slots, so run positions j and j + per / 2 share a CU, which then holds
-    // a long and a short context (on the Llama-shaped batch 63.4 -> 60.8 us,
-    // verify 63.3 -> 59.8 us, against both halves longest first)
+    // pair (every workgroup resident at once): the run's second half in
+    // reverse. The XCD's workgroups fill its CUs' first slots in run order,
+    // then their second slots, so run positions j and j + per / 2 share a CU,
+    // which then holds a long and a short context (Llama-shaped batch 63.4 ->
+    // 60.8 us, verify 63.3 -> 59.8 us, against both halves longest first).
+    // With more workgroups than slots the run stays longest first, which
+    // starts the longest contexts first (the int8 batch, 128 sequences: 139.7
+    // us longest first, 152.7 us paired).
     const int per = S / 8, x = p / per, j0 = p % per, half = per / 2;
-    const int j = j0 < half ? j0 : per - 1 - (j0 - half);
+    const int j = (!pair || j0 < half) ? j0 : per - 1 - (j0 - half);
     const int r = 8 * j + ((j & 1) ? 7 - x : x);
     if (t < S) {
         const int Lt = sh[t];
@@ -191,7 +196,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     if (a.row_tiles == 1 && NP == 1 && W % 8 == 0 && a.num_seqs % 8 == 0 &&
         a.num_seqs <= kSnakeMax) {
         sp = snake_place(a.context_lens, a.query_start_loc, a.num_seqs, sg / Hkv,
-                         reinterpret_cast<int*>(lds));
+                         reinterpret_cast<int*>(lds), a.one_round != 0);
     } else {
         sp.s = sg / Hkv;
         sp.q0 = ld_const(a.query_start_loc, sp.s);
@@ -684,14 +689,22 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     }
 }
 
+template <int NR, int MB, bool I8, int BS, bool WR>
+void launch_one(PrefillArgs a, dim3 grid, hipStream_t st) {
+    const void* fn = reinterpret_cast<const void*>(&prefill_kernel<NR, MB, I8, BS, WR>);
+    const int resident = balanced_grid(fn, 256, st);  // workgroups the device holds at once
+    a.one_round = resident > 0 && (int64_t)grid.x <= resident;
+    hipLaunchKernelGGL((prefill_kernel<NR, MB, I8, BS, WR>), grid, dim3(256), 0, st, a);
+}
+
 template <int NR, int MB, int BS>
 void launch_bs(const PrefillArgs& a, dim3 grid, hipStream_t st) {
     if (a.cache == Dtype::I8)
-        hipLaunchKernelGGL((prefill_kernel<NR, MB, true, BS, false>), grid, dim3(256), 0, st, a);
+        launch_one<NR, MB, true, BS, false>(a, grid, st);
     else if (a.key)
-        hipLaunchKernelGGL((prefill_kernel<NR, MB, false, BS, true>), grid, dim3(256), 0, st, a);
+        launch_one<NR, MB, false, BS, true>(a, grid, st);
     else
-        hipLaunchKernelGGL((prefill_kernel<NR, MB, false, BS, false>), grid, dim3(256), 0, st, a);
+        launch_one<NR, MB, false, BS, false>(a, grid, st);
 }
 
 template <int NR, int MB>

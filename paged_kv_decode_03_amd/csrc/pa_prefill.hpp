@@ -40,6 +40,7 @@ struct PrefillArgs {
     void* k_cache_w = nullptr;       // k_cache / v_cache, writable
     void* v_cache_w = nullptr;
     int row_tiles = 0;               // set by the launcher: row tiles per (sequence, kv head)
+    int one_round = 0;               // set by the launcher: every workgroup resident at once
 };
 
 bool prefill_supports(const PrefillArgs& a);

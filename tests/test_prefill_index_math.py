@@ -41,13 +41,14 @@ def launch_shape(max_query_len, G):
     return 4, 2, (rows + 127) // 128
 
 
-def snake_seq(lens, p):
-    """Sequence taking place p of the XCD-contiguous list (snake_place)."""
+def snake_seq(lens, p, pair=True):
+    """Sequence taking place p of the XCD-contiguous list (snake_place); pair:
+    every workgroup resident at once, the run's second half reversed."""
     S = len(lens)
     per = S // 8
     x, j0 = p // per, p % per
     half = per // 2
-    j = j0 if j0 < half else per - 1 - (j0 - half)   # the run's second half reversed
+    j = j0 if (not pair or j0 < half) else per - 1 - (j0 - half)
     r = 8 * j + (7 - x if j & 1 else x)
     order = sorted(range(S), key=lambda t: (-int(lens[t]), t))   # rank r -> sequence
     return order[r]
@@ -122,7 +123,8 @@ def model_launch(lens, qlens, Hq, Hkv, B, i8=False, wr=False, P=0, max_query_len
         sg = rest // NP
         part = (rest + sg) % NP if spread else rest % NP
         g = sg % Hkv
-        s = snake_seq(lens, sg // Hkv) if snake else sg // Hkv
+        # one round on MI355X: two workgroups per CU for these instances, 256 CUs
+        s = snake_seq(lens, sg // Hkv, pair=W <= 512) if snake else sg // Hkv
         check(0 <= s < S, "sequence index")
         q0, n, L = int(qsl[s]), int(qlens[s]), int(lens[s])
         tiles = (n * G + RT - 1) // RT
@@ -319,5 +321,6 @@ def test_snake_place_is_a_permutation():
     rng = np.random.default_rng(0)
     for S in (8, 40, 64, 72, 256):
         lens = rng.integers(1, 40, size=S)
-        got = sorted(snake_seq(lens, p) for p in range(S))
-        assert got == list(range(S))
+        for pair in (False, True):
+            got = sorted(snake_seq(lens, p, pair) for p in range(S))
+            assert got == list(range(S))
