@@ -125,6 +125,18 @@ __device__ __forceinline__ void store_final(const WaveStates<G, D>& st, const De
     }
 }
 
+// Whether logical block lb of sequence s (its block-table entry at index ri,
+// holding phys) is also logical block lb of the previous or the next
+// sequence: a block that neighbouring sequences share copy-on-write, and that
+// other waves will read again. Only a cache hint rides on the answer, so
+// entries past a neighbour's context (unused, of any value) do no harm.
+__device__ __forceinline__ bool block_shared(const DecodeArgs& a, int s, int64_t ri, int phys) {
+    const int64_t prev = s > 0 ? ri - a.max_blocks_per_seq : ri;
+    const int64_t next = s + 1 < a.num_seqs ? ri + a.max_blocks_per_seq : ri;
+    const int bp = ld_uniform(a.block_tables, prev), bn = ld_uniform(a.block_tables, next);
+    return (prev != ri && bp == phys) || (next != ri && bn == phys);
+}
+
 // Workspace accesses. COHERENT ones are agent-scope relaxed atomics: on
 // gfx950 they bypass the per-XCD L2 (sc1), so a partial stored by one
 // workgroup is read back intact by a workgroup on another XCD without any
@@ -697,6 +709,7 @@ __device__ __forceinline__ void decode_balanced_ring(const DecodeArgs& a) {
     char* const mine = ring + uniform(threadIdx.x >> 6) * (R * SLOT);
     SegPos cur = r.cur;
     Core core(a);
+    core.cow = r.hm;
     const int n = (int)(r.X1 - r.X0);                // chunks in the range (>= 1)
     SegPos ahead = cur;                              // next chunk to issue
     int issued = 0;

@@ -67,6 +67,7 @@ struct MfmaCore {
     };
 
     const DecodeArgs& a;
+    bool cow = false;    // neighbouring sequences share blocks: stream the others (issue)
     int lane, j4, qd, tg;
     uint32_t k_off, v_off;                       // byte offsets inside a chunk
     float sl2;
@@ -134,7 +135,11 @@ struct MfmaCore {
     // Start the loads of chunk c of segment (s, g) into ring slot `slot`
     // (DPC vector memory instructions; two more with `fresh`, which also load
     // sequence s's new K and V rows of kv head g from key / value, and its
-    // slot_mapping entry).
+    // slot_mapping entry). In a batch with copy-on-write sharing (cow), a
+    // block that no neighbouring sequence shares is loaded non-temporal, so
+    // that the L2 keeps the shared prefix blocks, which the other sequences of
+    // the group read again: on the mixed batch (four 64-sequence groups) HBM
+    // traffic 1.30x -> 1.04x the algorithmic bytes, 213.0 -> 205.3 us.
     __device__ void issue(char* slot, int s, int g, int c, bool fresh) const {
         if (fresh) {
             if (lane < 32) {                     // lanes 0..15: K, 16..31: V, 16 bytes each
@@ -144,14 +149,22 @@ struct MfmaCore {
             }
             if (lane < 2) dma4((const char*)(a.slot_mapping + s) + 4 * lane, slot + NEW + 4 * D);
         }
-        const int phys = ld_uniform(a.block_tables, (int64_t)s * a.max_blocks_per_seq + (c >> shift));
+        const int64_t ri = (int64_t)s * a.max_blocks_per_seq + (c >> shift);
+        const int phys = ld_uniform(a.block_tables, ri);
         const int64_t off = phys * block_stride + g * head_stride + (int64_t)(c & shift) * CHUNK * D;
         const char* kt = (const char*)a.k_cache + off * CE;
         const char* vt = (const char*)a.v_cache + off * CE;
+        auto tiles = [&](auto nt) {
 #pragma unroll
-        for (int i = 0; i < NDK; ++i) dma16(at(kt, kdma[i]), slot + 1024 * i);
+            for (int i = 0; i < NDK; ++i) dma16p<nt()>(at(kt, kdma[i]), slot + 1024 * i);
 #pragma unroll
-        for (int i = 0; i < NDK; ++i) dma16(at(vt + 1024 * i, 16u * lane), slot + KT + 1024 * i);
+            for (int i = 0; i < NDK; ++i)
+                dma16p<nt()>(at(vt + 1024 * i, 16u * lane), slot + KT + 1024 * i);
+        };
+        if (cow && !block_shared(a, s, ri, phys))
+            tiles(std::true_type{});
+        else
+            tiles(std::false_type{});
         if constexpr (Q8) {
             if (lane == 0) {
                 dma4(a.k_scale + (int64_t)phys * a.num_kv_heads + g, slot + 2 * KT);
@@ -647,6 +660,7 @@ struct Mfma16Core {
     static constexpr int R = 2;                  // ring slots per wave
 
     const DecodeArgs& a;
+    bool cow = false;    // as MfmaCore::cow
     int lane, n, qg;
     float sl2;
     int shift;
@@ -689,14 +703,21 @@ struct Mfma16Core {
             }
             if (lane < 2) dma4((const char*)(a.slot_mapping + s) + 4 * lane, slot + NEW + 4 * D);
         }
-        const int phys = ld_uniform(a.block_tables, (int64_t)s * a.max_blocks_per_seq + (c >> shift));
+        const int64_t ri = (int64_t)s * a.max_blocks_per_seq + (c >> shift);
+        const int phys = ld_uniform(a.block_tables, ri);
         const int64_t off = phys * block_stride + g * head_stride + (int64_t)(c & shift) * CHUNK * D;
         const char* kt = (const char*)a.k_cache + off * 2;
         const char* vt = (const char*)a.v_cache + off * 2;
+        auto tiles = [&](auto nt) {
 #pragma unroll
-        for (int i = 0; i < NDK; ++i) dma16(at(kt, kdma[i]), slot + 1024 * i);
+            for (int i = 0; i < NDK; ++i) dma16p<nt()>(at(kt, kdma[i]), slot + 1024 * i);
 #pragma unroll
-        for (int i = 0; i < NDK; ++i) dma16(at(vt, vdma[i]), slot + KT + 1024 * i);
+            for (int i = 0; i < NDK; ++i) dma16p<nt()>(at(vt, vdma[i]), slot + KT + 1024 * i);
+        };
+        if (cow && !block_shared(a, s, ri, phys))
+            tiles(std::true_type{});
+        else
+            tiles(std::false_type{});
     }
 
     static __device__ void write_vector_at(const DecodeArgs& a, int s, int g, int v) {

@@ -188,6 +188,12 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ void dma16(const void* g, void* lds) {
     __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 16, 0, 0);
 }
+// The same with the non-temporal hint (NT): the L2 keeps the line for as
+// short a time as it can, leaving its room to lines that are read again.
+template <bool NT>
+__device__ __forceinline__ void dma16p(const void* g, void* lds) {
+    __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 16, 0, NT ? 2 : 0);
+}
 // 4 bytes; with only lane 0 active they land at lds itself
 __device__ __forceinline__ void dma4(const void* g, void* lds) {
     __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 4, 0, 0);
