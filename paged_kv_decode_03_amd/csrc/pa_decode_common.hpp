@@ -227,6 +227,7 @@ __device__ __forceinline__ void decode_partitions(const DecodeArgs& a) {
     }
     const int t1 = min(L, t0 + P);
     Core core(a);
+    core.cow = first_block_shared(a.block_tables, a.max_blocks_per_seq, a.num_seqs, s);
     core.begin_segment(s, g);
     run_piece(core, st, s, g, t0 / CHUNK, (t1 + CHUNK - 1) / CHUNK, t1);
     if (a.partition_size > 0)
@@ -621,6 +622,7 @@ __device__ __forceinline__ void decode_balanced(const DecodeArgs& a) {
     if (!balanced_setup<G, D, NW>(a, sh, r)) return;
     SegPos cur = r.cur;
     Core core(a);
+    core.cow = r.hm;
     core.begin_segment(cur.s, cur.g);
     typename Core::State St;
     core.init(St);

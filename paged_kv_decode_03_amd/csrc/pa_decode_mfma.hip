@@ -67,7 +67,7 @@ struct MfmaCore {
     };
 
     const DecodeArgs& a;
-    bool cow = false;    // neighbouring sequences share blocks: stream the others (issue)
+    bool cow = false;    // neighbouring sequences share blocks: keep those cached (issue, load)
     int lane, j4, qd, tg;
     uint32_t k_off, v_off;                       // byte offsets inside a chunk
     float sl2;
@@ -135,11 +135,14 @@ struct MfmaCore {
     // Start the loads of chunk c of segment (s, g) into ring slot `slot`
     // (DPC vector memory instructions; two more with `fresh`, which also load
     // sequence s's new K and V rows of kv head g from key / value, and its
-    // slot_mapping entry). In a batch with copy-on-write sharing (cow), a
-    // block that no neighbouring sequence shares is loaded non-temporal, so
-    // that the L2 keeps the shared prefix blocks, which the other sequences of
-    // the group read again: on the mixed batch (four 64-sequence groups) HBM
-    // traffic 1.30x -> 1.04x the algorithmic bytes, 213.0 -> 205.3 us.
+    // slot_mapping entry). Tiles are loaded non-temporal: every (sequence, kv
+    // head) tile is read once per launch, and kept out of the L2's way it
+    // leaves the room to lines that are read again (int8 batch 130.5 -> 123.5
+    // us; the mixed batch without shared prefixes 325 -> 294 us). In a batch
+    // with copy-on-write sharing (cow) a block that a neighbouring sequence
+    // shares is the exception: the other sequences of its group read it again,
+    // from the L2 (mixed batch with four 64-sequence groups: HBM traffic 1.30x
+    // -> 1.04x the algorithmic bytes, 213.0 -> 205.3 us).
     __device__ void issue(char* slot, int s, int g, int c, bool fresh) const {
         if (fresh) {
             if (lane < 32) {                     // lanes 0..15: K, 16..31: V, 16 bytes each
@@ -161,7 +164,7 @@ struct MfmaCore {
             for (int i = 0; i < NDK; ++i)
                 dma16p<nt()>(at(vt + 1024 * i, 16u * lane), slot + KT + 1024 * i);
         };
-        if (cow && !block_shared(a, s, ri, phys))
+        if (!cow || !block_shared(a, s, ri, phys))
             tiles(std::true_type{});
         else
             tiles(std::false_type{});
@@ -309,28 +312,39 @@ struct MfmaCore {
         }
     }
 
+    // (cache policy as in issue)
     __device__ Chunk load(int s, int g, int c) const {
         Chunk ch;
-        const int phys = ld_uniform(a.block_tables, (int64_t)s * a.max_blocks_per_seq + (c >> shift));
+        const int64_t ri = (int64_t)s * a.max_blocks_per_seq + (c >> shift);
+        const int phys = ld_uniform(a.block_tables, ri);
         const int64_t off = phys * block_stride + g * head_stride + (int64_t)(c & shift) * CHUNK * D;
         const char* kp = at((const char*)a.k_cache + off * CE, k_off);
         const char* vp = at((const char*)a.v_cache + off * CE, v_off);
-        if constexpr (Q8) {
-            ch.k[0] = ld16(kp);
-            ch.k[1] = ld16(kp + 64);
-            ch.k[2] = ch.k[3] = make_uint4(0, 0, 0, 0);
+        auto tiles = [&](auto nt) {
+            if constexpr (Q8) {
+                ch.k[0] = ld16p<nt()>(kp);
+                ch.k[1] = ld16p<nt()>(kp + 64);
+                ch.k[2] = ch.k[3] = make_uint4(0, 0, 0, 0);
 #pragma unroll
-            for (int step = 0; step < 4; ++step) {
-                const uint2 w = ld8(vp + step * 4 * D);
-                ch.v[step] = make_uint4(w.x, w.y, 0, 0);
+                for (int step = 0; step < 4; ++step) {
+                    const uint2 w = ld8p<nt()>(vp + step * 4 * D);
+                    ch.v[step] = make_uint4(w.x, w.y, 0, 0);
+                }
+            } else {
+#pragma unroll
+                for (int m = 0; m < 4; ++m) ch.k[m] = ld16p<nt()>(kp + 64 * m);
+#pragma unroll
+                for (int step = 0; step < 4; ++step) ch.v[step] = ld16p<nt()>(vp + step * 4 * D * CE);
             }
+        };
+        if (!cow || !block_shared(a, s, ri, phys))
+            tiles(std::true_type{});
+        else
+            tiles(std::false_type{});
+        if constexpr (Q8) {
             ch.ks = ld_uniform(a.k_scale, (int64_t)phys * a.num_kv_heads + g);
             ch.vs = ld_uniform(a.v_scale, (int64_t)phys * a.num_kv_heads + g);
         } else {
-#pragma unroll
-            for (int m = 0; m < 4; ++m) ch.k[m] = ld16(kp + 64 * m);
-#pragma unroll
-            for (int step = 0; step < 4; ++step) ch.v[step] = ld16(vp + step * 4 * D * CE);
             ch.ks = ch.vs = 1.0f;
         }
         return ch;
@@ -714,7 +728,7 @@ struct Mfma16Core {
 #pragma unroll
             for (int i = 0; i < NDK; ++i) dma16p<nt()>(at(vt, vdma[i]), slot + KT + 1024 * i);
         };
-        if (cow && !block_shared(a, s, ri, phys))
+        if (!cow || !block_shared(a, s, ri, phys))
             tiles(std::true_type{});
         else
             tiles(std::false_type{});

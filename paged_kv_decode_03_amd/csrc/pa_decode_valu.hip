@@ -64,6 +64,7 @@ struct ValuCore {
     };
 
     const DecodeArgs& a;
+    bool cow = false;    // neighbouring sequences share blocks: keep those cached (load)
     int lane, tt, qq;
     uint32_t row_off;                            // bytes inside a 16-token chunk
     int shift;
@@ -106,17 +107,30 @@ struct ValuCore {
         }
     }
 
+    // Non-temporal loads (each tile is read once per launch), except blocks
+    // that a neighbouring sequence shares in a copy-on-write batch (cow), and
+    // fp32 caches (there the two load paths push the largest instance into
+    // register spills).
     __device__ Chunk load(int s, int g, int c) const {
         Chunk ch;
-        const int phys = ld_uniform(a.block_tables, (int64_t)s * a.max_blocks_per_seq + (c >> shift));
+        const int64_t ri = (int64_t)s * a.max_blocks_per_seq + (c >> shift);
+        const int phys = ld_uniform(a.block_tables, ri);
         const int64_t off = phys * block_stride + g * head_stride + (int64_t)(c & shift) * CHUNK * D;
         const char* kp = at((const char*)a.k_cache + off * CE, row_off);
         const char* vp = at((const char*)a.v_cache + off * CE, row_off);
+        auto tiles = [&](auto nt) {
 #pragma unroll
-        for (int m = 0; m < NM; ++m) {
-            ch.k[m] = ld16(kp + 64 * m);
-            ch.v[m] = ld16(vp + 64 * m);
-        }
+            for (int m = 0; m < NM; ++m) {
+                ch.k[m] = ld16p<nt()>(kp + 64 * m);
+                ch.v[m] = ld16p<nt()>(vp + 64 * m);
+            }
+        };
+        if constexpr (CT == F32)
+            tiles(std::false_type{});
+        else if (!cow || !block_shared(a, s, ri, phys))
+            tiles(std::true_type{});
+        else
+            tiles(std::false_type{});
         if constexpr (CT == I8) {
             ch.ks = ld_uniform(a.k_scale, (int64_t)phys * a.num_kv_heads + g);
             ch.vs = ld_uniform(a.v_scale, (int64_t)phys * a.num_kv_heads + g);

@@ -185,6 +185,18 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// 16-byte loads; with NT the non-temporal hint, for data that no other wave
+// of the launch reads again (as for dma16p)
+template <bool NT>
+__device__ __forceinline__ uint4 ld16p(const void* p) {
+    if constexpr (NT) {
+        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+        return make_uint4(v.x, v.y, v.z, v.w);
+    } else {
+        return *reinterpret_cast<const uint4*>(p);
+    }
+}
+
 __device__ __forceinline__ void dma16(const void* g, void* lds) {
     __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 16, 0, 0);
 }
@@ -197,6 +209,30 @@ __device__ __forceinline__ void dma16p(const void* g, void* lds) {
 // 4 bytes; with only lane 0 active they land at lds itself
 __device__ __forceinline__ void dma4(const void* g, void* lds) {
     __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 4, 0, 0);
+}
+
+template <bool NT>
+__device__ __forceinline__ uint2 ld8p(const void* p) {
+    if constexpr (NT) {
+        const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+        return make_uint2(v.x, v.y);
+    } else {
+        return *reinterpret_cast<const uint2*>(p);
+    }
+}
+
+// Whether sequence s starts on the same physical block as the previous or the
+// next sequence (rows of mbps entries in bt): a member of a group sharing
+// prefix blocks copy-on-write, whose blocks other workgroups read as well.
+// Only a cache hint rides on the answer, so a neighbour's unused entry (of any
+// value) does no harm.
+__device__ __forceinline__ bool first_block_shared(const int32_t* bt, int64_t mbps, int S, int s) {
+    const int64_t prev = s > 0 ? (int64_t)(s - 1) * mbps : -1;
+    const int64_t next = s + 1 < S ? (int64_t)(s + 1) * mbps : -1;
+    const int b = ld_uniform(bt, (int64_t)s * mbps);
+    const int bp = ld_uniform(bt, prev >= 0 ? prev : (int64_t)s * mbps);
+    const int bn = ld_uniform(bt, next >= 0 ? next : (int64_t)s * mbps);
+    return (prev >= 0 && bp == b) || (next >= 0 && bn == b);
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {

@@ -308,19 +308,19 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
             base[hf] = kt * TK + 16 * hf < limit
                 ? (int64_t)ld_uniform(bt, (kt * TK + 16 * hf) / B) * blk_stride + head_off : 0;
     };
-    auto load_tile = [&](int kt, const int64_t (&base)[2], uint4 (&kr)[NLD], uint4 (&vr)[NLD]) {
-        // WR: bit t set when token kt TK + t is a new token with a negative
-        // slot: it is not written, so its position is read from the cache
-        // like any other (scalar loads, only for tiles that hold new tokens)
-        uint32_t negm = 0;
-        if constexpr (WR) {
-            const int j0 = kt * TK - new0;            // new-token index of the tile's token 0
-            if (j0 + TK > 0 && j0 < n) {
-                const int tb = max(0, -j0), te = min(TK, n - j0);
-                for (int t = tb; t < te; ++t)
-                    if (ld_uniform(a.slot_mapping, (int64_t)q0 + j0 + t) < 0) negm |= 1u << t;
-            }
-        }
+    // A KV tile that no other workgroup of the launch reads is loaded
+    // non-temporal: kept out of the L2's way, it leaves the room to lines that
+    // are read again. That holds in the instances of at most 64 rows (one row
+    // tile per sequence) unless the sequence starts on a block that a
+    // neighbouring sequence shares copy-on-write. Llama-shaped decode 60.5 ->
+    // 52.9 us, speculative verify 59.6 -> 52.2 us, 8 x 32768 split-K step
+    // 188.8 -> 169.6 us. (The 128-row instance keeps cached loads: its row
+    // tiles of a sequence read the same KV, and the second load path alone
+    // slowed chunked prefill by 2%.)
+    const bool stream = RT <= 64 &&
+        !first_block_shared(a.block_tables, a.max_blocks_per_seq, a.num_seqs, s);
+    auto load_tile_p = [&](int kt, const int64_t (&base)[2], uint4 (&kr)[NLD], uint4 (&vr)[NLD],
+                           uint32_t negm, auto nt) {
 #pragma unroll
         for (int k = 0; k < NLD; ++k) {
             const int p = ti + k * TPT, t = p / PPR, e = (p % PPR) * EPP;
@@ -345,13 +345,31 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
                     kp = reinterpret_cast<const char*>(a.key) + src * 2;
                     vp = reinterpret_cast<const char*>(a.value) + src * 2;
                 }
-                kr[k] = ld16(kp);
-                vr[k] = ld16(vp);
+                kr[k] = ld16p<nt()>(kp);
+                vr[k] = ld16p<nt()>(vp);
             } else {
-                kr[k] = ld16(at(reinterpret_cast<const char*>(a.k_cache) + bb, lo));
-                vr[k] = ld16(at(reinterpret_cast<const char*>(a.v_cache) + bb, lo));
+                kr[k] = ld16p<nt()>(at(reinterpret_cast<const char*>(a.k_cache) + bb, lo));
+                vr[k] = ld16p<nt()>(at(reinterpret_cast<const char*>(a.v_cache) + bb, lo));
             }
         }
+    };
+    auto load_tile = [&](int kt, const int64_t (&base)[2], uint4 (&kr)[NLD], uint4 (&vr)[NLD]) {
+        // WR: bit t set when token kt TK + t is a new token with a negative
+        // slot: it is not written, so its position is read from the cache
+        // like any other (scalar loads, only for tiles that hold new tokens)
+        uint32_t negm = 0;
+        if constexpr (WR) {
+            const int j0 = kt * TK - new0;            // new-token index of the tile's token 0
+            if (j0 + TK > 0 && j0 < n) {
+                const int tb = max(0, -j0), te = min(TK, n - j0);
+                for (int t = tb; t < te; ++t)
+                    if (ld_uniform(a.slot_mapping, (int64_t)q0 + j0 + t) < 0) negm |= 1u << t;
+            }
+        }
+        if (RT <= 64 && stream)
+            load_tile_p(kt, base, kr, vr, negm, std::true_type{});
+        else
+            load_tile_p(kt, base, kr, vr, negm, std::false_type{});
     };
     char* kl = lds + tg * TGBYTES;                    // the token group's buffer in use
     char* vl = kl + KBYTES;
