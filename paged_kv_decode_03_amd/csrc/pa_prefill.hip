@@ -302,11 +302,17 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     // fetched one tile ahead: under a saturated memory system even a cached
     // id takes long to come back, and waiting for it between a tile's arrival
     // and the next tile's loads would leave the wave with nothing in flight.
-    auto tile_bases = [&](int kt, int64_t (&base)[2]) {
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf)
-            base[hf] = kt * TK + 16 * hf < limit
-                ? (int64_t)ld_uniform(bt, (kt * TK + 16 * hf) / B) * blk_stride + head_off : 0;
+    // A half wholly past the context takes the other half's base (a block of
+    // the sequence when the tile is computed at all; block 0 of the pool for
+    // a spare tile past the context, which is loaded but never computed).
+    // (kt is the same in every lane of the wave; saying so keeps the test and
+    // the bases in scalar registers: 1-3% fewer VGPRs)
+    auto tile_bases = [&](int kt_, int64_t (&base)[2]) {
+        const int kt = uniform(kt_);
+        base[0] = kt * TK < limit
+            ? (int64_t)ld_uniform(bt, (kt * TK) / B) * blk_stride + head_off : 0;
+        base[1] = kt * TK + 16 < limit
+            ? (int64_t)ld_uniform(bt, (kt * TK + 16) / B) * blk_stride + head_off : base[0];
     };
     // A KV tile that no other workgroup of the launch reads is loaded
     // non-temporal: kept out of the L2's way, it leaves the room to lines that
@@ -324,12 +330,12 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int k = 0; k < NLD; ++k) {
             const int p = ti + k * TPT, t = p / PPR, e = (p % PPR) * EPP;
-            // a token at or past `limit` reads the tile's first token instead
-            // (cached, so finite): every row masks it (x = -inf, weight 0)
+            // a token at or past `limit` reads the first token of its half's
+            // block instead, a token of the context (so finite, whatever the
+            // pool's unused blocks hold): every row masks it (x = -inf, weight 0)
             const bool in = kt * TK + t < limit;
             const uint32_t lo = (uint32_t)(((in ? t % B : 0) * PD + e) * ELT);
-            const int64_t bb = !in ? base[0]
-                             : HALF_UNIFORM ? base[(k * TOK_PER_LD) / 16]
+            const int64_t bb = HALF_UNIFORM ? base[(k * TOK_PER_LD) / 16]
                                             : (t < 16 ? base[0] : base[1]);
             if constexpr (WR) {
                 // a new token's row comes from key / value (its slot is being

@@ -203,6 +203,15 @@ def model_launch(lens, qlens, Hq, Hkv, B, i8=False, wr=False, P=0, max_query_len
             for hv in (0, 1):
                 need = inn & (half == hv)
                 check(~need | fetched[hv][:, None], "piece of a block never fetched")
+            # a piece past the context reads token 0 of its half's base, which
+            # must be a block of the context whenever the tile is computed (the
+            # masked weight is 0, but 0 times a non-finite pool value is not):
+            # half 1 wholly past the context takes half 0's base
+            live = kts < nkt
+            for hv in (0, 1):
+                own = fetched[hv] if hv == 0 else (fetched[1] | fetched[0])
+                past = ~inn & (half == hv) & live[:, None]
+                check(~past | own[:, None], "masked piece read outside the context")
             if wr:
                 jn = kts[:, None] * TK + np.where(inn, t[None, :], 0) - new0
                 sel = (jn >= 0) if planted_jn_bound else (jn >= 0) & (jn < n)
