@@ -179,7 +179,12 @@ int pa_decode(void *out, const void *q, const void *k_cache, const void *v_cache
  * finished in place. A context cut by range ends leaves one partial per piece
  * in the workspace; the wave that completes its last piece (an atomic counter
  * per (sequence, kv head)) combines the pieces exactly as
- * pa_decode_splitk_reduce would, writes `out`, and resets the counter.
+ * pa_decode_splitk_reduce would, writes `out`, and resets the counter. With 8
+ * query heads per kv head on a bf16 cache (and at most 4096 sequences) the
+ * list holds pairs of neighbouring sequences instead, the 16 query heads of a
+ * pair filling one 16-column MFMA tile: the leading chunks that both block
+ * tables place on the same physical blocks (copy-on-write prefixes) are read
+ * and computed once for the two, the other chunks for their own sequence.
  *
  *   out, q, k_cache, v_cache, block_tables, context_lens, k_scale, v_scale,
  *   scale, num_seqs .. max_context_len, q_dtype, cache_dtype: as pa_decode.
@@ -240,7 +245,7 @@ int pa_write_decode_balanced(const void *key, const void *value, const int64_t *
  * (partials, maxima, sums, counters) in a static array of the library instead
  * of caller buffers. It calls no hipMalloc or hipFree and allocates nothing.
  *
- * The array is 40 MiB per GPU (held by every device that loads the library
+ * The array is 72 MiB per GPU (held by every device that loads the library
  * until the process ends): a 1 MiB region of int32 counters, cleared by a
  * kernel on `stream` at the first call on each device and left zero by every
  * call, then the partial states. Shapes whose workspace (pa_balanced_workspace)
@@ -382,7 +387,8 @@ int pa_write_prefill(const void *key, const void *value, const int64_t *slot_map
  * (any dtypes): *slots partial-state slots, i.e. tmp_out [*slots][G][head_dim]
  * and tmp_max, tmp_sum [*slots][G] fp32 with G = num_heads / num_kv_heads,
  * and *counters int32 counters (num_seqs * num_kv_heads). The slots grow
- * with the device (4 per wave of the persistent grid), not with the context
+ * with the device (4 per wave of the persistent grid, 8 at G = 8, whose
+ * partial states may cover a pair of sequences), not with the context
  * lengths. Returns PA_OK, PA_ERR_NULL,
  * PA_ERR_SHAPE, PA_ERR_UNSUPPORTED (no balanced instance for head_dim and G)
  * or PA_ERR_LAUNCH (the runtime could not report the device's occupancy).

@@ -463,7 +463,9 @@ int pa_balanced_workspace(int num_seqs, int num_heads, int num_kv_heads, int hea
     if (wv < 0 || wm < 0) return PA_ERR_LAUNCH;
     const int waves = wv > wm ? wv : wm;
     if (waves == 0) return PA_ERR_UNSUPPORTED;
-    *slots = 4 * (int64_t)waves;
+    // 4 partial states per wave; at G = 8 the 16x16 core's states may cover
+    // two sequences (pair units), so twice as many slots of G heads
+    *slots = (G == 8 ? 8 : 4) * (int64_t)waves;
     *counters = (int64_t)num_seqs * num_kv_heads;
     return PA_OK;
 }
@@ -604,7 +606,7 @@ int pa_decode_splitk_reduce(void* out, const float* tmp_out, const float* tmp_ma
 // host code needs the memory.
 namespace {
 
-constexpr size_t kScratchBytes = size_t(40) << 20;           // 40 MiB per GPU
+constexpr size_t kScratchBytes = size_t(72) << 20;           // 72 MiB per GPU
 constexpr size_t kScratchCounters = size_t(1) << 18;         // int32 counters (1 MiB)
 static __device__ __align__(256) char scratch[kScratchBytes];
 

@@ -263,21 +263,102 @@ struct BalancedShared {
     int wave_tot[NWG], wave_shared[NWG];
     long long wave_cost[NWG];
     long long total, total_cost;
-    int s0[NWG + 1], L0[NWG + 1], g0[NWG + 1];
+    int s0[NWG + 1], nu[NWG + 1], g0[NWG + 1];       // unit, its chunks, kv head
     long long base0[NWG + 1], cbase0[NWG + 1];
 };
 
+// Units of the segment list. For most cores a unit is one sequence. A core
+// with PAIR set (the 16x16 core at 8 query heads per kv head, whose MFMA tile
+// has 16 columns) takes two neighbouring sequences per unit, 2u in columns
+// 0-7 and 2u + 1 (if any) in columns 8-15: first the ns leading chunks that
+// lie on the same physical blocks in both block tables (copy-on-write
+// prefixes), read and computed once for both, then the first sequence's own
+// chunks [ns, n0), then the second's [ns, n1). A shared chunk holds no token
+// of either sequence's last chunk (ns <= (L - 1) / 16 for both), so it is
+// full for both and carries no new token. Segments are (unit, kv head).
+constexpr int kMaxPairUnits = 2048;   // the pair table in LDS: 8 KB
+
 // Position of one chunk in the segment list (all fields wave-uniform).
 struct SegPos {
-    int s, g, c;      // sequence, kv head, chunk within the segment
-    int L, n;         // context length of s and its chunk count
+    int s, g, c;      // unit, kv head, chunk within the segment
+    int L, n;         // context length of the unit's (first) sequence; the segment's chunks
+    int L1, n0, ns;   // pair units: the second sequence's length, the first's chunks,
+                      // the shared chunks (otherwise 0, n, 0)
     long long A;      // list index of chunk 0 of segment (s, g)
     long long Y;      // cost position where chunk 0 of segment (s, g) starts
 };
 
+template <bool PAIR>
+__device__ __forceinline__ int num_units(const DecodeArgs& a) {
+    return PAIR ? (a.num_seqs + 1) / 2 : a.num_seqs;
+}
+
+// Shared leading chunks of the pair (s0, s0 + 1) with lengths L0, L1 (both
+// > 0), from the block tables: the run of equal entries, capped below both
+// sequences' last chunk. Per-lane loads (set-up only).
+__device__ __forceinline__ int pair_shared_chunks(const DecodeArgs& a, int s0, int L0, int L1) {
+    const int cap = min((L0 - 1) / CHUNK, (L1 - 1) / CHUNK);
+    if (cap <= 0) return 0;
+    const int cpb = a.block_size / CHUNK;              // chunks per block (1 or 2)
+    const int nb = (cap + cpb - 1) / cpb;              // blocks that may hold shared chunks
+    const int32_t* t0 = a.block_tables + (int64_t)s0 * a.max_blocks_per_seq;
+    const int32_t* t1 = t0 + a.max_blocks_per_seq;
+    int b = 0;
+    for (; b + 8 <= nb; b += 8) {                      // eight entries of each table at a time
+        int eq = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) eq |= (t0[b + i] == t1[b + i]) ? 0 : (1 << i);
+        if (eq) {
+            b += __builtin_ctz(eq);
+            return min(cap, b * cpb);
+        }
+    }
+    while (b < nb && t0[b] == t1[b]) ++b;
+    return min(cap, b * cpb);
+}
+
+// Fill p's unit fields for unit p.s. ns_tab: LDS byte address of the pair
+// table (pair units' shared chunks, written by balanced_setup).
+template <bool PAIR>
+__device__ __forceinline__ void load_unit(const DecodeArgs& a, uint32_t ns_tab, SegPos& p) {
+    if constexpr (PAIR) {
+        const int s0 = 2 * p.s;
+        p.L = ld_uniform(a.context_lens, s0);
+        p.L1 = s0 + 1 < a.num_seqs ? ld_uniform(a.context_lens, s0 + 1) : 0;
+        p.n0 = (p.L + CHUNK - 1) / CHUNK;
+        p.ns = uniform((int)ds_read4_wait(ns_tab + 4 * p.s));
+        p.n = p.n0 + (p.L1 + CHUNK - 1) / CHUNK - p.ns;
+    } else {
+        p.L = ld_uniform(a.context_lens, p.s);
+        p.n = p.n0 = (p.L + CHUNK - 1) / CHUNK;
+        p.L1 = p.ns = 0;
+    }
+}
+
+// The chunk of a sequence that chunk p.c of segment (p.s, p.g) is: the
+// sequence, its chunk index, its length (tokens >= t1 are masked), which
+// columns it feeds (0 all, 1 the first sequence's, 2 the second's) and
+// whether it is the sequence's last chunk (which holds its new token).
+struct ChunkRef {
+    int s, c, t1, who;
+    bool last;
+};
+template <bool PAIR>
+__device__ __forceinline__ ChunkRef chunk_ref(const SegPos& p) {
+    if constexpr (!PAIR) {
+        return {p.s, p.c, p.L, 0, p.c + 1 == p.n};
+    } else {
+        if (p.c < p.ns) return {2 * p.s, p.c, p.L, 0, false};
+        if (p.c < p.n0) return {2 * p.s, p.c, p.L, 1, p.c + 1 == p.n0};
+        return {2 * p.s + 1, p.c - p.n0 + p.ns, p.L1, 2, p.c + 1 == p.n};
+    }
+}
+
 // hm: the segment list is kv head major; sc: a segment's fixed cost (see
 // balanced_setup)
-__device__ __forceinline__ SegPos next_pos(const DecodeArgs& a, SegPos p, bool hm, int sc) {
+template <bool PAIR = false>
+__device__ __forceinline__ SegPos next_pos(const DecodeArgs& a, SegPos p, bool hm, int sc,
+                                           uint32_t ns_tab = 0) {
     if (p.c + 1 < p.n) {
         ++p.c;
         return p;
@@ -285,14 +366,14 @@ __device__ __forceinline__ SegPos next_pos(const DecodeArgs& a, SegPos p, bool h
     p.c = 0;
     p.Y += (long long)p.n * kChunkCost + sc;
     p.A += p.n;
+    const int U = num_units<PAIR>(a);
     if (hm) {
-        do {                               // sequences with an empty context have no segments
-            if (++p.s == a.num_seqs) {
+        do {                               // units with no context have no segments
+            if (++p.s == U) {
                 p.s = 0;
                 ++p.g;
             }
-            p.L = ld_uniform(a.context_lens, p.s);
-            p.n = (p.L + CHUNK - 1) / CHUNK;
+            load_unit<PAIR>(a, ns_tab, p);
         } while (p.n == 0);
         return p;
     }
@@ -300,8 +381,7 @@ __device__ __forceinline__ SegPos next_pos(const DecodeArgs& a, SegPos p, bool h
     p.g = 0;
     do {
         ++p.s;
-        p.L = ld_uniform(a.context_lens, p.s);
-        p.n = (p.L + CHUNK - 1) / CHUNK;
+        load_unit<PAIR>(a, ns_tab, p);
     } while (p.n == 0);
     return p;
 }
@@ -342,9 +422,11 @@ struct WaveRange {
 // Set-up shared by the balanced drivers: chunk counts, their scan over the
 // sequences, the range size C and the position of each wave's first chunk.
 // Ends with a workgroup barrier; returns false for a wave with no work.
-template <int G, int D, int NWG>
+// PAIR: units are pairs of sequences; their shared chunks go to the LDS table
+// ns_tab (int[kMaxPairUnits], unused otherwise).
+template <int G, int D, int NWG, bool PAIR = false>
 __device__ __forceinline__ bool balanced_setup(const DecodeArgs& a, BalancedShared<NWG>& sh,
-                                               WaveRange& r) {
+                                               WaveRange& r, int* ns_tab = nullptr) {
     const int tid = threadIdx.x, lane = tid & 63, wave = uniform(tid >> 6);
     const int S = a.num_seqs, Hkv = a.num_kv_heads;
     const int W = gridDim.x;
@@ -384,22 +466,45 @@ __device__ __forceinline__ bool balanced_setup(const DecodeArgs& a, BalancedShar
     // range holding its last unit P + kChunkCost - 1.
     constexpr int CC = kChunkCost, SC = G >= 8 ? kSegCostG8 : kSegCost;
 
-    // 1. chunk counts and costs per sequence: thread t sums its slice
-    const int K = (S + NWG * 64 - 1) / (NWG * 64);
-    const int sb = min(S, tid * K), se = min(S, sb + K);
-    int my = 0, L1 = 0;                              // L1: length of sequence sb, kept
+    // 1. chunk counts and costs per unit: thread t sums its slice of units
+    // (and, for pair units, finds their shared chunks)
+    const int U = num_units<PAIR>(a);
+    const int K = (U + NWG * 64 - 1) / (NWG * 64);
+    const int ub = min(U, tid * K), ue = min(U, ub + K);
+    const int sb = PAIR ? min(S, 2 * ub) : ub, se = PAIR ? min(S, 2 * ue) : ue;   // its sequences
+    // chunks of unit u (pair units: its shared chunks into the table)
+    auto unit_chunks = [&](int u, bool fill) -> int {
+        if constexpr (PAIR) {
+            const int s0 = 2 * u;
+            const int L0 = ld_const(a.context_lens, s0);
+            const int L1 = s0 + 1 < S ? ld_const(a.context_lens, s0 + 1) : 0;
+            int ns;
+            if (fill) {
+                ns = (L0 > 0 && L1 > 0) ? pair_shared_chunks(a, s0, L0, L1) : 0;
+                ns_tab[u] = ns;
+            } else {
+                ns = ns_tab[u];
+            }
+            return (L0 + CHUNK - 1) / CHUNK + (L1 + CHUNK - 1) / CHUNK - ns;
+        } else {
+            (void)fill;
+            return (ld_const(a.context_lens, u) + CHUNK - 1) / CHUNK;
+        }
+    };
+    int my = 0;
     int shared = 0;                                  // s whose first block is s + 1's
     long long myc = 0;
+    for (int u = ub; u < ue; ++u) {
+        const int n = unit_chunks(u, true);
+        my += n;
+        myc += n ? (long long)n * CC + SC : 0;
+    }
     for (int s = sb; s < se; ++s) {
         // all four loads at once (entry 0 of a block-table row always exists)
         const int t = min(s + 1, S - 1);
         const int L = ld_const(a.context_lens, s), Ln = ld_const(a.context_lens, t);
         const int b = ld_const(a.block_tables, (int64_t)s * a.max_blocks_per_seq);
         const int bn = ld_const(a.block_tables, (int64_t)t * a.max_blocks_per_seq);
-        if (s == sb) L1 = L;
-        const int n = (L + CHUNK - 1) / CHUNK;
-        my += n;
-        myc += n ? (long long)n * CC + SC : 0;
         if (t > s && L > a.block_size && Ln > a.block_size && b == bn) ++shared;
     }
     int inc = my;                                    // inclusive scans over the workgroup
@@ -431,7 +536,7 @@ __device__ __forceinline__ bool balanced_setup(const DecodeArgs& a, BalancedShar
         nshared += sh.wave_shared[v];
     }
     const bool hm = uniform(nshared) * 4 >= S;       // kv head major (see above)
-    const int excl = wbase + inc - my;               // chunks of sequences before sb
+    const int excl = wbase + inc - my;               // chunks of units before ub
     const long long exclc = wbasec + incc - myc;     // their cost, per kv head
     if (tid == NWG * 64 - 1) {
         sh.total = (long long)Hkv * (wbase + inc);
@@ -470,8 +575,8 @@ __device__ __forceinline__ bool balanced_setup(const DecodeArgs& a, BalancedShar
         rg.Cs = rg.Cf = max(cmin, C);
     }
 
-    // 2. locate the sequence holding the cost position where each wave's
-    // range starts (v = NWG: the next workgroup's first, where the last ends)
+    // 2. locate the unit holding the cost position where each wave's range
+    // starts (v = NWG: the next workgroup's first, where the last ends)
     const long long Th = T / Hkv, Tch = Tc / Hkv;    // one kv head's chunks and cost
     auto locate = [&](long long Y, int v) {
         if (hm) {
@@ -480,13 +585,12 @@ __device__ __forceinline__ bool balanced_setup(const DecodeArgs& a, BalancedShar
             const long long Yr = Y - (long long)g * Tch;
             if (exclc <= Yr && Yr < exclc + myc) {
                 long long base = excl, cbase = exclc;
-                for (int s = sb; s < se; ++s) {
-                    const int L = s == sb ? L1 : ld_const(a.context_lens, s);
-                    const int n = (L + CHUNK - 1) / CHUNK;
+                for (int u = ub; u < ue; ++u) {
+                    const int n = unit_chunks(u, false);
                     const long long cost = n ? (long long)n * CC + SC : 0;
                     if (Yr < cbase + cost) {
-                        sh.s0[v] = s;
-                        sh.L0[v] = L;
+                        sh.s0[v] = u;
+                        sh.nu[v] = n;
                         sh.g0[v] = g;
                         sh.base0[v] = (long long)g * Th + base;
                         sh.cbase0[v] = (long long)g * Tch + cbase;
@@ -500,13 +604,12 @@ __device__ __forceinline__ bool balanced_setup(const DecodeArgs& a, BalancedShar
         }
         if ((long long)Hkv * exclc <= Y && Y < (long long)Hkv * (exclc + myc)) {
             long long base = (long long)Hkv * excl, cbase = (long long)Hkv * exclc;
-            for (int s = sb; s < se; ++s) {
-                const int L = s == sb ? L1 : ld_const(a.context_lens, s);
-                const int n = (L + CHUNK - 1) / CHUNK;
+            for (int u = ub; u < ue; ++u) {
+                const int n = unit_chunks(u, false);
                 const long long cost = n ? (long long)Hkv * ((long long)n * CC + SC) : 0;
                 if (Y < cbase + cost) {
-                    sh.s0[v] = s;
-                    sh.L0[v] = L;
+                    sh.s0[v] = u;
+                    sh.nu[v] = n;
                     sh.base0[v] = base;
                     sh.cbase0[v] = cbase;
                     break;
@@ -521,19 +624,17 @@ __device__ __forceinline__ bool balanced_setup(const DecodeArgs& a, BalancedShar
     // chunk list index of the first chunk whose last unit is at or after Y
     auto chunk_at = [&](long long Y, int v, SegPos* p) -> long long {
         if (Y >= Tc) return T;
-        const int s = uniform(sh.s0[v]), L = uniform(sh.L0[v]);
+        const int u = uniform(sh.s0[v]), n = uniform(sh.nu[v]);
         const long long base = uniform64(sh.base0[v]), cbase = uniform64(sh.cbase0[v]);
-        const int n = (L + CHUNK - 1) / CHUNK;
         const long long sc = (long long)n * CC + SC;
-        // head major: base / cbase already name segment (s, g0)
+        // head major: base / cbase already name segment (u, g0)
         const int g = hm ? uniform(sh.g0[v]) : (int)((Y - cbase) / sc);
-        const long long gb = hm ? 0 : g;              // segments of s before (s, g)
+        const long long gb = hm ? 0 : g;              // segments of u before (u, g)
         const long long off = (Y - cbase) - gb * sc;   // < sc, so c < n
         const int c = off < SC ? 0 : (int)((off - SC) / CC);
         if (p) {
-            p->s = s;
-            p->L = L;
-            p->n = n;
+            p->s = u;
+            load_unit<PAIR>(a, lds_addr(ns_tab), *p);
             p->g = g;
             p->c = c;
             p->A = base + gb * n;
@@ -696,7 +797,9 @@ __device__ __forceinline__ void wait_ring(int later) {
 template <class Core, int NWG>
 __device__ __forceinline__ void decode_balanced_ring(const DecodeArgs& a) {
     constexpr int G = Core::G, D = Core::D, R = Core::R, SLOT = Core::SLOT, DPC = Core::DPC;
+    constexpr bool PAIR = Core::PAIR;
     __shared__ BalancedShared<NWG> sh;
+    __shared__ int ns_tab[PAIR ? kMaxPairUnits : 1];
     __shared__ __attribute__((aligned(16))) char ring[NWG * R * SLOT];
     if (a.slot_mapping != nullptr && blockIdx.x == 0) {
         // new tokens of sequences with an empty context: no chunk carries them
@@ -707,7 +810,8 @@ __device__ __forceinline__ void decode_balanced_ring(const DecodeArgs& a) {
                         Core::write_vector_at(a, s, g, v);
     }
     WaveRange r;
-    if (!balanced_setup<G, D, NWG>(a, sh, r)) return;
+    if (!balanced_setup<G, D, NWG, PAIR>(a, sh, r, ns_tab)) return;
+    const uint32_t nst = lds_addr(ns_tab);
     char* const mine = ring + uniform(threadIdx.x >> 6) * (R * SLOT);
     SegPos cur = r.cur;
     Core core(a);
@@ -715,15 +819,16 @@ __device__ __forceinline__ void decode_balanced_ring(const DecodeArgs& a) {
     const int n = (int)(r.X1 - r.X0);                // chunks in the range (>= 1)
     SegPos ahead = cur;                              // next chunk to issue
     int issued = 0;
-    // When the decode writes the new tokens: a segment's last chunk holds the
-    // new token of (s, g), and one wave consumes it. That wave loads the
+    // When the decode writes the new tokens: a sequence's last chunk holds its
+    // new token of kv head g, and one wave consumes it. That wave loads the
     // token's rows with the chunk and, once both are in LDS, writes the token
     // into its cache slot and over the chunk's stale row (patch_new_token), so
     // the kernel never reads back what it stores.
     const bool writes = a.slot_mapping != nullptr;
     auto issue_next = [&](char* sp) {
-        core.issue(sp, ahead.s, ahead.g, ahead.c, writes && ahead.c + 1 == ahead.n);
-        if (++issued < n) ahead = next_pos(a, ahead, r.hm, r.sc);
+        const ChunkRef q = chunk_ref<PAIR>(ahead);
+        core.issue(sp, q.s, ahead.g, q.c, writes && q.last);
+        if (++issued < n) ahead = next_pos<PAIR>(a, ahead, r.hm, r.sc, nst);
     };
 #pragma unroll
     for (int k = 0; k < R; ++k)
@@ -737,11 +842,15 @@ __device__ __forceinline__ void decode_balanced_ring(const DecodeArgs& a) {
     for (int i = 0;; ++i) {
         wait_ring<R, DPC>(n - 1 - i);                // chunk i is in its slot
         char* const sp = mine + slot * SLOT;
-        if (writes && cur.c + 1 == cur.n) core.patch_new_token(sp, cur.g, cur.L);
+        const ChunkRef q = chunk_ref<PAIR>(cur);
+        if (writes && q.last) core.patch_new_token(sp, cur.g, q.t1);
         const typename Core::Chunk ch = core.fetch(sp);   // the slot is free again
         if (issued < n) issue_next(sp);
         slot = (slot + 1 == R) ? 0 : slot + 1;
-        core.step(St, ch, cur.c, cur.L);
+        if constexpr (PAIR)
+            core.step(St, ch, q.c, q.t1, q.who);
+        else
+            core.step(St, ch, q.c, q.t1);
         const bool last = i + 1 == n;
         if (!last && cur.c + 1 < cur.n) {            // same segment
             ++cur.c;
@@ -749,7 +858,7 @@ __device__ __forceinline__ void decode_balanced_ring(const DecodeArgs& a) {
         }
         end(St, cur, last);
         if (last) break;
-        cur = next_pos(a, cur, r.hm, r.sc);
+        cur = next_pos<PAIR>(a, cur, r.hm, r.sc, nst);
         core.begin_segment(cur.s, cur.g);
         wait_vmcnt<0>();
         core.init(St);

@@ -51,6 +51,7 @@ struct MfmaCore {
     static constexpr int G = G_;
     static constexpr int D = 128;
     static constexpr bool BASE2 = true;
+    static constexpr bool PAIR = false;          // one sequence per segment
     static constexpr int NHB = G / 4;           // 4-head groups
     static constexpr bool Q8 = (CT == I8);
     static constexpr int CE = Q8 ? 1 : 2;        // cache bytes per element
@@ -649,13 +650,20 @@ struct MfmaCore {
 // and the transposing V reads (rows 4*qg .. +3, 32 bytes each) spread over the
 // banks. The direct loads write 16 bytes per lane at consecutive addresses, so
 // the permutation is applied to the global addresses the lanes read.
-template <int G_>
+//
+// PAIR (G = 8): the segments are pairs of sequences (see the units of the
+// balanced driver): column n is head n % G of sequence 2s + n / G, so the 16
+// columns are all in use. A chunk that only one of the two sequences holds
+// feeds only its columns (step's `who`); the other columns see it masked.
+template <int G_, bool PAIR_ = false>
 struct Mfma16Core {
     static constexpr int G = G_;
+    static constexpr bool PAIR = PAIR_;
+    static constexpr int GC = PAIR ? 2 * G : G;      // columns in use
     static constexpr int D = 128;
     static constexpr bool BASE2 = true;
     static constexpr float kSlack = 8.0f;
-    static_assert(G <= 16, "one 16-column tile of query heads");
+    static_assert(GC <= 16, "one 16-column tile of query heads");
 
     struct State {
         float m, l;
@@ -786,15 +794,27 @@ struct Mfma16Core {
         return ch;
     }
 
-    // Query head n of the segment (zero for n >= G; the load is clamped to a
-    // head of the segment), dims 32*kk + 8*qg .. +7.
+    // Row of q / out that column n of segment (s, g) holds, counted in heads
+    // from row (first sequence of the segment, head g G): n, or for pair
+    // units (n / G) Hq + n % G.
+    __device__ uint32_t col_row() const {
+        return PAIR ? (uint32_t)((n / G) * a.num_heads + n % G) : (uint32_t)n;
+    }
+    __device__ int64_t first_row(int s, int g) const {
+        return ((int64_t)(PAIR ? 2 * s : s) * a.num_heads + g * G) * D;
+    }
+
+    // The query of column n (zero for a column with no head: n >= G, or the
+    // missing second sequence of the last pair unit; the load is then
+    // clamped to the segment's first row), dims 32*kk + 8*qg .. +7.
     __device__ void begin_segment(int s, int g) {
-        const uint16_t* q0 = (const uint16_t*)a.q + ((int64_t)s * a.num_heads + g * G) * D;
-        const int h = n < G ? n : 0;
+        const uint16_t* q0 = (const uint16_t*)a.q + first_row(s, g);
+        const bool live = PAIR ? 2 * s + n / G < a.num_seqs : n < G;
+        const uint32_t row = live ? col_row() : 0u;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-            const uint4 w = ld16(at(q0, 2 * (h * D + 32 * kk + 8 * qg)));
-            qr[kk] = n < G ? w : make_uint4(0, 0, 0, 0);
+            const uint4 w = ld16(at(q0, 2 * (row * D + 32 * kk + 8 * qg)));
+            qr[kk] = live ? w : make_uint4(0, 0, 0, 0);
         }
     }
 
@@ -805,8 +825,11 @@ struct Mfma16Core {
         for (int j = 0; j < 8; ++j) S.acc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     }
 
-    __device__ void step(State& S, const Chunk& cur, int c, int t1) const {
+    // who (pair units): 0 the chunk feeds every column, 1 only the first
+    // sequence's, 2 only the second's; the others see its tokens masked.
+    __device__ void step(State& S, const Chunk& cur, int c, int t1, int who = 0) const {
         const bool tail = ((c + 1) * CHUNK) > t1;
+        const bool off = PAIR && who != 0 && ((who == 1) == (n >= G));
         f32x4 sacc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
@@ -818,14 +841,15 @@ struct Mfma16Core {
         for (int i = 0; i < 4; ++i) {
             // x is rounded once; the max and exp2(x - max) see the same x
             x[i] = sacc[i] * sl2;
-            if (tail && c * CHUNK + 4 * qg + i >= t1) x[i] = kNegInf;
+            if (off || (tail && c * CHUNK + 4 * qg + i >= t1)) x[i] = kNegInf;
         }
         float mloc = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
         mloc = fmaxf(mloc, lane_xor16(mloc));
         mloc = fmaxf(mloc, lane_xor32(mloc));
         const float mnew = (mloc > S.m + kSlack) ? mloc : S.m;
         const float muse = (mnew == kNegInf) ? 0.0f : mnew;
-        const float alpha = __builtin_amdgcn_exp2f(S.m - muse);
+        // an empty state (no token yet: acc and l are 0) needs no rescale
+        const float alpha = S.m == kNegInf ? 1.0f : __builtin_amdgcn_exp2f(S.m - muse);
         float p[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(x[i] - muse);
@@ -858,34 +882,36 @@ struct Mfma16Core {
         S.l += lane_xor32(S.l);
     }
 
-    // The lane's 4 values of dims 16*j + 4*qg .. +3 of head n as bf16.
+    // The lane's 4 values of dims 16*j + 4*qg .. +3 of column n as bf16.
     __device__ void store4(int s, int g, int j, float v0, float v1, float v2, float v3) const {
-        uint16_t* o0 = (uint16_t*)a.out + ((int64_t)s * a.num_heads + g * G + n) * D;
+        uint16_t* o0 = (uint16_t*)a.out + first_row(s, g);
         const uint2 w = make_uint2(f32_to_bf16(v0) | ((uint32_t)f32_to_bf16(v1) << 16),
                                    f32_to_bf16(v2) | ((uint32_t)f32_to_bf16(v3) << 16));
-        *reinterpret_cast<uint2*>(at(o0, 2 * (16 * j + 4 * qg))) = w;
+        *reinterpret_cast<uint2*>(at(o0, 2 * (col_row() * D + 16 * j + 4 * qg))) = w;
     }
 
+    // (pair units: a column that saw no token belongs to a sequence with an
+    // empty context, whose zeros are written elsewhere, or to none at all)
     __device__ void store_final(const State& S, int s, int g) const {
-        if (n >= G) return;
+        if (n >= GC || (PAIR && !(S.l > 0.0f))) return;
 #pragma unroll
         for (int j = 0; j < 8; ++j)
             store4(s, g, j, S.acc[j][0] / S.l, S.acc[j][1] / S.l, S.acc[j][2] / S.l,
                    S.acc[j][3] / S.l);
     }
 
-    // Workspace slot: tmp_out [G][D] (unnormalised), tmp_max / tmp_sum [G]
+    // Workspace slot: tmp_out [GC][D] (unnormalised), tmp_max / tmp_sum [GC]
     // (m base 2, l), all with coherent stores.
     __device__ void store_slot(const State& S, int64_t slot) const {
-        if (n >= G) return;
-        const __amdgpu_buffer_rsrc_t rs = ws_rsrc(a.tmp_out + slot * (G * D), G * D * 4);
+        if (n >= GC) return;
+        const __amdgpu_buffer_rsrc_t rs = ws_rsrc(a.tmp_out + slot * (GC * D), GC * D * 4);
 #pragma unroll
         for (int j = 0; j < 8; ++j)
             ws_store16(rs, 4 * (n * D + 16 * j + 4 * qg), S.acc[j][0], S.acc[j][1], S.acc[j][2],
                        S.acc[j][3]);
         if (qg == 0) {
-            ws_store<true>(at(a.tmp_max + slot * G, 4 * n), S.m);
-            ws_store<true>(at(a.tmp_sum + slot * G, 4 * n), S.l);
+            ws_store<true>(at(a.tmp_max + slot * GC, 4 * n), S.m);
+            ws_store<true>(at(a.tmp_sum + slot * GC, 4 * n), S.l);
         }
     }
 
@@ -894,11 +920,11 @@ struct Mfma16Core {
     // kBatch pieces at a time with a running maximum.
     static constexpr int kBatch = 2;
     __device__ void combine(long long first, int np, int s, int g) const {
-        if (n >= G) return;
+        if (n >= GC) return;
         const int64_t slot0 = 2 * first;
-        const __amdgpu_buffer_rsrc_t rs = ws_rsrc(a.tmp_out + slot0 * (G * D), (uint32_t)(2 * np) * (G * D * 4));
-        const __amdgpu_buffer_rsrc_t rm = ws_rsrc(a.tmp_max + slot0 * G, (uint32_t)(2 * np) * (G * 4));
-        const __amdgpu_buffer_rsrc_t rl = ws_rsrc(a.tmp_sum + slot0 * G, (uint32_t)(2 * np) * (G * 4));
+        const __amdgpu_buffer_rsrc_t rs = ws_rsrc(a.tmp_out + slot0 * (GC * D), (uint32_t)(2 * np) * (GC * D * 4));
+        const __amdgpu_buffer_rsrc_t rm = ws_rsrc(a.tmp_max + slot0 * GC, (uint32_t)(2 * np) * (GC * 4));
+        const __amdgpu_buffer_rsrc_t rl = ws_rsrc(a.tmp_sum + slot0 * GC, (uint32_t)(2 * np) * (GC * 4));
         float M = kNegInf, lsum = 0.0f;
         f32x4 o[8];
 #pragma unroll
@@ -910,11 +936,11 @@ struct Mfma16Core {
             for (int jj = 0; jj < kBatch; ++jj) {
                 const uint32_t k = (uint32_t)min(k0 + jj, np - 1);
                 const uint32_t sl = 2 * k + (k == 0 ? 1u : 0u);
-                mk[jj] = ws_load4(rm, 4 * (sl * G + n));
-                lk[jj] = ws_load4(rl, 4 * (sl * G + n));
+                mk[jj] = ws_load4(rm, 4 * (sl * GC + n));
+                lk[jj] = ws_load4(rl, 4 * (sl * GC + n));
 #pragma unroll
                 for (int j = 0; j < 8; ++j)
-                    x[jj][j] = ws_load16(rs, 4 * (sl * (G * D) + n * D + 16 * j + 4 * qg));
+                    x[jj][j] = ws_load16(rs, 4 * (sl * (GC * D) + n * D + 16 * j + 4 * qg));
             }
             float Mb = M;
 #pragma unroll
@@ -935,6 +961,7 @@ struct Mfma16Core {
             }
             M = Mb;
         }
+        if (PAIR && !(lsum > 0.0f)) return;          // (as in store_final)
 #pragma unroll
         for (int j = 0; j < 8; ++j)
             store4(s, g, j, o[j][0] / lsum, o[j][1] / lsum, o[j][2] / lsum, o[j][3] / lsum);
@@ -964,23 +991,35 @@ constexpr int NWR = 8;
 // mixed copy-on-write batch (G 8) 202.5 -> 197.3 us; at G = 4 the 16x16 core,
 // three quarters of whose MFMA columns are then idle, was slower (8 x 32768
 // batch 186.2 -> 195.1 us, Llama-shaped batch 67.3 -> 72.9 us).
-template <int G, Dtype CT>
-using RingCore =
-    typename std::conditional<CT == BF16 && G == 8, Mfma16Core<G>, MfmaCore<G, CT>>::type;
+// PAIR: the 16x16 core takes pairs of sequences (used up to 2 kMaxPairUnits
+// sequences, the size of its LDS table).
+template <int G, Dtype CT, bool PAIR>
+using RingCore = typename std::conditional<CT == BF16 && G == 8, Mfma16Core<G, PAIR>,
+                                           MfmaCore<G, CT>>::type;
 
-template <int G, Dtype CT>
+template <int G, Dtype CT, bool PAIR = false>
 __global__ __launch_bounds__(NWR * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void mfma_balanced(DecodeArgs a) {
-    decode_balanced_ring<RingCore<G, CT>, NWR>(a);
+    decode_balanced_ring<RingCore<G, CT, PAIR>, NWR>(a);
+}
+
+template <int G, Dtype CT, bool PAIR>
+hipError_t launch_balanced(const DecodeArgs& a, hipStream_t st) {
+    const void* fn = reinterpret_cast<const void*>(&mfma_balanced<G, CT, PAIR>);
+    const int grid = balanced_grid(fn, NWR * 64, st);
+    if (grid <= 0) return hipErrorLaunchFailure;
+    hipLaunchKernelGGL((mfma_balanced<G, CT, PAIR>), dim3(grid), dim3(NWR * 64), 0, st, a);
+    return hipSuccess;
 }
 
 template <int G, Dtype CT>
 hipError_t launch(const DecodeArgs& a, Schedule sch, hipStream_t st) {
     if (sch == Schedule::Balanced) {
-        const void* fn = reinterpret_cast<const void*>(&mfma_balanced<G, CT>);
-        const int grid = balanced_grid(fn, NWR * 64, st);
-        if (grid <= 0) return hipErrorLaunchFailure;
-        hipLaunchKernelGGL((mfma_balanced<G, CT>), dim3(grid), dim3(NWR * 64), 0, st, a);
+        constexpr bool kPairs = CT == BF16 && G == 8;
+        const hipError_t e = kPairs && (a.num_seqs + 1) / 2 <= kMaxPairUnits
+                                 ? launch_balanced<G, CT, kPairs>(a, st)
+                                 : launch_balanced<G, CT, false>(a, st);
+        if (e != hipSuccess) return e;
     } else {
         const int64_t nwg = (int64_t)a.num_kv_heads * a.num_seqs * a.num_partitions;
         hipLaunchKernelGGL((mfma_partitions<G, CT>), dim3((unsigned)nwg), dim3(NW * 64), 0, st, a);
@@ -992,10 +1031,12 @@ hipError_t launch(const DecodeArgs& a, Schedule sch, hipStream_t st) {
 
 int balanced_waves_mfma(int head_dim, int G, hipStream_t st) {
     if (head_dim != 128 || (G != 4 && G != 8)) return 0;
-    const void* fns[2] = {G == 4 ? reinterpret_cast<const void*>(&mfma_balanced<4, BF16>)
+    const void* fns[3] = {G == 4 ? reinterpret_cast<const void*>(&mfma_balanced<4, BF16>)
                                  : reinterpret_cast<const void*>(&mfma_balanced<8, BF16>),
                           G == 4 ? reinterpret_cast<const void*>(&mfma_balanced<4, I8>)
-                                 : reinterpret_cast<const void*>(&mfma_balanced<8, I8>)};
+                                 : reinterpret_cast<const void*>(&mfma_balanced<8, I8>),
+                          G == 4 ? reinterpret_cast<const void*>(&mfma_balanced<4, BF16>)
+                                 : reinterpret_cast<const void*>(&mfma_balanced<8, BF16, true>)};
     int m = 0;
     for (const void* fn : fns) {
         const int grid = balanced_grid(fn, NWR * 64, st);

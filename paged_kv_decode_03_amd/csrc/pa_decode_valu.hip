@@ -49,6 +49,7 @@ struct ValuCore {
     static constexpr int G = G_;
     static constexpr int D = D_;
     static constexpr bool BASE2 = false;
+    static constexpr bool PAIR = false;          // one sequence per segment
     static constexpr int CE = esize<CT>();
     static constexpr int EPC = 16 / CE;          // cache elements per 16-byte piece
     static constexpr int NM = D * CE / 64;       // pieces per lane per row

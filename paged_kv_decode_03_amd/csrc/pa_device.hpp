@@ -260,6 +260,13 @@ template <int OFF = 0>
 __device__ __forceinline__ void ds_write16(uint32_t addr, u32x4 v) {
     asm volatile("ds_write_b128 %0, %1 offset:%2" : : "v"(addr), "v"(v), "i"(OFF) : "memory");
 }
+// 4 bytes, waited for in the same asm block (for a lone read of a small table
+// while global->LDS loads are in flight)
+__device__ __forceinline__ uint32_t ds_read4_wait(uint32_t addr) {
+    uint32_t v;
+    asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
+    return v;
+}
 __device__ __forceinline__ void ds_write4(uint32_t addr, uint32_t v) {
     asm volatile("ds_write_b32 %0, %1" : : "v"(addr), "v"(v) : "memory");
 }

@@ -22,9 +22,16 @@ bench make:
   descriptors (10 int32 per range) lie inside the counters the workspace
   query reports (segment counters, then 11 per wave, then two).
 
+At 8 query heads per kv head on a bf16 cache the 16x16 core takes pairs of
+sequences per segment ("units"): the model then builds the units the way the
+device does (the shared leading chunks from the block tables, capped below
+both sequences' last chunks) and checks that every chunk a unit walks is a
+chunk of its sequence inside its context, and every shared one a chunk that
+both sequences' tables place on the same block.
+
 A planted mistake (every partial stored in slot 2k, the first-segment slot,
-so that a piece's last segment overwrites its first) is caught. Nothing here
-runs on the GPU.
+so that a piece's last segment overwrites its first) is caught, and so is a
+pair table that shares one chunk too many. Nothing here runs on the GPU.
 """
 import math
 
@@ -40,26 +47,63 @@ class Plan:
     pass
 
 
-def setup(lens, shared_next, Hkv, G, NWG, W, P, B, tails):
-    """balanced_setup: shared_next[s] is whether s and s + 1 start on the same
-    physical block (both longer than a block)."""
+def units_of(lens, tables, B, pair, extra_shared=0):
+    """(nu, info): the chunk count of every unit and, per unit, (first
+    sequence, L0, L1, n0, ns) -- the device's load_unit and
+    pair_shared_chunks. tables: the block tables (rows of block ids), used
+    for pair units only. extra_shared plants a mistake (one shared chunk too
+    many)."""
+    lens = np.asarray(lens, np.int64)
     S = len(lens)
+    if not pair:
+        n = (lens + CHUNK - 1) // CHUNK
+        return n, [(s, int(lens[s]), 0, int(n[s]), 0) for s in range(S)]
+    cpb = B // CHUNK
+    nu, info = [], []
+    for u in range((S + 1) // 2):
+        s0 = 2 * u
+        L0 = int(lens[s0])
+        L1 = int(lens[s0 + 1]) if s0 + 1 < S else 0
+        ns = 0
+        if L0 > 0 and L1 > 0:
+            cap = min((L0 - 1) // CHUNK, (L1 - 1) // CHUNK)
+            if cap > 0:
+                nb = -(-cap // cpb)
+                run = 0
+                while run < nb and tables[s0][run] == tables[s0 + 1][run]:
+                    run += 1
+                ns = min(cap, run * cpb)
+            ns = min(ns + extra_shared, cap) if extra_shared and cap > 0 else ns
+        n0 = -(-L0 // CHUNK)
+        nu.append(n0 + -(-L1 // CHUNK) - ns)
+        info.append((s0, L0, L1, n0, ns))
+    return np.asarray(nu, np.int64), info
+
+
+def setup(lens, shared_next, Hkv, G, NWG, W, P, B, tails, units=None):
+    """balanced_setup: shared_next[s] is whether s and s + 1 start on the same
+    physical block (both longer than a block); units: (nu, info) of
+    units_of (default: one sequence per unit)."""
+    S = len(lens)
+    if units is None:
+        units = units_of(lens, None, B, False)
+    n, info = units
+    U = len(n)
     SC = SC8 if G >= 8 else SC4
-    K = -(-S // (NWG * 64)) if S else 0
-    n = (np.asarray(lens, np.int64) + CHUNK - 1) // CHUNK
+    K = -(-U // (NWG * 64)) if U else 0
     cost = np.where(n > 0, n * CC + SC, 0)
     cum_chunks, cum_cost = [], []
     run_n = run_c = 0
     for t in range(NWG * 64):
-        sb = min(S, t * K)
-        se = min(S, sb + K)
-        run_n += int(n[sb:se].sum())
-        run_c += int(cost[sb:se].sum())
+        ub = min(U, t * K)
+        ue = min(U, ub + K)
+        run_n += int(n[ub:ue].sum())
+        run_c += int(cost[ub:ue].sum())
         cum_chunks.append(run_n)
         cum_cost.append(run_c)
     p = Plan()
-    p.S, p.Hkv, p.K, p.sc, p.B = S, Hkv, K, SC, B
-    p.n = n
+    p.S, p.U, p.Hkv, p.K, p.sc, p.B = S, U, Hkv, K, SC, B
+    p.n, p.info = n, info
     p.cum_chunks, p.cum_cost = np.array(cum_chunks, np.int64), np.array(cum_cost, np.int64)
     p.T, p.Tc = Hkv * run_n, Hkv * run_c
     p.Th, p.Tch = run_n, run_c
@@ -129,7 +173,7 @@ def piece_of(p, X):
     return 2 * j + (1 if X >= start(p, j) + rlen(p, j) - tail(p, j) else 0)
 
 
-def locate(p, lens, Y):
+def locate(p, Y):
     g, Yt, mul = 0, Y, p.Hkv
     if p.hm:
         g = Y // p.Tch
@@ -142,39 +186,49 @@ def locate(p, lens, Y):
     if p.hm:
         base += g * p.Th
         cbase += g * p.Tch
-    sb = min(p.S, t * p.K)
-    se = min(p.S, sb + p.K)
+    ub = min(p.U, t * p.K)
+    ue = min(p.U, ub + p.K)
     found = None
-    for s in range(sb, se):
-        L = int(lens[s])
-        nn = (L + CHUNK - 1) // CHUNK
+    for u in range(ub, ue):
+        nn = int(p.n[u])
         c = mul * (nn * CC + p.sc) if nn else 0
         if Y < cbase + c:
-            found = s
+            found = u
             break
         base += mul * nn
         cbase += c
     assert found is not None, "locate: position not in its slice"
-    return found, int(lens[found]), g, base, cbase
+    return found, int(p.n[found]), g, base, cbase
 
 
-def chunk_at(p, lens, Y):
+def chunk_at(p, Y):
     """(list index, SegPos dict or None)."""
     if Y >= p.Tc:
         return p.T, None
-    s, L, g0, base, cbase = locate(p, lens, Y)
-    nn = (L + CHUNK - 1) // CHUNK
+    s, nn, g0, base, cbase = locate(p, Y)
     sc = nn * CC + p.sc
     g = g0 if p.hm else (Y - cbase) // sc
     gb = 0 if p.hm else g
     off = (Y - cbase) - gb * sc
     assert 0 <= off < sc
     c = 0 if off < p.sc else (off - p.sc) // CC
-    pos = dict(s=s, L=L, n=nn, g=g, c=c, A=base + gb * nn, Y=cbase + gb * sc + p.sc)
+    pos = dict(s=s, n=nn, g=g, c=c, A=base + gb * nn, Y=cbase + gb * sc + p.sc)
     return base + gb * nn + c, pos
 
 
-def next_pos(p, lens, q):
+def chunk_ref(p, q):
+    """(sequence, its chunk, its length, columns 0 all / 1 first / 2 second,
+    shared) of chunk q["c"] of unit q["s"] (the device's chunk_ref)."""
+    s0, L0, L1, n0, ns = p.info[q["s"]]
+    c = q["c"]
+    if c < ns:
+        return s0, c, L0, 0, True
+    if c < n0:
+        return s0, c, L0, 1, False
+    return s0 + 1, c - n0 + ns, L1, 2, False
+
+
+def next_pos(p, q):
     q = dict(q)
     if q["c"] + 1 < q["n"]:
         q["c"] += 1
@@ -185,12 +239,11 @@ def next_pos(p, lens, q):
     if p.hm:
         while True:
             q["s"] += 1
-            if q["s"] == p.S:
+            if q["s"] == p.U:
                 q["s"] = 0
                 q["g"] += 1
             assert q["g"] < p.Hkv, "next_pos: walked past the last head"
-            q["L"] = int(lens[q["s"]])
-            q["n"] = (q["L"] + CHUNK - 1) // CHUNK
+            q["n"] = int(p.n[q["s"]])
             if q["n"]:
                 return q
     q["g"] += 1
@@ -199,28 +252,29 @@ def next_pos(p, lens, q):
     q["g"] = 0
     while True:
         q["s"] += 1
-        assert q["s"] < p.S, "next_pos: walked past the last sequence"
-        q["L"] = int(lens[q["s"]])
-        q["n"] = (q["L"] + CHUNK - 1) // CHUNK
+        assert q["s"] < p.U, "next_pos: walked past the last unit"
+        q["n"] = int(p.n[q["s"]])
         if q["n"]:
             return q
 
 
-def chunk_list(p, lens):
-    """(s, g, c) of every list index, in list order."""
+def chunk_list(p):
+    """(u, g, c) of every list index, in list order."""
     out = []
-    order = ([(g, s) for g in range(p.Hkv) for s in range(p.S)] if p.hm else
-             [(g, s) for s in range(p.S) for g in range(p.Hkv)])
-    for g, s in order:
-        for c in range(int(p.n[s])):
-            out.append((s, g, c))
+    order = ([(g, u) for g in range(p.Hkv) for u in range(p.U)] if p.hm else
+             [(g, u) for u in range(p.U) for g in range(p.Hkv)])
+    for g, u in order:
+        for c in range(int(p.n[u])):
+            out.append((u, g, c))
     return out
 
 
-def simulate(lens, shared_next, Hkv, G, NWG, W, P, B, tails, planted=False):
+def simulate(lens, shared_next, Hkv, G, NWG, W, P, B, tails, planted=False, tables=None,
+             pair=False, extra_shared=0):
     lens = np.asarray(lens, np.int64)
-    p = setup(lens, shared_next, Hkv, G, NWG, W, P, B, tails)
-    want = chunk_list(p, lens)
+    units = units_of(lens, tables, B, pair, extra_shared)
+    p = setup(lens, shared_next, Hkv, G, NWG, W, P, B, tails, units)
+    want = chunk_list(p)
     assert len(want) == p.T
     owner = np.full(p.T, -1, np.int64)
     stored = {}                                        # (segment) -> {piece: slot}
@@ -231,8 +285,8 @@ def simulate(lens, shared_next, Hkv, G, NWG, W, P, B, tails, planted=False):
         Y0 = pstart(p, k)
         if Y0 >= p.Tc:
             continue
-        X0, cur = chunk_at(p, lens, Y0)
-        X1, _ = chunk_at(p, lens, min(p.Tc, pstart(p, k + 1)))
+        X0, cur = chunk_at(p, Y0)
+        X1, _ = chunk_at(p, min(p.Tc, pstart(p, k + 1)))
         if X0 >= X1:
             continue
         q = cur
@@ -241,7 +295,12 @@ def simulate(lens, shared_next, Hkv, G, NWG, W, P, B, tails, planted=False):
             assert owner[X] < 0, f"chunk {X} walked twice"
             owner[X] = k
             assert want[X] == (q["s"], q["g"], q["c"]), f"chunk {X}: {want[X]} vs walk"
-            assert (q["c"] * CHUNK) // B < -(-q["L"] // B), "block-table entry past the context"
+            sq, cc, Lq, who, sh_ = chunk_ref(p, q)
+            assert sq < p.S and (cc * CHUNK) // B < -(-Lq // B), "block-table entry past the context"
+            if sh_:                                    # a shared chunk: full, and on one block for both
+                assert (cc + 1) * CHUNK < Lq and (cc + 1) * CHUNK < lens[sq + 1], "shared chunk not full"
+                assert tables[sq][cc * CHUNK // B] == tables[sq + 1][cc * CHUNK // B], \
+                    "shared chunk on different blocks"
             assert q["A"] + q["c"] == X
             last = i + 1 == X1 - X0
             if last or q["c"] + 1 == q["n"]:           # a segment end inside the piece
@@ -259,7 +318,7 @@ def simulate(lens, shared_next, Hkv, G, NWG, W, P, B, tails, planted=False):
                     stored.setdefault(seg, {})[k] = slot
                     assert declared.setdefault(seg, (first, pieces)) == (first, pieces)
             if not last:
-                q = next_pos(p, lens, q)
+                q = next_pos(p, q)
     assert (owner >= 0).all(), "a chunk no piece walks"
     for seg, ks in stored.items():
         assert seg not in finals
@@ -267,7 +326,7 @@ def simulate(lens, shared_next, Hkv, G, NWG, W, P, B, tails, planted=False):
         assert sorted(ks) == list(range(first, first + pieces)), f"segment {seg}: pieces"
         for i in range(pieces):
             assert ks[first + i] == 2 * (first + i) + (1 if i == 0 else 0), "combine slot"
-    nseg = sum(p.Hkv for s in range(p.S) if p.n[s])
+    nseg = sum(p.Hkv for u in range(p.U) if p.n[u])
     assert len(finals) + len(stored) == nseg, "a segment is neither finished nor combined"
     # claims: flags[0, Wv), the done counter and 10 int32 of descriptor per
     # range after the segment counters, inside S Hkv + 11 waves + 2 counters
@@ -289,6 +348,36 @@ def shared_first_blocks(spec, lens):
     return out
 
 
+def block_tables(spec, lens):
+    """Block tables with synth's sharing: the sequences of a prefix group hold
+    the group's blocks for their first min(prefix blocks, (L - 1) // B) logical
+    blocks, every other block is their own (ids are distinct otherwise)."""
+    S, B = len(lens), spec.block_size
+    nxt = [0]
+
+    def fresh():
+        nxt[0] += 1
+        return nxt[0]
+    gsz = S // spec.prefix_groups if spec.prefix_groups else 0
+    pblk = spec.prefix_tokens // B if spec.prefix_groups else 0
+    groups = {}
+    rows = []
+    for s in range(S):
+        nb = -(-int(lens[s]) // B)
+        sh = min(pblk, (int(lens[s]) - 1) // B) if gsz else 0
+        ids = groups.setdefault(s // gsz, [fresh() for _ in range(pblk)]) if gsz else []
+        rows.append(list(ids[:sh]) + [fresh() for _ in range(nb - sh)] + [0])
+    return rows
+
+
+def pairs_used(spec):
+    """The balanced kernel takes pair units: the 16x16 core (8 query heads per
+    kv head, head_dim 128, bf16 queries and cache) and at most 4096 sequences."""
+    G = spec.num_heads // spec.num_kv_heads
+    return (G == 8 and spec.head_dim == 128 and spec.act == "bf16" and spec.cache == "bf16"
+            and (spec.num_seqs + 1) // 2 <= 2048)
+
+
 def _cases():
     C = synth.CONFIGS
     S_ = synth.Spec
@@ -303,6 +392,8 @@ def _cases():
         "mid_g8_cow": S_("mid cow", 48, ("lognormal", 800, 1.0, 1, 6000), 64, 8, 128, 32,
                          max_len=6000, prefix_groups=4, prefix_tokens=512),
         "g2": S_("G=2", 6, ("uniform", 1, 600), 8, 4, 128, 32, max_len=600),
+        "g8_odd": S_("G=8 odd", 7, ("uniform", 1, 700), 64, 8, 128, 16, max_len=700,
+                     prefix_groups=1, prefix_tokens=256),
     }
     out = []
     for name, spec in small.items():
@@ -335,7 +426,44 @@ def test_balanced_schedule(case):
     name, L, spec, NWG, W, P = case
     G = spec.num_heads // spec.num_kv_heads
     sh = shared_first_blocks(spec, L)
-    simulate(L, sh, spec.num_kv_heads, G, NWG, W, P, spec.block_size, tails=False)
+    pair = pairs_used(spec)
+    simulate(L, sh, spec.num_kv_heads, G, NWG, W, P, spec.block_size, tails=False,
+             tables=block_tables(spec, L) if pair else None, pair=pair)
+
+
+def test_block_tables_follow_synth():
+    """The model's tables share exactly the blocks synth's pool shares."""
+    spec = synth.CONFIGS[5].replace(num_seqs=16, lens=("lognormal", 200, 1.0, 1, 1500),
+                                    max_len=1500, prefix_groups=2, prefix_tokens=256)
+    case = synth.make_case(spec, 11)
+    L = case.context_lens
+    mine = block_tables(spec, L)
+    for a in range(len(L)):
+        for b in range(len(L)):
+            for lb in range(-(-int(min(L[a], L[b])) // spec.block_size)):
+                assert ((case.block_tables[a][lb] == case.block_tables[b][lb])
+                        == (mine[a][lb] == mine[b][lb])), (a, b, lb)
+
+
+def test_pair_units_of_the_cow_batch():
+    """The mixed copy-on-write batch as pair units: most pairs share their
+    prefix chunks, and the walk covers every chunk once."""
+    spec = synth.CONFIGS[5]
+    L = synth.draw_lens(spec, 5)
+    tab = block_tables(spec, L)
+    nu, info = units_of(L, tab, spec.block_size, True)
+    shared = sum(i[4] for i in info)
+    assert shared * CHUNK > 0.4 * (412020 - 223252) / 2
+    assert int(nu.sum()) + shared == int(((np.asarray(L) + CHUNK - 1) // CHUNK).sum())
+
+
+def test_planted_pair_table_mistake_is_caught():
+    spec = synth.CONFIGS[5].replace(num_seqs=16, lens=("lognormal", 200, 1.0, 1, 1500),
+                                    max_len=1500, prefix_groups=2, prefix_tokens=256)
+    L = synth.draw_lens(spec, 7)
+    with pytest.raises(AssertionError):
+        simulate(L, shared_first_blocks(spec, L), 8, 8, 8, 256, 16, spec.block_size,
+                 tails=False, tables=block_tables(spec, L), pair=True, extra_shared=1)
 
 
 def test_cow_batch_is_head_major():

@@ -50,6 +50,12 @@ SMALL = {
                                    act="f32", cache="f32", max_len=400),
     "g2_i8_bf16q": synth.Spec("G=2 int8", 4, ("uniform", 1, 400), 4, 2, 64, 16, act="bf16",
                               cache="i8", max_len=400),
+    # 8 query heads per kv head on a bf16 cache: the balanced kernel takes pairs
+    # of sequences; an odd count leaves the last pair without a second, and one
+    # copy-on-write group makes most pairs share their leading blocks
+    "g8_odd_cow": synth.Spec("G=8 bf16 CoW, odd count", 7, ("uniform", 1, 700), 64, 8, 128, 16,
+                             act="bf16", cache="bf16", max_len=700, prefix_groups=1,
+                             prefix_tokens=256),
 }
 
 # Batches of 20k-30k 16-token chunks over all kv heads: every wave of the
@@ -449,7 +455,7 @@ def test_balanced_placement_invariance(name):
         assert np.abs(got - as_f64(run_decode(dc, 32, balanced=True))).max() <= tol(case)
 
 
-@pytest.mark.parametrize("name", ["cfg1", "cfg2s", "cfg4s", "cfg5s"])
+@pytest.mark.parametrize("name", ["cfg1", "cfg2s", "cfg4s", "cfg5s", "g8_odd_cow"])
 def test_balanced_zero_lengths(name):
     """Empty contexts anywhere in the batch (first, middle, last) give zeros and
     do not disturb the pieces of their neighbours."""
