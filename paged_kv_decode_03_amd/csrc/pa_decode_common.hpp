@@ -32,6 +32,7 @@ constexpr float kNegInf = -__builtin_huge_valf();
 constexpr int NW = 4;        // waves per workgroup
 constexpr int CHUNK = 16;    // tokens per chunk
 constexpr int kFastShare = 160;   // see balanced_setup
+constexpr int kFastShareCow = 152;   // the same, kv head major (copy-on-write) batches
 constexpr int kChunkCost = 16;    // cost units per chunk (see balanced_setup)
 constexpr int kSegCost = 32;      // cost units per segment (see balanced_setup)
 constexpr int kSegCostG8 = 64;    // the same, 8 or more query heads per kv head
@@ -564,11 +565,16 @@ __device__ __forceinline__ bool balanced_setup(const DecodeArgs& a, BalancedShar
     // shortens the idle time rather than the launch: 0-4% faster measured.
     // Shares of 128, 144, 160, 176 and 192 measured in one process: 160 was
     // best or level on all four batches, 1.7% faster than 144 on the int8 one.)
+    // In a copy-on-write batch many chunks come from the L2, where the older
+    // wave's edge is smaller: on the mixed batch the older waves ended 24 us
+    // after the younger ones (a speed ratio of 1.44 against the 1.67 the share
+    // assumes), and kFastShareCow = 152 was 0.7% faster there and 2.0% with 32
+    // query heads; 144 and 136 were slower.
     // Every range keeps at least the cost of a minimum piece, cmin.
     Ranges rg;
     if (NWG == 8) {
         rg.H = NWG / 2;
-        rg.Cs = max(cmin, 2 * C * (256 - kFastShare) / 256);
+        rg.Cs = max(cmin, 2 * C * (256 - (hm ? kFastShareCow : kFastShare)) / 256);
         rg.Cf = max(rg.Cs, 2 * C - rg.Cs);
     } else {
         rg.H = 0;

@@ -40,7 +40,7 @@ import pytest
 
 import synth
 
-CHUNK, CC, SC4, SC8, FAST, TAIL = 16, 16, 32, 64, 160, 48
+CHUNK, CC, SC4, SC8, FAST, FAST_COW, TAIL = 16, 16, 32, 64, 160, 152, 48
 
 
 class Plan:
@@ -110,9 +110,10 @@ def setup(lens, shared_next, Hkv, G, NWG, W, P, B, tails, units=None):
     p.Wv = W * NWG
     C = -(-p.Tc // p.Wv)
     cmin = max(1, P // CHUNK) * CC
+    p.hm = int(np.sum(shared_next)) * 4 >= S
     if NWG == 8:
         p.H = NWG // 2
-        p.Cs = max(cmin, 2 * C * (256 - FAST) // 256)
+        p.Cs = max(cmin, 2 * C * (256 - (FAST_COW if p.hm else FAST)) // 256)
         p.Cf = max(p.Cs, 2 * C - p.Cs)
     else:
         p.H = 0
@@ -125,7 +126,6 @@ def setup(lens, shared_next, Hkv, G, NWG, W, P, B, tails, units=None):
     if p.Tf == 0 or p.Ts == 0:
         p.Tf = p.Ts = 0
     p.PPR = 2 if p.Tf else 1
-    p.hm = int(np.sum(shared_next)) * 4 >= S
     return p
 
 
