@@ -68,13 +68,19 @@ PREFILL_SOURCES = ["pa_prefill.hip", "pa_prefill.hpp", "pa_device.hpp", "pa_kern
                    "pa_write_row.hpp"]
 # The step each workload is timed with by default: the fastest measured schedule
 # (the multi-query kernel with the new tokens written in the same launch for the
-# bf16 workloads, split over 2048-token partitions for the long contexts; the
+# bf16 workloads, split over 4096-token partitions for the long contexts, one
+# resident round of 512 workgroups: 168.6 against 170.4 us per step with 2048; the
 # multi-query kernel after a separate write for the int8 batch, 119.8 against
 # 125.0 us for the balanced kernel with the write fused; the balanced schedule
 # for the mixed copy-on-write batch, and for the fp32 one, which the
 # multi-query kernel does not cover).
-AUTO_SCHEDULE = {1: ("balanced", None), 2: ("multi-query", 0), 3: ("multi-query", 2048),
+AUTO_SCHEDULE = {1: ("balanced", None), 2: ("multi-query", 0), 3: ("multi-query", 4096),
                  4: ("multi-query", 0), 5: ("balanced", None)}
+# The split-K partition of the long-context verify workload (4 query tokens on
+# 8 x 32768 contexts): 4096 tokens, one resident round of 512 workgroups.
+# Measured per step in one process: 512 tokens 203.9 us, 1024 191.1 us, 2048
+# 180.1 us, 4096 170.6 us.
+VERIFY_LONG_PARTITION = 4096
 
 
 def source_hash(files) -> str:
@@ -286,8 +292,10 @@ def bench_multi_query(args, torch, np, pa, synth):
     out = torch.empty_like(q)
     mq = int(qs.q_lens.max())
     nbytes, kv, flops = multi_query_counts(case, qs, np)
-    # long contexts: split-K over 512-token partitions, then the log-sum-exp reduce
-    P = spec.partition_size if args.multi_query == "verify_long" else 0
+    # long contexts: split-K, then the log-sum-exp reduce (--partition, else the
+    # fastest measured partition size)
+    P = (args.partition if args.partition is not None else VERIFY_LONG_PARTITION) \
+        if args.multi_query == "verify_long" else 0
     maxL = case.max_context_len
     ws = pa.prefill_workspace(qs.num_tokens, case.Hq, case.D, maxL, P, dev) if P else None
 
@@ -437,7 +445,7 @@ def main():
     ap.add_argument("--multi-query", choices=["verify", "verify_long", "prefill"], default=None,
                     help="instead of the decode step, time pa_prefill: the speculative verify "
                          "of 4 tokens per sequence on the Llama-shaped batch (verify) or on the "
-                         "8 x 32768 batch with 512-token split-K and the reduce (verify_long), "
+                         "8 x 32768 batch with split-K and the reduce (verify_long), "
                          "or 512-token prefill chunks after 3584 cached tokens (8 sequences)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only time a device copy of 1 GiB (read 1 GiB + write 1 GiB); the "

@@ -175,10 +175,10 @@ def test_prefill_no_rows():
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("cfg,P", [(2, 0), (3, 2048), (4, 0)])
+@pytest.mark.parametrize("cfg,P", [(2, 0), (3, 4096), (4, 0)])
 def test_default_step_full_size_sampled(cfg, P):
     """The default decode step of the Llama-shaped batch (one pass), of the
-    long contexts (2048-token partitions, then the reduce) and of the int8
+    long contexts (4096-token partitions, then the reduce) and of the int8
     batch at full size, in the launch configuration the bench times:
     pa_write_prefill with one query row per sequence writes the new tokens
     (their slots hold poison before) and attends; on the int8 cache
@@ -231,10 +231,11 @@ def test_default_step_full_size_sampled(cfg, P):
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("name", ["verify", "prefill", "verify_long"])
-def test_prefill_full_size_sampled(name):
+@pytest.mark.parametrize("name,P", [("verify", 0), ("prefill", 0), ("verify_long", 512),
+                                    ("verify_long", 4096)])
+def test_prefill_full_size_sampled(name, P):
+    """(verify_long at 4096-token partitions is the launch bench.py times.)"""
     spec, ql = synth.MULTI_QUERY[name]
-    P = spec.partition_size if name == "verify_long" else 0
     print(f"[prefill full] {name}: generating", flush=True)
     case = synth.make_case(spec, 2)
     qs = synth.make_queries(case, ql, 3)

@@ -283,7 +283,7 @@ def _cases():
     # the bench's multi-query steps: one row per sequence on the five
     # workloads (fused write on bf16 caches), split or not; the verify and
     # prefill workloads
-    for cfg, P in ((2, 0), (3, 2048), (4, 0), (5, 1024)):
+    for cfg, P in ((2, 0), (3, 2048), (3, 4096), (4, 0), (5, 1024)):
         spec = C[cfg]
         L = synth.draw_lens(spec, cfg)
         n = np.ones(len(L), np.int64)
@@ -292,8 +292,8 @@ def _cases():
         spec, ql = synth.MULTI_QUERY[name]
         L = synth.draw_lens(spec, 2)
         n = synth.query_counts(L, ql, np.random.default_rng(3))
-        P = spec.partition_size if name == "verify_long" else 0
-        out.append((name, L, n, spec, False, False, P))
+        for P in ((spec.partition_size, 4096) if name == "verify_long" else (0,)):
+            out.append((f"{name}-P{P}", L, n, spec, False, False, P))
     return out
 
 
