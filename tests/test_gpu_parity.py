@@ -56,6 +56,10 @@ SMALL = {
     "g8_odd_cow": synth.Spec("G=8 bf16 CoW, odd count", 7, ("uniform", 1, 700), 64, 8, 128, 16,
                              act="bf16", cache="bf16", max_len=700, prefix_groups=1,
                              prefix_tokens=256),
+    # groups of three: every other pair straddles two groups and shares nothing
+    "g8_cow_g3": synth.Spec("G=8 bf16 CoW, groups of 3", 15, ("uniform", 1, 900), 64, 8, 128,
+                            32, act="bf16", cache="bf16", max_len=900, prefix_groups=5,
+                            prefix_tokens=256),
 }
 
 # Batches of 20k-30k 16-token chunks over all kv heads: every wave of the
@@ -455,7 +459,7 @@ def test_balanced_placement_invariance(name):
         assert np.abs(got - as_f64(run_decode(dc, 32, balanced=True))).max() <= tol(case)
 
 
-@pytest.mark.parametrize("name", ["cfg1", "cfg2s", "cfg4s", "cfg5s", "g8_odd_cow"])
+@pytest.mark.parametrize("name", ["cfg1", "cfg2s", "cfg4s", "cfg5s", "g8_odd_cow", "g8_cow_g3"])
 def test_balanced_zero_lengths(name):
     """Empty contexts anywhere in the batch (first, middle, last) give zeros and
     do not disturb the pieces of their neighbours."""
