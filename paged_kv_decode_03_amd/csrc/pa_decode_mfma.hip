@@ -831,11 +831,15 @@ struct Mfma16Core {
         const bool tail = ((c + 1) * CHUNK) > t1;
         const bool off = PAIR && who != 0 && ((who == 1) == (n >= G));
         f32x4 sacc = {0.0f, 0.0f, 0.0f, 0.0f};
+        // the MFMA runs at raised issue priority, as in the multi-query
+        // kernel (mixed copy-on-write batch 199.1 -> 198.1 us)
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
             sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                 __builtin_bit_cast(bf16x8_t, cur.k[kk]), __builtin_bit_cast(bf16x8_t, qr[kk]), sacc,
                 0, 0, 0);
+        __builtin_amdgcn_s_setprio(0);
         float x[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -870,10 +874,12 @@ struct Mfma16Core {
             m23 = (t0 + 2 < t1 ? 0x0000ffffu : 0u) | (t0 + 3 < t1 ? 0xffff0000u : 0u);
         }
         const i16x4 pb = as_i16x4(pk0, pk1);
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int j = 0; j < 8; ++j)
             S.acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
                 as_i16x4(cur.v[j].x & m01, cur.v[j].y & m23), pb, S.acc[j], 0, 0, 0);
+        __builtin_amdgcn_s_setprio(0);
     }
 
     // The 4 lanes of head n share m; their token sums add up.

@@ -425,7 +425,13 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
             for (int tt = 0; tt < 2; ++tt) acc[mb][tt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         // k slices outermost: the 2 MB accumulators take turns, so no MFMA
-        // waits for the one before it
+        // waits for the one before it. The wave raises its issue priority
+        // for its runs of MFMAs (here and for P V): the other wave of the
+        // SIMD, usually in its softmax, then issues its vector work in the
+        // gaps, and the matrix cores idle less (chunked prefill 317.8 ->
+        // 303.2 us; the QK^T run alone 313.0, the P V run alone 306.6 us;
+        // priority 3 level with 1; the decode shapes level).
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
@@ -436,6 +442,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
                 for (int mb = 0; mb < MB; ++mb)
                     acc[mb][tt] = mfma16x16x32(kop, qop[mb][ks], acc[mb][tt]);
             }
+        __builtin_amdgcn_s_setprio(0);
         bf16x8 pop[MB];
         if constexpr (!I8) {
             // every row block's max first, then one wave-uniform test for the
@@ -538,6 +545,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
         // slots 4-7 of its second, so on an int8 cache the product splits into
         // two 16x16x16 MFMAs, one per half (one block each), whose results are
         // scaled by that block's V scale in fp32.
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
             const uint2 x0 = ds_read_tr16(vl + vtr + 32 * dt);
@@ -564,6 +572,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
                 }
             }
         }
+        __builtin_amdgcn_s_setprio(0);
     };
 
     // One iteration: tile `it` (held in kr/vr) to LDS, tile it + 1 into
