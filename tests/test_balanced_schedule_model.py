@@ -411,6 +411,10 @@ def _cases():
         spec = C[cfg]
         L = synth.draw_lens(spec, cfg)
         out.append((f"cfg{cfg}-P128", L, spec, 8, 256, 128))
+    for n in (4096, 4097):                             # the pair table full, and one past it
+        spec = S_(f"G=8 bf16 {n}", n, ("uniform", 1, 48), 64, 8, 128, 16, max_len=48,
+                  prefix_groups=64 if n == 4096 else 17, prefix_tokens=16)
+        out.append((f"many{n}-P128", synth.draw_lens(spec, 5), spec, 8, 256, 128))
     # odd grids (not a multiple of 8: no XCD remap) and tiny batches
     spec = C[2].replace(num_seqs=5, lens=("uniform", 1, 300), max_len=300)
     out.append(("odd-grid", synth.draw_lens(spec, 3), spec, 8, 100, 16))

@@ -73,6 +73,14 @@ MID = {
     "mid_g8_cow": synth.Spec("G=8 bf16 CoW, mid-size", 48, ("lognormal", 800, 1.0, 1, 6000),
                              64, 8, 128, 32, act="bf16", cache="bf16", max_len=6000,
                              prefix_groups=4, prefix_tokens=512),
+    # around the balanced kernel's pair table (2048 pair units): 4096 sequences
+    # fill it, 4097 take the kernel with one sequence per segment
+    "many_g8_4096": synth.Spec("G=8 bf16, 4096 sequences", 4096, ("uniform", 1, 48), 64, 8,
+                               128, 16, act="bf16", cache="bf16", max_len=48,
+                               prefix_groups=64, prefix_tokens=16),
+    "many_g8_4097": synth.Spec("G=8 bf16, 4097 sequences", 4097, ("uniform", 1, 48), 64, 8,
+                               128, 16, act="bf16", cache="bf16", max_len=48,
+                               prefix_groups=17, prefix_tokens=16),
 }
 
 _cache = {}
@@ -554,7 +562,7 @@ def test_full_size_sampled(cfg):
 # ---- write + decode in one call (pa_write_decode_balanced) ------------------------
 
 FUSED = ["cfg2s", "cfg3s", "cfg4s", "cfg5s", "g8_i8", "g4_b32", "mid_g4_bf16", "mid_g8_i8",
-         "mid_g8_cow", "cfg1", "mha_bf16_d128", "g2_i8_bf16q"]
+         "mid_g8_cow", "cfg1", "mha_bf16_d128", "g2_i8_bf16q", "many_g8_4096", "many_g8_4097"]
 
 
 @pytest.mark.parametrize("name", FUSED)
