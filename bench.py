@@ -70,12 +70,14 @@ PREFILL_SOURCES = ["pa_prefill.hip", "pa_prefill.hpp", "pa_device.hpp", "pa_kern
 # (the multi-query kernel with the new tokens written in the same launch for the
 # bf16 workloads, split over 4096-token partitions for the long contexts, one
 # resident round of 512 workgroups: 168.6 against 170.4 us per step with 2048; the
-# multi-query kernel after a separate write for the int8 batch, 119.8 against
-# 125.0 us for the balanced kernel with the write fused; the balanced schedule
-# for the mixed copy-on-write batch, and for the fp32 one, which the
-# multi-query kernel does not cover).
-AUTO_SCHEDULE = {1: ("balanced", None), 2: ("multi-query", 0), 3: ("multi-query", 4096),
-                 4: ("multi-query", 0), 5: ("balanced", None)}
+# multi-query kernel after a separate write for the int8 batch, 118.2 against
+# 124.9 us with the write fused into it and 125.0 us for the balanced kernel
+# with the write fused; the balanced schedule for the mixed copy-on-write
+# batch, and for the fp32 one, which the multi-query kernel does not cover).
+# (schedule, partition, separate write)
+AUTO_SCHEDULE = {1: ("balanced", None, False), 2: ("multi-query", 0, False),
+                 3: ("multi-query", 4096, False), 4: ("multi-query", 0, True),
+                 5: ("balanced", None, False)}
 # The split-K partition of the long-context verify workload (4 query tokens on
 # 8 x 32768 contexts): 4096 tokens, one resident round of 512 workgroups.
 # Measured per step in one process: 512 tokens 203.9 us, 1024 191.1 us, 2048
@@ -427,12 +429,13 @@ def main():
                     default="auto",
                     help="balanced: pa_write_decode_balanced (one launch); partitions: "
                          "pa_write_kv_cache, pa_decode, pa_decode_splitk_reduce; multi-query: "
-                         "pa_write_prefill with one query row per sequence (bf16; int8: "
-                         "pa_write_kv_cache then pa_prefill), split-K and the reduce with "
-                         "--partition; auto (default): the fastest measured one for the "
+                         "pa_write_prefill with one query row per sequence, split-K and "
+                         "the reduce with --partition (with --separate-write: "
+                         "pa_write_kv_cache then pa_prefill); auto (default): the fastest measured one for the "
                          "workload")
     ap.add_argument("--separate-write", action="store_true",
-                    help="balanced schedule: the write kernel, then the decode (two launches)")
+                    help="balanced and multi-query schedules: the write kernel, then the "
+                         "decode (two launches)")
     ap.add_argument("--graph", action="store_true",
                     help="capture each step (one graph per pool copy) in a HIP graph and time "
                          "graph replays")
@@ -476,9 +479,10 @@ def main():
         bench_copy_blocks(args, spec, torch, np, pa, synth)
         return
     if args.schedule == "auto":
-        args.schedule, auto_p = AUTO_SCHEDULE[args.config]
+        args.schedule, auto_p, auto_sep = AUTO_SCHEDULE[args.config]
         if args.partition is None and auto_p is not None:
             args.partition = auto_p
+        args.separate_write = args.separate_write or auto_sep
     balanced = args.schedule == "balanced"
     mq = args.schedule == "multi-query"
     if args.partition is not None:
@@ -507,9 +511,8 @@ def main():
     scale = float(case.scale)
     stream = torch.cuda.current_stream(dev)
 
-    # the new tokens written by the decode launch itself (the multi-query kernel
-    # does this for bf16 caches)
-    fused = (balanced or (mq and spec.cache == "bf16")) and not args.separate_write
+    # the new tokens written by the decode launch itself
+    fused = (balanced or mq) and not args.separate_write
     one_launch = fused and not (mq and P > 0)      # split-K adds the reduce launch
 
     def step(i, ev=None):
@@ -520,11 +523,12 @@ def main():
             if P > 0:
                 pa.write_prefill(dc.key, dc.value, dc.slot_mapping, None, dc.q, k, v,
                                  dc.block_tables, dc.context_lens, qsl, scale, 1, maxL,
-                                 partition_size=P, tmp_out=ws[0], tmp_max=ws[1], tmp_sum=ws[2],
-                                 row_lens=ws[3])
+                                 dc.k_scale, dc.v_scale, partition_size=P, tmp_out=ws[0],
+                                 tmp_max=ws[1], tmp_sum=ws[2], row_lens=ws[3])
             else:
                 pa.write_prefill(dc.key, dc.value, dc.slot_mapping, out, dc.q, k, v,
-                                 dc.block_tables, dc.context_lens, qsl, scale, 1, maxL)
+                                 dc.block_tables, dc.context_lens, qsl, scale, 1, maxL,
+                                 dc.k_scale, dc.v_scale)
             if ev is not None:
                 ev[1].record(stream)
             if P > 0:
@@ -645,7 +649,7 @@ def main():
             "num_kv_heads": case.Hkv, "head_dim": D, "block_size": case.B,
             "context_lens": list(spec.lens), "sum_context": tr["sum_len"],
             "unique_kv_tokens": tr["unique_tokens"], "partition_size": P, "pool_copies": R,
-            "schedule": args.schedule + ("" if not balanced or fused else " (separate write)")
+            "schedule": args.schedule + ("" if fused or not (balanced or mq) else " (separate write)")
                         + (", HIP graph replays" if args.graph else ""),
             "step": ("write + balanced split-K decode + combine, one launch" if fused and balanced
                      else "write + multi-query kernel with one row per sequence, one launch" +

@@ -365,17 +365,24 @@ int pa_prefill(void *out, const void *q, const void *k_cache, const void *v_cach
  * and value, never from the cache, and stores them to their slots, so the
  * cache holds them afterwards exactly as after pa_write_kv_cache. A token with
  * a negative slot is not written, and its position is read from the cache as
- * it stands. Result and pool are therefore bit-identical to pa_write_kv_cache
- * followed by pa_prefill. context_lens counts the new tokens. Other arguments
- * and the split-K option as in pa_prefill.
- * Supported: bf16 q and cache (an int8 cache returns PA_ERR_UNSUPPORTED; use
- * pa_write_kv_cache then pa_prefill). key and value 16-byte aligned; PA_CHECK=1
- * also verifies each slot against its position.
+ * it stands. With an int8 cache the kernel stores each new token's codes
+ * under the scales of its (block, kv head), k_scale / v_scale as in
+ * pa_write_kv_cache, and quantises the positions it reads from key and value
+ * the same way, so the attention sees the codes the cache then holds. Result
+ * and pool are therefore bit-identical to pa_write_kv_cache followed by
+ * pa_prefill. context_lens counts the new tokens. Other arguments and the
+ * split-K option as in pa_prefill.
+ * Supported: bf16 q, key and value; bf16 or int8 cache (k_scale and v_scale
+ * required for int8, ignored for bf16). key and value 16-byte aligned;
+ * PA_CHECK=1 also verifies each slot against its position (the kernel takes
+ * a new token's scale from the block its position maps to, the block of its
+ * slot when the two agree).
  */
 int pa_write_prefill(const void *key, const void *value, const int64_t *slot_mapping, void *out,
                      const void *q, void *k_cache, void *v_cache, const int32_t *block_tables,
                      int max_blocks_per_seq, const int32_t *context_lens,
-                     const int32_t *query_start_loc, float scale, int num_seqs,
+                     const int32_t *query_start_loc, const float *k_scale,
+                     const float *v_scale, float scale, int num_seqs,
                      int num_query_tokens, int max_query_len, int num_heads, int num_kv_heads,
                      int head_dim, int block_size, int64_t num_blocks, int max_context_len,
                      int partition_size, float *tmp_out, float *tmp_max, float *tmp_sum,

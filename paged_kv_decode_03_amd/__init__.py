@@ -63,8 +63,8 @@ _lib.pa_decode_splitk_reduce.restype = _i
 _lib.pa_prefill.argtypes = [_p, _p, _p, _p, _p, _i, _p, _p, _p, _p, _f, _i, _i, _i, _i, _i, _i,
                             _i, _i64, _i, _i, _p, _p, _p, _p, _i, _i, _p]
 _lib.pa_prefill.restype = _i
-_lib.pa_write_prefill.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _i, _p, _p, _f, _i, _i, _i, _i,
-                                  _i, _i, _i, _i64, _i, _i, _p, _p, _p, _p, _i, _i, _p]
+_lib.pa_write_prefill.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _i, _p, _p, _p, _p, _f, _i, _i,
+                                  _i, _i, _i, _i, _i, _i64, _i, _i, _p, _p, _p, _p, _i, _i, _p]
 _lib.pa_write_prefill.restype = _i
 _lib.pa_decode_splitk_reduce.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p]
 
@@ -209,12 +209,13 @@ def prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_start_lo
 
 def write_prefill(key, value, slot_mapping, out, q, k_cache, v_cache, block_tables,
                   context_lens, query_start_loc, scale, max_query_len, max_context_len,
-                  partition_size=0, tmp_out=None, tmp_max=None, tmp_sum=None, row_lens=None,
-                  stream=None):
-    """pa_write_kv_cache of the new tokens (key / value [T, Hkv, D], one row per
-    query row, slot_mapping [T] int64) and pa_prefill in one launch (bf16)."""
+                  k_scale=None, v_scale=None, partition_size=0, tmp_out=None, tmp_max=None,
+                  tmp_sum=None, row_lens=None, stream=None):
+    """pa_write_kv_cache of the new tokens (key / value [T, Hkv, D] bf16, one row
+    per query row, slot_mapping [T] int64) and pa_prefill in one launch; a bf16
+    or int8 cache (k_scale / v_scale [NB, Hkv] fp32 for int8)."""
     dev = _dev(key, value, slot_mapping, out, q, k_cache, v_cache, block_tables, context_lens,
-               query_start_loc, tmp_out, tmp_max, tmp_sum, row_lens)
+               query_start_loc, k_scale, v_scale, tmp_out, tmp_max, tmp_sum, row_lens)
     if slot_mapping.dtype != torch.int64:
         raise TypeError("slot_mapping must be int64")
     T, Hq, D = q.shape
@@ -227,7 +228,7 @@ def write_prefill(key, value, slot_mapping, out, q, k_cache, v_cache, block_tabl
     rc = _lib.pa_write_prefill(_ptr(key), _ptr(value), _ptr(slot_mapping), _ptr(out), _ptr(q),
                                _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
                                block_tables.shape[1], _ptr(context_lens), _ptr(query_start_loc),
-                               float(scale), S, T, int(max_query_len), Hq, Hkv, D, B, NB,
+                               _ptr(k_scale), _ptr(v_scale), float(scale), S, T, int(max_query_len), Hq, Hkv, D, B, NB,
                                int(max_context_len), int(partition_size), _ptr(tmp_out),
                                _ptr(tmp_max), _ptr(tmp_sum), _ptr(row_lens), _dt(q),
                                _dt(k_cache), _stream(stream, dev))

@@ -355,7 +355,8 @@ int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cach
 int pa_write_prefill(const void* key, const void* value, const int64_t* slot_mapping, void* out,
                      const void* q, void* k_cache, void* v_cache, const int32_t* block_tables,
                      int max_blocks_per_seq, const int32_t* context_lens,
-                     const int32_t* query_start_loc, float scale, int num_seqs,
+                     const int32_t* query_start_loc, const float* k_scale,
+                     const float* v_scale, float scale, int num_seqs,
                      int num_query_tokens, int max_query_len, int num_heads, int num_kv_heads,
                      int head_dim, int block_size, int64_t num_blocks, int max_context_len,
                      int partition_size, float* tmp_out, float* tmp_max, float* tmp_sum,
@@ -364,11 +365,9 @@ int pa_write_prefill(const void* key, const void* value, const int64_t* slot_map
         if (!key || !value || !slot_mapping) return PA_ERR_NULL;
         if (!aligned16(key) || !aligned16(value)) return PA_ERR_ALIGN;
     }
-    if (cache_dtype != PA_BF16 && valid_cache(cache_dtype) && valid_act(q_dtype))
-        return PA_ERR_UNSUPPORTED;
     return prefill(num_query_tokens > 0 ? key : nullptr, value, slot_mapping, out, q, k_cache,
                    v_cache, block_tables, max_blocks_per_seq, context_lens, query_start_loc,
-                   nullptr, nullptr, scale, num_seqs, num_query_tokens, max_query_len, num_heads,
+                   k_scale, v_scale, scale, num_seqs, num_query_tokens, max_query_len, num_heads,
                    num_kv_heads, head_dim, block_size, num_blocks, max_context_len,
                    partition_size, tmp_out, tmp_max, tmp_sum, row_lens, q_dtype, cache_dtype,
                    stream);

@@ -33,7 +33,8 @@ struct PrefillArgs {
     // already in the cache): rows [qsl[s], qsl[s+1]) of key / value [T][Hkv][D]
     // (q dtype) are the n_s newest tokens of sequence s, going to slots
     // slot_mapping[row]; their positions are read from key / value, never from
-    // the cache. bf16 caches only.
+    // the cache. bf16 or int8 caches (int8: the codes under k_scale / v_scale
+    // of the token's block).
     const void* key = nullptr;
     const void* value = nullptr;
     const int64_t* slot_mapping = nullptr;

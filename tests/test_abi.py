@@ -206,13 +206,14 @@ def test_prefill_validation(kw, code):
 
 def write_prefill(**kw):
     args = dict(key=FAKE, value=FAKE, slots=FAKE, out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, MB=8,
-                lens=FAKE, qsl=FAKE, scale=0.125, S=4, T=16, maxq=4, Hq=32, Hkv=8, D=128, B=16,
-                NB=64, maxL=128, P=0, to=None, tm=None, ts=None, rl=None, qdt=BF16, cdt=BF16)
+                lens=FAKE, qsl=FAKE, ks=None, vs=None, scale=0.125, S=4, T=16, maxq=4, Hq=32,
+                Hkv=8, D=128, B=16, NB=64, maxL=128, P=0, to=None, tm=None, ts=None, rl=None,
+                qdt=BF16, cdt=BF16)
     args.update(kw)
     a = args
     return pa.lib().pa_write_prefill(
         a["key"], a["value"], a["slots"], a["out"], a["q"], a["k"], a["v"], a["bt"], a["MB"],
-        a["lens"], a["qsl"], a["scale"], a["S"], a["T"], a["maxq"], a["Hq"], a["Hkv"], a["D"],
+        a["lens"], a["qsl"], a["ks"], a["vs"], a["scale"], a["S"], a["T"], a["maxq"], a["Hq"], a["Hkv"], a["D"],
         a["B"], a["NB"], a["maxL"], a["P"], a["to"], a["tm"], a["ts"], a["rl"], a["qdt"],
         a["cdt"], None)
 
@@ -220,7 +221,8 @@ def write_prefill(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(key=None), NULL), (dict(value=None), NULL), (dict(slots=None), NULL),
     (dict(key=MIS), ALIGN), (dict(value=MIS), ALIGN),
-    (dict(cdt=I8), UNSUP),                        # the fused write covers bf16 caches
+    (dict(cdt=I8), NULL),                         # an int8 cache needs its scales
+    (dict(cdt=I8, ks=FAKE), NULL),
     (dict(qdt=F32, cdt=F32), UNSUP), (dict(P=16), SHAPE), (dict(qsl=None), NULL),
     (dict(T=0, key=None, value=None, slots=None), OK),
 ])

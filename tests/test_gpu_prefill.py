@@ -181,10 +181,9 @@ def test_default_step_full_size_sampled(cfg, P):
     long contexts (4096-token partitions, then the reduce) and of the int8
     batch at full size, in the launch configuration the bench times:
     pa_write_prefill with one query row per sequence writes the new tokens
-    (their slots hold poison before) and attends; on the int8 cache
-    pa_write_kv_cache writes them first and pa_prefill attends. The pool is
-    byte-identical to the oracle's; sampled sequences (every head and dim) are
-    checked against the oracle's decode."""
+    (their slots hold poison before; int8: their codes) and attends. The pool
+    is byte-identical to the oracle's; sampled sequences (every head and dim)
+    are checked against the oracle's decode."""
     from gpu_helpers import poison_pool
     spec = synth.CONFIGS[cfg]
     print(f"[default step] cfg{cfg} P={P}: generating", flush=True)
@@ -197,19 +196,17 @@ def test_default_step_full_size_sampled(cfg, P):
     out = torch.full_like(dc.q, float("nan"))
     maxL = case.max_context_len
     print(f"[default step] cfg{cfg} P={P}: gpu", flush=True)
-    if spec.cache == "i8":
-        pa.write_kv_cache(dc.key, dc.value, k, v, dc.slot_mapping, dc.k_scale, dc.v_scale)
-        pa.prefill(out, dc.q, k, v, dc.block_tables, dc.context_lens, qsl, float(case.scale), 1,
-                   maxL, dc.k_scale, dc.v_scale)
-    elif P:
+    if P:
         ws = pa.prefill_workspace(case.S, case.Hq, case.D, maxL, P, "cuda")
         pa.write_prefill(dc.key, dc.value, dc.slot_mapping, None, dc.q, k, v, dc.block_tables,
-                         dc.context_lens, qsl, float(case.scale), 1, maxL, partition_size=P,
-                         tmp_out=ws[0], tmp_max=ws[1], tmp_sum=ws[2], row_lens=ws[3])
+                         dc.context_lens, qsl, float(case.scale), 1, maxL, dc.k_scale,
+                         dc.v_scale, partition_size=P, tmp_out=ws[0], tmp_max=ws[1],
+                         tmp_sum=ws[2], row_lens=ws[3])
         pa.decode_splitk_reduce(out, ws[0], ws[1], ws[2], ws[3], maxL, P)
     else:
         pa.write_prefill(dc.key, dc.value, dc.slot_mapping, out, dc.q, k, v, dc.block_tables,
-                         dc.context_lens, qsl, float(case.scale), 1, maxL)
+                         dc.context_lens, qsl, float(case.scale), 1, maxL, dc.k_scale,
+                         dc.v_scale)
     torch.cuda.synchronize()
     got = as_f64(out)
     assert np.isfinite(got).all()
@@ -279,11 +276,14 @@ def new_token_rows(case, qs):
 @pytest.mark.parametrize("name,P", [("verify_g4", 0), ("verify_g8_b32", 0), ("mixed_g4", 0),
                                     ("chunk_g4", 0), ("whole_mha", 0), ("cow_g8", 0),
                                     ("decode_ties_s64", 0), ("decode_s256", 0),
-                                    ("verify_g4", 64), ("chunk_g4", 256), ("cow_g8", 512)])
+                                    ("verify_g4", 64), ("chunk_g4", 256), ("cow_g8", 512),
+                                    ("verify_g4_i8", 0), ("g2_i8_b32", 0), ("chunk_i8_g8", 0),
+                                    ("verify_g4_i8", 64), ("chunk_i8_g8", 256)])
 def test_write_prefill_parity(name, P):
     """One launch writes the new tokens and attends: the pool afterwards is
-    byte-identical to the oracle's write, the output within tolerance of the
-    oracle. The new tokens' slots hold poison (NaN) before the call."""
+    byte-identical to the oracle's write (int8: the oracle's codes under the
+    block scales), the output within tolerance of the oracle. The new tokens'
+    slots hold poison (NaN, int8 -128) before the call."""
     spec, ql = CASES[name]
     if name == "cow_g8":
         ql = ("const", 1)
@@ -296,10 +296,11 @@ def test_write_prefill_parity(name, P):
     kp, vp = ok.copy(), ov.copy()
     flat_k = kp.reshape(case.num_blocks, case.Hkv, case.B, case.D)
     flat_v = vp.reshape(case.num_blocks, case.Hkv, case.B, case.D)
-    flat_k[slots // case.B, :, slots % case.B, :] = synth.BF16_POISON
-    flat_v[slots // case.B, :, slots % case.B, :] = synth.BF16_POISON
-    k = host_to_dev(kp, "bf16", "cuda")
-    v = host_to_dev(vp, "bf16", "cuda")
+    poison = synth.I8_POISON if case.spec.cache == "i8" else synth.BF16_POISON
+    flat_k[slots // case.B, :, slots % case.B, :] = poison
+    flat_v[slots // case.B, :, slots % case.B, :] = poison
+    k = host_to_dev(kp, case.spec.cache, "cuda")
+    v = host_to_dev(vp, case.spec.cache, "cuda")
     dc = to_device(case)
     q = host_to_dev(qs.q, "bf16", "cuda")
     qsl = torch.from_numpy(qs.query_start_loc).cuda()
@@ -310,28 +311,31 @@ def test_write_prefill_parity(name, P):
     if P:
         ws = pa.prefill_workspace(qs.num_tokens, case.Hq, case.D, maxL, P, "cuda")
         pa.write_prefill(*args, None, q, k, v, dc.block_tables, dc.context_lens, qsl,
-                         float(case.scale), int(qs.q_lens.max()), maxL, partition_size=P,
-                         tmp_out=ws[0], tmp_max=ws[1], tmp_sum=ws[2], row_lens=ws[3])
+                         float(case.scale), int(qs.q_lens.max()), maxL, dc.k_scale, dc.v_scale,
+                         partition_size=P, tmp_out=ws[0], tmp_max=ws[1], tmp_sum=ws[2],
+                         row_lens=ws[3])
         pa.decode_splitk_reduce(out, ws[0], ws[1], ws[2], ws[3], maxL, P)
     else:
         pa.write_prefill(*args, out, q, k, v, dc.block_tables, dc.context_lens, qsl,
-                         float(case.scale), int(qs.q_lens.max()), maxL)
+                         float(case.scale), int(qs.q_lens.max()), maxL, dc.k_scale, dc.v_scale)
     torch.cuda.synchronize()
     from gpu_helpers import dev_to_host
     assert np.array_equal(dev_to_host(k).view(np.uint8), ok.view(np.uint8)), "K pool differs"
     assert np.array_equal(dev_to_host(v).view(np.uint8), ov.view(np.uint8)), "V pool differs"
     got = as_f64(out)
     ref = oracle.prefill(qs.q, ok, ov, case.block_tables, case.context_lens, qs.query_start_loc,
-                         case.scale)
+                         case.scale, case.k_scale, case.v_scale)
     assert np.isfinite(got).all()
     err = np.abs(got - ref).max()
     print(f"[write_prefill] {name} P={P}: max |gpu - oracle| = {err:.3e}", flush=True)
     assert err <= tol(case)
 
 
-def test_write_prefill_matches_two_calls():
-    """Bit-identical to pa_write_kv_cache followed by pa_prefill."""
-    case, qs, dc = prepare("verify_g4")
+@pytest.mark.parametrize("name", ["verify_g4", "verify_g4_i8", "g2_i8_b32", "chunk_i8_g8"])
+def test_write_prefill_matches_two_calls(name):
+    """Bit-identical to pa_write_kv_cache followed by pa_prefill (output and
+    pool)."""
+    case, qs, dc = prepare(name)
     kn, vn, slots = new_token_rows(case, qs)
     args = (host_to_dev(kn, "bf16", "cuda"), host_to_dev(vn, "bf16", "cuda"),
             torch.from_numpy(slots).cuda())
@@ -341,13 +345,17 @@ def test_write_prefill_matches_two_calls():
     a = torch.empty_like(q)
     b = torch.empty_like(q)
     mq, maxL = int(qs.q_lens.max()), case.max_context_len
+    ks, vs = dc.k_scale, dc.v_scale
     pa.write_prefill(*args, a, q, dc.k_cache, dc.v_cache, dc.block_tables, dc.context_lens, qsl,
-                     float(case.scale), mq, maxL)
-    pa.write_kv_cache(args[0], args[1], k2, v2, args[2])
-    pa.prefill(b, q, k2, v2, dc.block_tables, dc.context_lens, qsl, float(case.scale), mq, maxL)
+                     float(case.scale), mq, maxL, ks, vs)
+    pa.write_kv_cache(args[0], args[1], k2, v2, args[2], ks, vs)
+    pa.prefill(b, q, k2, v2, dc.block_tables, dc.context_lens, qsl, float(case.scale), mq, maxL,
+               ks, vs)
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
-    assert torch.equal(dc.k_cache.view(torch.int16), k2.view(torch.int16))
+    iv = torch.int8 if case.spec.cache == "i8" else torch.int16    # bits (the pool holds NaN)
+    assert torch.equal(dc.k_cache.view(iv), k2.view(iv))
+    assert torch.equal(dc.v_cache.view(iv), v2.view(iv))
 
 
 def test_pa_check_rejects_bad_queries(monkeypatch):
@@ -569,7 +577,8 @@ def test_prefill_placement_bit_identical(name):
             assert np.array_equal(run_prefill(var, qs, dv, partition_size=P), b), f"P={P}"
 
 
-@pytest.mark.parametrize("name", ["verify_g4", "mixed_g4", "cow_g8", "decode_ties_s64"])
+@pytest.mark.parametrize("name", ["verify_g4", "mixed_g4", "cow_g8", "decode_ties_s64",
+                                  "verify_g4_i8", "g2_i8_b32"])
 def test_write_prefill_negative_slots_match_two_calls(name):
     """New tokens with a negative slot are neither written nor read from key /
     value: the fused launch stays bit-identical (output and pool) to
@@ -586,34 +595,37 @@ def test_write_prefill_negative_slots_match_two_calls(name):
     q = host_to_dev(qs.q, "bf16", "cuda")
     qsl = torch.from_numpy(qs.query_start_loc).cuda()
     mq, maxL = int(qs.q_lens.max()), case.max_context_len
+    ks, vs = dc.k_scale, dc.v_scale
     for P in (0, 64):
         k1, v1 = dc.k_cache.clone(), dc.v_cache.clone()
         k2, v2 = dc.k_cache.clone(), dc.v_cache.clone()
         # the skipped positions hold other values in the cache than in key / value
+        # (bf16: one mantissa ulp; int8: one code)
+        iv = torch.int8 if case.spec.cache == "i8" else torch.int16
         for kk, vv in ((k1, v1), (k2, v2)):
-            kk.view(torch.int16).bitwise_xor_(1)      # one mantissa ulp
-            vv.view(torch.int16).bitwise_xor_(1)
+            kk.view(iv).bitwise_xor_(1)
+            vv.view(iv).bitwise_xor_(1)
         a = torch.empty_like(q)
         b = torch.empty_like(q)
         if P:
             w1 = pa.prefill_workspace(qs.num_tokens, case.Hq, case.D, maxL, P, "cuda")
             w2 = pa.prefill_workspace(qs.num_tokens, case.Hq, case.D, maxL, P, "cuda")
             pa.write_prefill(*args, None, q, k1, v1, dc.block_tables, dc.context_lens, qsl,
-                             float(case.scale), mq, maxL, partition_size=P, tmp_out=w1[0],
-                             tmp_max=w1[1], tmp_sum=w1[2], row_lens=w1[3])
+                             float(case.scale), mq, maxL, ks, vs, partition_size=P,
+                             tmp_out=w1[0], tmp_max=w1[1], tmp_sum=w1[2], row_lens=w1[3])
             pa.decode_splitk_reduce(a, w1[0], w1[1], w1[2], w1[3], maxL, P)
-            pa.write_kv_cache(args[0], args[1], k2, v2, args[2])
+            pa.write_kv_cache(args[0], args[1], k2, v2, args[2], ks, vs)
             pa.prefill(None, q, k2, v2, dc.block_tables, dc.context_lens, qsl,
-                       float(case.scale), mq, maxL, partition_size=P, tmp_out=w2[0],
+                       float(case.scale), mq, maxL, ks, vs, partition_size=P, tmp_out=w2[0],
                        tmp_max=w2[1], tmp_sum=w2[2], row_lens=w2[3])
             pa.decode_splitk_reduce(b, w2[0], w2[1], w2[2], w2[3], maxL, P)
         else:
             pa.write_prefill(*args, a, q, k1, v1, dc.block_tables, dc.context_lens, qsl,
-                             float(case.scale), mq, maxL)
-            pa.write_kv_cache(args[0], args[1], k2, v2, args[2])
+                             float(case.scale), mq, maxL, ks, vs)
+            pa.write_kv_cache(args[0], args[1], k2, v2, args[2], ks, vs)
             pa.prefill(b, q, k2, v2, dc.block_tables, dc.context_lens, qsl, float(case.scale),
-                       mq, maxL)
+                       mq, maxL, ks, vs)
         torch.cuda.synchronize()
-        assert torch.equal(k1.view(torch.int16), k2.view(torch.int16)), f"P={P}: K pool"
-        assert torch.equal(v1.view(torch.int16), v2.view(torch.int16)), f"P={P}: V pool"
+        assert torch.equal(k1.view(iv), k2.view(iv)), f"P={P}: K pool"
+        assert torch.equal(v1.view(iv), v2.view(iv)), f"P={P}: V pool"
         assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"P={P}: output"

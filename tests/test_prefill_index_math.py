@@ -85,7 +85,7 @@ def check(cond, what):
 
 
 def model_launch(lens, qlens, Hq, Hkv, B, i8=False, wr=False, P=0, max_query_len=None,
-                 planted_jn_bound=False):
+                 planted_jn_bound=False, planted_masked_half=False):
     """Walk one launch; raise OOB at the first out-of-range index. Returns the
     number of workgroups that did work (a sanity count)."""
     lens = np.asarray(lens, np.int64)
@@ -191,6 +191,10 @@ def model_launch(lens, qlens, Hq, Hkv, B, i8=False, wr=False, P=0, max_query_len
             for jj in j0[has]:
                 tb, te = max(0, -int(jj)), min(TK, n - int(jj))
                 check(q0 + jj + tb >= 0 and q0 + jj + te - 1 < T, "slot_mapping entry")
+            if i8:                                     # the new tokens' scales, per half
+                for hf in range(2):
+                    T0 = kts[has] * TK + 16 * hf
+                    check(T0[T0 < limit] // B < nvalid, "new-token scale's block")
         for k in range(NLD):                           # load_tile
             t, e = PIECE_T[(NR, i8)][k], PIECE_E[(NR, i8)][k]
             inn = kts[:, None] * TK + t[None, :] < limit
@@ -217,6 +221,26 @@ def model_launch(lens, qlens, Hq, Hkv, B, i8=False, wr=False, P=0, max_query_len
                 sel = (jn >= 0) if planted_jn_bound else (jn >= 0) & (jn < n)
                 check((q0 + jn[sel] < T) & (q0 + jn[sel] >= 0),
                       "new-token row read from key/value")
+                # Which position each piece of a computed tile reads from the
+                # cache: none where it comes from key / value (a tile holding
+                # new tokens, jn a new token); else its own token, or, past
+                # `limit`, the first token of the block of its base -- base 0
+                # in a tile holding new tokens, its half's base elsewhere.
+                # None may be a new token (the launch writes those slots while
+                # it reads: another workgroup's, or its own without a barrier).
+                j0 = kts * TK - new0
+                fresh = ((j0 + TK > 0) & (j0 < n))[:, None]
+                from_key = fresh & (jn >= 0) & (jn < n)
+                blk0 = np.where(kts * TK < limit, kts * TK, -1)[:, None]
+                hb = kts[:, None] * TK + 16 * half
+                blkh = np.where(hb < limit, hb // B * B, blk0)
+                blk = np.where(fresh & ~np.asarray(planted_masked_half), blk0, blkh)
+                pos = np.where(inn, kts[:, None] * TK + t[None, :], blk)
+                live_p = (kts < nkt)[:, None]
+                check(~(live_p & ~from_key & (pos >= new0) & (pos < new0 + n)),
+                      "cache read of a new token the launch writes")
+                # a piece of EPP cache elements reads EPP bf16 activations
+                check(e + EPP <= PD, "new-token piece inside its key/value row")
         if i8:                                         # compute: int8 scales
             live = kts[kts < nkt]
             for tt in range(2):
@@ -268,7 +292,9 @@ def _cases():
         ("verify_g4", 0, True), ("verify_g8_b32", 0, True), ("mixed_g4", 0, True),
         ("chunk_g4", 0, True), ("whole_mha", 0, True), ("cow_g8", 0, True),
         ("decode_ties_s64", 0, True), ("decode_s256", 0, True), ("verify_g4", 64, True),
-        ("chunk_g4", 256, True), ("cow_g8", 512, True)]
+        ("chunk_g4", 256, True), ("cow_g8", 512, True), ("verify_g4_i8", 0, True),
+        ("g2_i8_b32", 0, True), ("chunk_i8_g8", 0, True), ("verify_g4_i8", 64, True),
+        ("chunk_i8_g8", 256, True)]
     for name, P, wr in used:
         spec, ql = tests[name]
         if name == "cow_g8" and wr:
@@ -280,14 +306,14 @@ def _cases():
             n = synth.query_counts(L, ql, np.random.default_rng(12))
         out.append((f"{name}-P{P}" + ("-write" if wr else ""), L, n, spec,
                     spec.cache == "i8", wr, P))
-    # the bench's multi-query steps: one row per sequence on the five
-    # workloads (fused write on bf16 caches), split or not; the verify and
-    # prefill workloads
+    # the bench's multi-query steps: one row per sequence on the bf16 and
+    # int8 workloads, the new tokens written by the same launch, split or
+    # not; the verify and prefill workloads
     for cfg, P in ((2, 0), (3, 2048), (3, 4096), (4, 0), (5, 1024)):
         spec = C[cfg]
         L = synth.draw_lens(spec, cfg)
         n = np.ones(len(L), np.int64)
-        out.append((f"cfg{cfg}-P{P}", L, n, spec, spec.cache == "i8", spec.cache == "bf16", P))
+        out.append((f"cfg{cfg}-P{P}-write", L, n, spec, spec.cache == "i8", True, P))
     for name in ("verify", "verify_long", "prefill"):
         spec, ql = synth.MULTI_QUERY[name]
         L = synth.draw_lens(spec, 2)
@@ -323,6 +349,29 @@ def test_planted_jn_bound_is_caught():
         model_launch(L, n, spec.num_heads, spec.num_kv_heads, spec.block_size, wr=True,
                      planted_jn_bound=True)
     model_launch(L, n, spec.num_heads, spec.num_kv_heads, spec.block_size, wr=True)
+
+
+@pytest.mark.parametrize("name", ["mixed_g4", "decode_b16", "decode_b16_i8"])
+def test_planted_masked_half_base_is_caught(name):
+    """Masked pieces (past the tile's last row) of a tile holding new tokens
+    read the first token of their half's block: with 16-token blocks that
+    token may be a new one, whose slot the same launch is writing -- the NaN
+    poison of a new token's slot then reached an output through a zero
+    weight. The model flags it; taking base 0 (the tile's first token: an
+    older token, or a new one read from key / value) does not. decode: one
+    new token per sequence at the first position of a tile's second half
+    (L = 32 k + 17)."""
+    if name.startswith("decode"):
+        L = np.array([17, 49, 81, 113, 145, 177, 209, 1041], np.int64)
+        n = np.ones(len(L), np.int64)
+        Hq, Hkv, B, i8 = 32, 8, 16, name.endswith("i8")
+    else:
+        cases = {c[0]: c for c in CASES}
+        _, L, n, spec, i8, wr, P = cases[f"{name}-P0-write"]
+        Hq, Hkv, B = spec.num_heads, spec.num_kv_heads, spec.block_size
+    with pytest.raises(OOB, match="new token the launch writes"):
+        model_launch(L, n, Hq, Hkv, B, i8=i8, wr=True, planted_masked_half=True)
+    model_launch(L, n, Hq, Hkv, B, i8=i8, wr=True)
 
 
 def test_snake_place_is_a_permutation():
