@@ -335,6 +335,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
                            uint32_t negm, const float (&nks)[2], const float (&nvs)[2], auto nt,
                            auto fresh_tag) {
         constexpr bool FRESH = decltype(fresh_tag)::value;
+        // (the two bases as values: an index into `base` chosen per lane
+        // would put the array in memory)
+        const int64_t base0 = base[0], base1 = base[1];
 #pragma unroll
         for (int k = 0; k < NLD; ++k) {
             const int p = ti + k * TPT, t = p / PPR, e = (p % PPR) * EPP;
@@ -343,8 +346,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
             // pool's unused blocks hold): every row masks it (x = -inf, weight 0)
             const bool in = kt * TK + t < limit;
             const uint32_t lo = (uint32_t)(((in ? t % B : 0) * PD + e) * ELT);
-            const int64_t bb = HALF_UNIFORM ? base[(k * TOK_PER_LD) / 16]
-                                            : (t < 16 ? base[0] : base[1]);
+            const int64_t bb = HALF_UNIFORM ? ((k * TOK_PER_LD) / 16 ? base1 : base0)
+                                            : (t < 16 ? base0 : base1);
             if constexpr (FRESH) {
                 // a new token's row comes from key / value (its slot is being
                 // written by this launch). A masked piece stands for the
@@ -356,7 +359,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
                 // the cache instead, like the other instances.
                 const int tt = in ? t : 0;
                 const int jn = kt * TK + tt - new0;
-                const int64_t bf = in ? bb : base[0];
+                const int64_t bf = in ? bb : base0;
                 const char* kp = reinterpret_cast<const char*>(a.k_cache) + bf + lo;
                 const char* vp = reinterpret_cast<const char*>(a.v_cache) + bf + lo;
                 const bool fresh = jn >= 0 && jn < n && !((negm >> tt) & 1u);
@@ -402,9 +405,19 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
             if (j0 + TK > 0 && j0 < n) {
                 uint32_t negm = 0;
                 float nks[2] = {1.0f, 1.0f}, nvs[2] = {1.0f, 1.0f};
+                // the slots' high words, eight scalar loads at a time (the
+                // index clamped into the tile's new tokens), one wait each
                 const int tb = max(0, -j0), te = min(TK, n - j0);
-                for (int t = tb; t < te; ++t)
-                    if (ld_uniform(a.slot_mapping, (int64_t)q0 + j0 + t) < 0) negm |= 1u << t;
+                const int32_t* shi = reinterpret_cast<const int32_t*>(a.slot_mapping) + 1;
+                for (int t0 = tb; t0 < te; t0 += 8) {
+                    int32_t hi[8];
+#pragma unroll
+                    for (int u = 0; u < 8; ++u)
+                        hi[u] = ld_uniform(shi, 2 * ((int64_t)q0 + j0 + min(t0 + u, te - 1)));
+#pragma unroll
+                    for (int u = 0; u < 8; ++u)
+                        if (t0 + u < te && hi[u] < 0) negm |= 1u << (t0 + u);
+                }
                 if constexpr (I8) {
 #pragma unroll
                     for (int h = 0; h < 2; ++h) {
