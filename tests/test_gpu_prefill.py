@@ -175,15 +175,17 @@ def test_prefill_no_rows():
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("cfg,P", [(2, 0), (3, 4096), (4, 0)])
-def test_default_step_full_size_sampled(cfg, P):
+@pytest.mark.parametrize("cfg,P,sep", [(2, 0, False), (3, 4096, False), (4, 0, True),
+                                       (4, 0, False)])
+def test_default_step_full_size_sampled(cfg, P, sep):
     """The default decode step of the Llama-shaped batch (one pass), of the
     long contexts (4096-token partitions, then the reduce) and of the int8
     batch at full size, in the launch configuration the bench times:
     pa_write_prefill with one query row per sequence writes the new tokens
-    (their slots hold poison before; int8: their codes) and attends. The pool
-    is byte-identical to the oracle's; sampled sequences (every head and dim)
-    are checked against the oracle's decode."""
+    (their slots hold poison before) and attends; on the int8 batch
+    pa_write_kv_cache then pa_prefill (sep), and the fused int8 write too. The
+    pool is byte-identical to the oracle's; sampled sequences (every head and
+    dim) are checked against the oracle's decode."""
     from gpu_helpers import poison_pool
     spec = synth.CONFIGS[cfg]
     print(f"[default step] cfg{cfg} P={P}: generating", flush=True)
@@ -195,8 +197,12 @@ def test_default_step_full_size_sampled(cfg, P):
     qsl = torch.arange(case.S + 1, dtype=torch.int32, device="cuda")
     out = torch.full_like(dc.q, float("nan"))
     maxL = case.max_context_len
-    print(f"[default step] cfg{cfg} P={P}: gpu", flush=True)
-    if P:
+    print(f"[default step] cfg{cfg} P={P} separate write {sep}: gpu", flush=True)
+    if sep:
+        pa.write_kv_cache(dc.key, dc.value, k, v, dc.slot_mapping, dc.k_scale, dc.v_scale)
+        pa.prefill(out, dc.q, k, v, dc.block_tables, dc.context_lens, qsl, float(case.scale), 1,
+                   maxL, dc.k_scale, dc.v_scale)
+    elif P:
         ws = pa.prefill_workspace(case.S, case.Hq, case.D, maxL, P, "cuda")
         pa.write_prefill(dc.key, dc.value, dc.slot_mapping, None, dc.q, k, v, dc.block_tables,
                          dc.context_lens, qsl, float(case.scale), 1, maxL, dc.k_scale,
