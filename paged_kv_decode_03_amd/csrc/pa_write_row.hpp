@@ -68,9 +68,13 @@ __device__ __forceinline__ void write_vector(const void* key, const void* value,
                                              int64_t tok, int g, int v) {
     constexpr int VEC = (ACT == F32) ? 4 : 8;            // elements per 16-byte vector
     constexpr int E = (ACT == F32) ? 4 : 2;
+    // the activations are loaded with the slot, not after it: their addresses
+    // do not depend on it, so the two loads overlap
+    const int64_t src = (tok * num_kv_heads + g) * head_dim + (int64_t)v * VEC;
+    const uint4 kw = ld16((const char*)key + src * E);
+    const uint4 vw = ld16((const char*)value + src * E);
     const int64_t slot = slot_mapping[tok];
     if (slot < 0) return;
-    const int64_t src = (tok * num_kv_heads + g) * head_dim + (int64_t)v * VEC;
     const int64_t dst = slot_row(slot, g, v, VEC, num_kv_heads, head_dim, block_size);
     float ks = 1.0f, vs = 1.0f;
     if constexpr (CACHE == I8) {
@@ -78,8 +82,8 @@ __device__ __forceinline__ void write_vector(const void* key, const void* value,
         ks = k_scale[sc];
         vs = v_scale[sc];
     }
-    put_vector<ACT, CACHE>(k_cache, dst, ld16((const char*)key + src * E), ks);
-    put_vector<ACT, CACHE>(v_cache, dst, ld16((const char*)value + src * E), vs);
+    put_vector<ACT, CACHE>(k_cache, dst, kw, ks);
+    put_vector<ACT, CACHE>(v_cache, dst, vw, vs);
 }
 
 }  // namespace pa
