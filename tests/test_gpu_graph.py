@@ -58,21 +58,29 @@ def make_step(case, dc, k, v, out, schedule):
         return step, None
     if schedule.startswith("multi-query"):
         # the default step on bf16 batches: pa_write_prefill with one query row
-        # per sequence, in one pass or split over P-token partitions + the reduce
+        # per sequence, in one pass or split over P-token partitions + the reduce;
+        # "multi-query-sep" (the int8 batch's default): pa_write_kv_cache, then
+        # pa_prefill
         P = int(schedule.split(":")[1]) if ":" in schedule else 0
+        sep = schedule.startswith("multi-query-sep")
         qsl = torch.arange(case.S + 1, dtype=torch.int32, device="cuda")
         ws = pa.prefill_workspace(case.S, case.Hq, case.D, maxL, P, "cuda") if P else None
+        ks, vs = dc.k_scale, dc.v_scale
 
         def step():
-            if P:
+            if sep:
+                pa.write_kv_cache(dc.key, dc.value, k, v, dc.slot_mapping, ks, vs)
+                pa.prefill(out, dc.q, k, v, dc.block_tables, dc.context_lens, qsl, scale, 1,
+                           maxL, ks, vs)
+            elif P:
                 pa.write_prefill(dc.key, dc.value, dc.slot_mapping, None, dc.q, k, v,
-                                 dc.block_tables, dc.context_lens, qsl, scale, 1, maxL,
+                                 dc.block_tables, dc.context_lens, qsl, scale, 1, maxL, ks, vs,
                                  partition_size=P, tmp_out=ws[0], tmp_max=ws[1], tmp_sum=ws[2],
                                  row_lens=ws[3])
                 pa.decode_splitk_reduce(out, *ws[:3], ws[3], maxL, P)
             else:
                 pa.write_prefill(dc.key, dc.value, dc.slot_mapping, out, dc.q, k, v,
-                                 dc.block_tables, dc.context_lens, qsl, scale, 1, maxL)
+                                 dc.block_tables, dc.context_lens, qsl, scale, 1, maxL, ks, vs)
         return step, ws
     P = case.spec.partition_size or 512
     ws = pa.workspace(case.S, case.Hq, case.D, maxL, P, "cuda")
@@ -89,7 +97,8 @@ def make_step(case, dc, k, v, out, schedule):
                                            ("cfg5s", "fused"), ("cfg3s", "partitions"),
                                            ("cfg2s", "partitions"), ("cfg2s", "multi-query"),
                                            ("cfg3s", "multi-query:2048"), ("cfg5s", "noalloc"),
-                                           ("cfg4s", "noalloc")])
+                                           ("cfg4s", "noalloc"), ("cfg4s", "multi-query-sep"),
+                                           ("cfg4s", "multi-query")])
 def test_graph_replays_match_eager(name, schedule):
     print(f"[graph] {name} {schedule}", flush=True)
     case = synth.make_case(SPECS[name], 21)
