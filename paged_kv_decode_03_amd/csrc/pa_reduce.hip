@@ -49,24 +49,42 @@ __global__ __launch_bounds__(RW * 64) void reduce_kernel(ReduceArgs a) {
     const int sh_i = blockIdx.x;
     const int s = sh_i / a.num_heads;
     const int64_t sh = sh_i;
-    const int L = a.context_lens[s];
-    const int n = (L + a.partition_size - 1) / a.partition_size;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int D = a.head_dim;
+    const int NP = a.num_partitions;
+    const float* mp = a.tmp_max + sh * NP;
+    const float* lp = a.tmp_sum + sh * NP;
+    const float* op = a.tmp_out + sh * NP * D;
+    // The first partitions' maxima, sums and (wave w combining partitions w,
+    // w + RW, ..., four per round) the first round's outputs are loaded at
+    // once with the context length: their addresses need only the workspace's
+    // partition count, and those past the sequence's own count n are read
+    // but never used.
+    constexpr int U = 4;
+    float x0[U][NV];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+            const int jj = wave + u * RW, d = lane + 64 * k;
+            x0[u][k] = (jj < NP && d < D) ? op[(int64_t)jj * D + d] : 0.0f;
+        }
+    const float m0 = tid < NP ? mp[tid] : kNegInf;
+    const float l0 = tid < NP ? lp[tid] : 0.0f;
+    const int L = a.context_lens[s];
+    const int n = (L + a.partition_size - 1) / a.partition_size;
     if (n == 0) {
         for (int d = tid; d < D; d += RW * 64) store_out(a.out, sh * D + d, 0.0f, a.out_dtype);
         return;
     }
-    const float* mp = a.tmp_max + sh * a.num_partitions;
-    const float* lp = a.tmp_sum + sh * a.num_partitions;
-    const float* op = a.tmp_out + sh * a.num_partitions * D;
-    float M = kNegInf;
-    for (int j = tid; j < n; j += RW * 64) M = fmaxf(M, mp[j]);
+    float M = tid < n ? m0 : kNegInf;
+    for (int j = tid + RW * 64; j < n; j += RW * 64) M = fmaxf(M, mp[j]);
     M = block_max(M, red);
     const bool in_lds = n <= WMAX;
     float ws = 0.0f;
     for (int j = tid; j < n; j += RW * 64) {
-        const float W = lp[j] * __builtin_amdgcn_exp2f((mp[j] - M) * kLog2e);
+        const float mj = j == tid ? m0 : mp[j], lj = j == tid ? l0 : lp[j];
+        const float W = lj * __builtin_amdgcn_exp2f((mj - M) * kLog2e);
         ws += W;
         if (in_lds) wts[j] = W;
     }
@@ -78,9 +96,17 @@ __global__ __launch_bounds__(RW * 64) void reduce_kernel(ReduceArgs a) {
     float acc[NV];
 #pragma unroll
     for (int k = 0; k < NV; ++k) acc[k] = 0.0f;
-    // wave w: partitions w, w + RW, ...; four of them per round, loads first
-    constexpr int U = 4;
-    int j = wave;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int jj = wave + u * RW;
+        if (jj < n) {
+            const float W = weight(jj);
+#pragma unroll
+            for (int k = 0; k < NV; ++k) acc[k] = fmaf(W, x0[u][k], acc[k]);
+        }
+    }
+    // the later rounds: loads first
+    int j = wave + U * RW;
     for (; j + (U - 1) * RW < n; j += U * RW) {
         float x[U][NV];
 #pragma unroll
