@@ -265,6 +265,7 @@ struct BalancedShared {
     long long wave_cost[NWG];
     long long total, total_cost;
     int s0[NWG + 1], nu[NWG + 1], g0[NWG + 1];       // unit, its chunks, kv head
+    int lu0[NWG + 1], lu1[NWG + 1];                  // its sequences' lengths (pair: both)
     long long base0[NWG + 1], cbase0[NWG + 1];
 };
 
@@ -473,12 +474,20 @@ __device__ __forceinline__ bool balanced_setup(const DecodeArgs& a, BalancedShar
     const int K = (U + NWG * 64 - 1) / (NWG * 64);
     const int ub = min(U, tid * K), ue = min(U, ub + K);
     const int sb = PAIR ? min(S, 2 * ub) : ub, se = PAIR ? min(S, 2 * ue) : ue;   // its sequences
+    // lengths of unit u's sequences (the second 0 without PAIR or past S)
+    auto unit_lens = [&](int u, int& L0, int& L1) {
+        if constexpr (PAIR) {
+            L0 = ld_const(a.context_lens, 2 * u);
+            L1 = 2 * u + 1 < S ? ld_const(a.context_lens, 2 * u + 1) : 0;
+        } else {
+            L0 = ld_const(a.context_lens, u);
+            L1 = 0;
+        }
+    };
     // chunks of unit u (pair units: its shared chunks into the table)
-    auto unit_chunks = [&](int u, bool fill) -> int {
+    auto unit_chunks = [&](int u, bool fill, int L0, int L1) -> int {
         if constexpr (PAIR) {
             const int s0 = 2 * u;
-            const int L0 = ld_const(a.context_lens, s0);
-            const int L1 = s0 + 1 < S ? ld_const(a.context_lens, s0 + 1) : 0;
             int ns;
             if (fill) {
                 ns = (L0 > 0 && L1 > 0) ? pair_shared_chunks(a, s0, L0, L1) : 0;
@@ -489,17 +498,38 @@ __device__ __forceinline__ bool balanced_setup(const DecodeArgs& a, BalancedShar
             return (L0 + CHUNK - 1) / CHUNK + (L1 + CHUNK - 1) / CHUNK - ns;
         } else {
             (void)fill;
-            return (ld_const(a.context_lens, u) + CHUNK - 1) / CHUNK;
+            (void)L1;
+            return (L0 + CHUNK - 1) / CHUNK;
         }
     };
     int my = 0;
     int shared = 0;                                  // s whose first block is s + 1's
     long long myc = 0;
+    int n_ub = 0, L0_ub = 0, L1_ub = 0;             // the slice's first unit
     for (int u = ub; u < ue; ++u) {
-        const int n = unit_chunks(u, true);
+        int L0, L1;
+        unit_lens(u, L0, L1);
+        const int n = unit_chunks(u, true, L0, L1);
+        if (u == ub) {
+            n_ub = n;
+            L0_ub = L0;
+            L1_ub = L1;
+        }
         my += n;
         myc += n ? (long long)n * CC + SC : 0;
     }
+    // (the locate below takes the first unit's lengths and count from here:
+    // a slice is one unit up to 64 x NWG units, and a load per range start,
+    // in turn, cost about as much as the rest of the set-up)
+    auto slice_unit = [&](int u, int& L0, int& L1) {
+        if (u == ub) {
+            L0 = L0_ub;
+            L1 = L1_ub;
+            return n_ub;
+        }
+        unit_lens(u, L0, L1);
+        return unit_chunks(u, false, L0, L1);
+    };
     for (int s = sb; s < se; ++s) {
         // all four loads at once (entry 0 of a block-table row always exists)
         const int t = min(s + 1, S - 1);
@@ -592,11 +622,14 @@ __device__ __forceinline__ bool balanced_setup(const DecodeArgs& a, BalancedShar
             if (exclc <= Yr && Yr < exclc + myc) {
                 long long base = excl, cbase = exclc;
                 for (int u = ub; u < ue; ++u) {
-                    const int n = unit_chunks(u, false);
+                    int L0, L1;
+                    const int n = slice_unit(u, L0, L1);
                     const long long cost = n ? (long long)n * CC + SC : 0;
                     if (Yr < cbase + cost) {
                         sh.s0[v] = u;
                         sh.nu[v] = n;
+                        sh.lu0[v] = L0;
+                        sh.lu1[v] = L1;
                         sh.g0[v] = g;
                         sh.base0[v] = (long long)g * Th + base;
                         sh.cbase0[v] = (long long)g * Tch + cbase;
@@ -611,11 +644,14 @@ __device__ __forceinline__ bool balanced_setup(const DecodeArgs& a, BalancedShar
         if ((long long)Hkv * exclc <= Y && Y < (long long)Hkv * (exclc + myc)) {
             long long base = (long long)Hkv * excl, cbase = (long long)Hkv * exclc;
             for (int u = ub; u < ue; ++u) {
-                const int n = unit_chunks(u, false);
+                int L0, L1;
+                const int n = slice_unit(u, L0, L1);
                 const long long cost = n ? (long long)Hkv * ((long long)n * CC + SC) : 0;
                 if (Y < cbase + cost) {
                     sh.s0[v] = u;
                     sh.nu[v] = n;
+                    sh.lu0[v] = L0;
+                    sh.lu1[v] = L1;
                     sh.base0[v] = base;
                     sh.cbase0[v] = cbase;
                     break;
@@ -639,8 +675,19 @@ __device__ __forceinline__ bool balanced_setup(const DecodeArgs& a, BalancedShar
         const long long off = (Y - cbase) - gb * sc;   // < sc, so c < n
         const int c = off < SC ? 0 : (int)((off - SC) / CC);
         if (p) {
+            // the unit's fields as load_unit fills them, from the locate's
+            // lengths in LDS rather than from memory
             p->s = u;
-            load_unit<PAIR>(a, lds_addr(ns_tab), *p);
+            p->L = uniform(sh.lu0[v]);
+            if constexpr (PAIR) {
+                p->L1 = uniform(sh.lu1[v]);
+                p->n0 = (p->L + CHUNK - 1) / CHUNK;
+                p->ns = uniform((int)ds_read4_wait(lds_addr(ns_tab) + 4 * u));
+            } else {
+                p->L1 = p->ns = 0;
+                p->n0 = n;
+            }
+            p->n = n;
             p->g = g;
             p->c = c;
             p->A = base + gb * n;
