@@ -311,12 +311,44 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     // a spare tile past the context, which is loaded but never computed).
     // (kt is the same in every lane of the wave; saying so keeps the test and
     // the bases in scalar registers: 1-3% fewer VGPRs)
+    // (int8: bid keeps the halves' block ids, -1 for a half wholly past the
+    // context, for the scales)
+    int bid[2] = {-1, -1};
     auto tile_bases = [&](int kt_, int64_t (&base)[2]) {
         const int kt = uniform(kt_);
-        base[0] = kt * TK < limit
-            ? (int64_t)ld_uniform(bt, (kt * TK) / B) * blk_stride + head_off : 0;
-        base[1] = kt * TK + 16 < limit
-            ? (int64_t)ld_uniform(bt, (kt * TK + 16) / B) * blk_stride + head_off : base[0];
+        if constexpr (I8) {
+            const int b0 = kt * TK < limit ? ld_uniform(bt, (kt * TK) / B) : -1;
+            const int b1 = kt * TK + 16 < limit ? ld_uniform(bt, (kt * TK + 16) / B) : -1;
+            base[0] = b0 >= 0 ? (int64_t)b0 * blk_stride + head_off : 0;
+            base[1] = b1 >= 0 ? (int64_t)b1 * blk_stride + head_off : base[0];
+            bid[0] = b0;
+            bid[1] = b1;
+        } else {
+            base[0] = kt * TK < limit
+                ? (int64_t)ld_uniform(bt, (kt * TK) / B) * blk_stride + head_off : 0;
+            base[1] = kt * TK + 16 < limit
+                ? (int64_t)ld_uniform(bt, (kt * TK + 16) / B) * blk_stride + head_off : base[0];
+        }
+    };
+    // int8: the (block, kv head) scales of a tile's two halves (1 for a half
+    // past the context), loaded when the tile's loads are issued, a tile
+    // ahead of its compute: loaded at the start of the compute they held up
+    // its first LDS reads, whose wait also waits for scalar loads
+    struct Scales {
+        float k0, k1, v0, v1;
+    };
+    auto fetch_scales = [&](Scales& sc) {
+        sc.k0 = sc.k1 = sc.v0 = sc.v1 = 1.0f;
+        {
+            if (bid[0] >= 0) {
+                sc.k0 = ld_uniform(a.k_scale, (int64_t)bid[0] * Hkv + g);
+                sc.v0 = ld_uniform(a.v_scale, (int64_t)bid[0] * Hkv + g);
+            }
+            if (bid[1] >= 0) {
+                sc.k1 = ld_uniform(a.k_scale, (int64_t)bid[1] * Hkv + g);
+                sc.v1 = ld_uniform(a.v_scale, (int64_t)bid[1] * Hkv + g);
+            }
+        }
     };
     // A KV tile that no other workgroup of the launch reads is loaded
     // non-temporal: kept out of the L2's way, it leaves the room to lines that
@@ -466,21 +498,11 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     };
 
     // EDGE: some row of the tile must mask some token of this KV tile
-    auto compute = [&](int kt, auto edge_tag) {
+    auto compute = [&](int kt, auto edge_tag, const Scales& sc) {
         constexpr bool EDGE = decltype(edge_tag)::value;
         // int8: per-(block, kv head) scales of the two 16-token halves
-        float ksc[2] = {1.0f, 1.0f}, vsc[2] = {1.0f, 1.0f};
-        if (I8) {
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt) {
-                const int T = kt * TK + tt * 16;
-                if (T < limit) {
-                    const int64_t b = ld_uniform(bt, T / B);
-                    ksc[tt] = ld_uniform(a.k_scale, b * Hkv + g);
-                    vsc[tt] = ld_uniform(a.v_scale, b * Hkv + g);
-                }
-            }
-        }
+        const float ksc[2] = {I8 ? sc.k0 : 1.0f, I8 ? sc.k1 : 1.0f};
+        const float vsc[2] = {I8 ? sc.v0 : 1.0f, I8 ? sc.v1 : 1.0f};
         // S^T for every row block; each K operand is read right before its
         // MFMAs (all row blocks use it), which keeps few operands live
         f32x4 acc[MB][2];
@@ -651,13 +673,16 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     // the other tile's loads as still in flight (conditional loads made it
     // wait for both).
     int64_t bnext[2] = {0, 0};
+    Scales sc1{1.0f, 1.0f, 1.0f, 1.0f}, sc2{1.0f, 1.0f, 1.0f, 1.0f};   // kr/vr's and kr2/vr2's tiles
     if (DEPTH == 2 || nit > 0) {
         tile_bases(kt0 + tg, bnext);
         load_tile(kt0 + tg, bnext, kr, vr);
+        if constexpr (I8) fetch_scales(sc1);
     }
     if (DEPTH == 2) {
         tile_bases(kt0 + tg + NT, bnext);
         load_tile(kt0 + tg + NT, bnext, kr2, vr2);
+        if constexpr (I8) fetch_scales(sc2);
     }
     if (DEPTH == 2 || nit > DEPTH) tile_bases(kt0 + tg + DEPTH * NT, bnext);
     // Iteration it: its tile (in kr/vr) to LDS, tile it + DEPTH into the same
@@ -667,22 +692,24 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     // tile's reads. With two, buffer b is written again two tiles later, after
     // the next tile's barrier, which every wave reaches only once it has
     // computed from b.
-    auto iteration = [&](int it, uint4 (&kr)[NLD], uint4 (&vr)[NLD], int buf) {
+    auto iteration = [&](int it, uint4 (&kr)[NLD], uint4 (&vr)[NLD], Scales& sc, int buf) {
         const int kt = kt0 + it * NT + tg;
         kl = lds + (buf * NT + tg) * TGBYTES;
         vl = kl + KBYTES;
         if constexpr (NR > 1 && DEPTH == 1) __syncthreads();
         store_tile(kr, vr);
+        const Scales cur = sc;                       // this tile's, before the next tile's
         if constexpr (NR > 1) __syncthreads();
         if (DEPTH == 2 || it + DEPTH < nit) {
             load_tile(kt + DEPTH * NT, bnext, kr, vr);
+            if constexpr (I8) fetch_scales(sc);
             if (DEPTH == 2 || it + DEPTH + 1 < nit) tile_bases(kt + (DEPTH + 1) * NT, bnext);
         }
         if (kt < nkt) {
             if (kt * TK + TK - 1 > p_first)
-                compute(kt, std::true_type{});
+                compute(kt, std::true_type{}, cur);
             else
-                compute(kt, std::false_type{});
+                compute(kt, std::false_type{}, cur);
         }
     };
     if constexpr (DEPTH == 2) {
@@ -690,12 +717,12 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
         // last tile after it
         int it = 0;
         for (; it + 1 < nit; it += 2) {
-            iteration(it, kr, vr, 0);
-            iteration(it + 1, kr2, vr2, 1);
+            iteration(it, kr, vr, sc1, 0);
+            iteration(it + 1, kr2, vr2, sc2, 1);
         }
-        if (it < nit) iteration(it, kr, vr, 0);
+        if (it < nit) iteration(it, kr, vr, sc1, 0);
     } else {
-        for (int it = 0; it < nit; ++it) iteration(it, kr, vr, 0);
+        for (int it = 0; it < nit; ++it) iteration(it, kr, vr, sc1, 0);
     }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) l[mb] = lsum[mb][0];   // already the whole row's sum
