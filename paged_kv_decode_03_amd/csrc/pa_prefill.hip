@@ -860,7 +860,10 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
     if (a.num_seqs == 0 || a.max_query_len == 0) return hipSuccess;
     const int64_t rows = (int64_t)a.max_query_len * (a.num_heads / a.num_kv_heads);
     if (rows <= 16) return launch_shape<1, 1>(a, 1, st);
-    if (rows <= 32) return launch_shape<1, 2>(a, 1, st);
+    // 17-64 rows: 2 row groups x 2 token groups. (One row group of two row
+    // blocks, for up to 32 rows, was level without the fused write and 2-3%
+    // slower with it, whose instance then needed more than 256 registers:
+    // one wave per SIMD.)
     if (rows <= 64) return launch_shape<2, 2>(a, 1, st);
     return launch_shape<4, 2>(a, (int)((rows + 127) / 128), st);
 }

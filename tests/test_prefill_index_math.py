@@ -34,8 +34,6 @@ def launch_shape(max_query_len, G):
     rows = max_query_len * G
     if rows <= 16:
         return 1, 1, 1
-    if rows <= 32:
-        return 1, 2, 1
     if rows <= 64:
         return 2, 2, 1
     return 4, 2, (rows + 127) // 128
