@@ -281,6 +281,35 @@ def test_reduce_from_oracle_partials():
         assert np.abs(as_f64(out) - want).max() <= tl
 
 
+@pytest.mark.parametrize("P", [16, 128])
+def test_reduce_ignores_partials_past_the_length(P):
+    """The reduce loads the first partitions of every row before it knows the
+    row's own partition count; those past it hold NaN here and must not
+    reach the output. P = 16: up to 69 partitions, so the later rounds of
+    the combine (past the first four per wave) run as well."""
+    case = synth.make_case(SMALL["cfg2s"], 5)
+    ok, ov = oracle.fill_cache(case)
+    o, m, l = oracle.decode_partials(case.q, ok, ov, case.block_tables, case.context_lens,
+                                     case.scale, P)
+    n = -(-case.context_lens.astype(np.int64) // P)
+    assert n.max() > 16 or P == 128
+    o32, m32, l32 = (a.astype(np.float32) for a in (o, m, l))
+    for s in range(case.S):                            # past the length: NaN (the oracle's)
+        assert np.isnan(o32[s, :, n[s]:]).all() and np.isnan(m32[s, :, n[s]:]).all()
+    want = oracle.splitk_reduce(np.nan_to_num(o32, nan=0.0).astype(np.float64),
+                                np.nan_to_num(m32, nan=0.0).astype(np.float64),
+                                np.nan_to_num(l32, nan=0.0).astype(np.float64),
+                                case.context_lens, P)
+    out = torch.empty((case.S, case.Hq, case.D), dtype=torch.float32, device="cuda")
+    pa.decode_splitk_reduce(out, torch.from_numpy(o32).cuda(), torch.from_numpy(m32).cuda(),
+                            torch.from_numpy(l32).cuda(), torch.from_numpy(case.context_lens).cuda(),
+                            case.max_context_len, P)
+    sync()
+    got = as_f64(out)
+    assert np.isfinite(got).all()
+    assert np.abs(got - want).max() <= 1e-5
+
+
 # ---- exactness ----------------------------------------------------------------
 
 def _onehot_case(spec, seed, tstar_of):
